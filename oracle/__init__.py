@@ -1,0 +1,172 @@
+"""fp64 CPU oracle for the MHLA forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never touch it, and it never touches them.
+
+Two independent implementations live here:
+
+* ``mhla_oracle.c`` (plain C, fp64, OpenMP over (batch, head) slices):
+  ``blockwise`` follows the three steps of "MHLA: Restoring Expressivity of
+  Linear Attention via Token-Level Multi-Head" §4.1 (block summaries S_b, z_b;
+  multi-head mixing S~_i, z~_i; readout), and ``rows`` is brute force on rows
+  of the explicit token-pair matrix of §4.2 Eq. 5.
+* ``numpy_bruteforce`` (NumPy fp64): the same explicit matrix, built whole,
+  for tiny inputs -- a second witness written without the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mhla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_mhla.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, -O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _configure(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lp = ctypes.POINTER(ctypes.c_long)
+    lib.oracle_mhla_blockwise.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ip, ip,
+                                          ctypes.c_int, ctypes.c_int]
+    lib.oracle_mhla_rows.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ip, ip, ctypes.c_int,
+                                     lp, ctypes.c_int]
+    lib.oracle_block_of_token.argtypes = [ip, ip, ctypes.c_long]
+    lib.oracle_num_blocks.argtypes = [ip, ip]
+    lib.oracle_phi.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_phi.restype = ctypes.c_double
+    lib.oracle_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def use_library(path):
+    """Point the wrappers at another build of mhla_oracle.c (used by the
+    mutation tests, which plant mistakes in a copy); returns the previous one."""
+    global _lib
+    prev = _lib
+    _lib = None if path is None else _configure(ctypes.CDLL(path))
+    return prev
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _g3(x: Sequence[int]):
+    x = tuple(int(v) for v in x)
+    x = (1,) * (3 - len(x)) + x
+    return (ctypes.c_int * 3)(*x)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def phi(kind: int, x: float) -> float:
+    return float(_load().oracle_phi(kind, float(x)))
+
+
+def num_blocks(grid, block) -> int:
+    return int(_load().oracle_num_blocks(_g3(grid), _g3(block)))
+
+
+def block_of_token(grid, block, t: int) -> int:
+    return int(_load().oracle_block_of_token(_g3(grid), _g3(block), int(t)))
+
+
+def blockwise(Q, K, V, W, grid, block, phi_kind: int, nthreads: int = 0) -> np.ndarray:
+    """Q,K,V: [B,H,N,d]; W: [H,M,M].  Returns Y [B,H,N,d] fp64."""
+    Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
+    B, H, N, d = Q.shape
+    Y = np.empty_like(Q)
+    rc = _load().oracle_mhla_blockwise(_dptr(Q), _dptr(K), _dptr(V), _dptr(W), _dptr(Y),
+                                       B, H, N, d, _g3(grid), _g3(block), int(phi_kind),
+                                       int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_mhla_blockwise rejected the arguments")
+    return Y
+
+
+def rows(Q, K, V, W, grid, block, phi_kind: int, flat_rows) -> np.ndarray:
+    """Brute-force rows.  flat_rows[r] = (b*H + h)*N + q.  Returns [nrows, d]."""
+    Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
+    B, H, N, d = Q.shape
+    r = np.ascontiguousarray(flat_rows, dtype=np.int64)
+    out = np.empty((len(r), d), dtype=np.float64)
+    rc = _load().oracle_mhla_rows(_dptr(Q), _dptr(K), _dptr(V), _dptr(W), _dptr(out),
+                                  B, H, N, d, _g3(grid), _g3(block), int(phi_kind),
+                                  r.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), len(r))
+    if rc != 0:
+        raise ValueError("oracle_mhla_rows rejected the arguments")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# NumPy witness (independent of the C file).
+# ---------------------------------------------------------------------------
+
+def np_phi(kind: int, x: np.ndarray) -> np.ndarray:
+    if kind == 0:
+        return np.maximum(x, 0.0)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def np_block_map(grid, block) -> np.ndarray:
+    """Token -> block index via np.unravel_index / np.ravel_multi_index."""
+    g = (1,) * (3 - len(grid)) + tuple(grid)
+    b = (1,) * (3 - len(block)) + tuple(block)
+    coords = np.unravel_index(np.arange(g[0] * g[1] * g[2]), g)
+    bc = tuple(c // s for c, s in zip(coords, b))
+    return np.ravel_multi_index(bc, tuple(gi // bi for gi, bi in zip(g, b)))
+
+
+def np_attention_matrix(q, k, w, grid, block, phi_kind) -> np.ndarray:
+    """Explicit A[q,j] = W[blk(q), blk(j)] * phi(q).phi(k_j) for one slice."""
+    bm = np_block_map(grid, block)
+    kern = np_phi(phi_kind, q) @ np_phi(phi_kind, k).T
+    return w[np.ix_(bm, bm)] * kern
+
+
+def numpy_bruteforce(Q, K, V, W, grid, block, phi_kind) -> np.ndarray:
+    Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
+    B, H, N, d = Q.shape
+    Y = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(H):
+            A = np_attention_matrix(Q[b, h], K[b, h], W[h], grid, block, phi_kind)
+            den = A.sum(axis=1)
+            num = A @ V[b, h]
+            safe = np.where(den == 0.0, 1.0, den)
+            Y[b, h] = np.where((den == 0.0)[:, None], 0.0, num / safe[:, None])
+    return Y
