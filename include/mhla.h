@@ -1,0 +1,120 @@
+/*
+ * mhla.h -- C ABI of libmhla, the MI355X (gfx950) forward pass of MHLA
+ * (Multi-Head Linear Attention with token-level heads).
+ *
+ * Operation (MHLA paper = "MHLA: Restoring Expressivity of Linear Attention
+ * via Token-Level Multi-Head", arXiv 2601.07832):
+ *   For every (batch b, channel head h) slice with Q, K, V in R^{N x d}
+ *   (§4.1, the projected queries, keys and values), the N tokens form a
+ *   (T, Hg, Wg) grid that is cut into M equal, non-overlapping (bt, bh, bw)
+ *   tiles (§1 and §4.1; blocks are numbered in raster order of the block grid,
+ *   Fig. 4b).  With phi the feature map (ReLU, or elu+1 -- the two choices of
+ *   the tutorial "Attention 变体：从 Sliding Window 到 MLA", linear attention
+ *   section):
+ *     S_b  = sum_{j in b} phi(K_j) V_j^T,   z_b = sum_{j in b} phi(K_j)   (§4.1)
+ *     S~_i = sum_b W[h][i][b] S_b,          z~_i = sum_b W[h][i][b] z_b   (§4.1-§4.2)
+ *     Y_q  = phi(Q_q) S~_i / (phi(Q_q) . z~_i)   for q in query block i   (§4.1)
+ *   The result equals the token-pair form of §4.2 Eq. 5 up to rounding order.
+ *   No 1/sqrt(d) scale is applied and V is used as given.  A row whose
+ *   denominator is exactly 0 (possible only with ReLU) is written as zeros.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, out: device pointers to [B, H, N, d] contiguous row-major
+ *     tensors of element type `dtype` (fp32 or bf16), tokens in raster order
+ *     of the grid (x fastest, then y, then t).  `out` must not overlap Q, K or V.
+ *   - Wmix: device pointer to [H, M, M] fp32 row-major; Wmix[h][i][b] is the
+ *     weight of key block b in query block i's mixture.  It is shared over B.
+ *     Any values are accepted (no sign or normalisation check); a positive
+ *     per-row scale cancels in the output.
+ *   - All pointers are caller-owned; the library never frees them.  Device
+ *     pointers must be 16-byte aligned.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued asynchronously; no host or device-wide synchronisation happens
+ *     (except when the library's workspace has to grow, which synchronises the
+ *     device once).
+ *   - Argument and shape errors are detected on the host before anything is
+ *     enqueued; the return code says which (MHLA_ERR_*), and
+ *     mhla_last_error() gives a message for the calling thread.
+ *   - Supported: d a multiple of 8 in [8, 128] (bf16) or any d in [1, 128]
+ *     (fp32); n_b = N / M >= 1; B*H <= 2^31-1 slices.
+ */
+#ifndef MHLA_H
+#define MHLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mhla_block_shape {
+  int ndim;      /* 1, 2 or 3: how many trailing grid axes are in use        */
+  int grid[3];   /* (T, Hg, Wg) token grid; unused leading entries are 1     */
+  int block[3];  /* (bt, bh, bw) block dims; each divides its grid dimension */
+} mhla_block_shape;
+
+enum { MHLA_PHI_RELU = 0, MHLA_PHI_ELU1 = 1 };
+enum { MHLA_DTYPE_F32 = 0, MHLA_DTYPE_BF16 = 1 };
+enum {
+  MHLA_OK = 0,
+  MHLA_ERR_INVALID_ARG = 1, /* null pointer, bad enum, non-positive size    */
+  MHLA_ERR_SHAPE = 2,       /* grid product != N, block does not divide grid */
+  MHLA_ERR_UNSUPPORTED = 3, /* d or dtype outside the supported set          */
+  MHLA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed    */
+  MHLA_ERR_ALIAS = 5        /* out overlaps Q, K or V                        */
+};
+
+/* Kernel path selection for mhla_forward_path (testing and tuning). */
+enum {
+  MHLA_PATH_AUTO = 0,       /* the library's choice for the shape            */
+  MHLA_PATH_GENERIC = 1,    /* summary -> mixing -> readout, three kernels   */
+  MHLA_PATH_FUSED = 2,      /* one workgroup per slice, summaries kept in LDS */
+  MHLA_PATH_PAIRS = 3       /* token-pair form of Eq. 5, no summaries        */
+};
+
+/* Forward pass (MHLA paper §4.1).  Returns MHLA_OK or an MHLA_ERR_* code. */
+int mhla_forward(const void* Q, const void* K, const void* V, const float* Wmix,
+                 void* out, int B, int H, int N, int d,
+                 const mhla_block_shape* block_shape, int phi_kind, int dtype,
+                 void* stream);
+
+/* Same as mhla_forward with an explicit kernel path.  A path that does not
+ * support the shape returns MHLA_ERR_UNSUPPORTED without enqueuing work. */
+int mhla_forward_path(const void* Q, const void* K, const void* V,
+                      const float* Wmix, void* out, int B, int H, int N, int d,
+                      const mhla_block_shape* block_shape, int phi_kind,
+                      int dtype, int path, void* stream);
+
+/* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
+ * would return for these sizes. */
+int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape,
+                  int phi_kind, int dtype);
+
+/* The path MHLA_PATH_AUTO picks for these sizes (host only), or -code. */
+int mhla_plan(int B, int H, int N, int d, const mhla_block_shape* block_shape,
+              int phi_kind, int dtype);
+
+/* Number of blocks M for a valid shape, or -code. */
+int mhla_num_blocks(int N, const mhla_block_shape* block_shape);
+
+/* Device workspace in bytes that `path` needs for these sizes (0 when the
+ * path keeps its intermediates on chip).  Returns 0 for invalid sizes. */
+size_t mhla_workspace_bytes(int B, int H, int N, int d,
+                            const mhla_block_shape* block_shape, int dtype,
+                            int path);
+
+/* Static description of a code; never NULL. */
+const char* mhla_error_string(int code);
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* mhla_last_error(void);
+
+/* Frees the library-owned workspaces on every device (synchronises each
+ * device that has one).  Safe to call at any time outside a forward call. */
+void mhla_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHLA_H */

@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/mhla.h declares, and rejects bad arguments on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_head_mhla_amd as m
+from mhla_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(_declared_functions()) == set(m.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m.library_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    for code in range(6):
+        assert m.mhla_error_string(code)
+    assert m.mhla_error_string(99) == "unknown error code"
+
+
+def _v(B=2, H=3, N=64, d=16, grid=(1, 8, 8), block=(1, 4, 4), phi=0, dtype=0):
+    return m.mhla_validate(B, H, N, d, m.BlockShape.make(grid, block), phi, dtype)
+
+
+def test_validate_accepts_workloads():
+    for wl in WORKLOADS.values():
+        rc = m.mhla_validate(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(wl.grid, wl.block),
+                             wl.phi, wl.dtype)
+        assert rc == m.MHLA_OK, (wl.name, m.mhla_last_error())
+        assert m.mhla_num_blocks(wl.N, m.BlockShape.make(wl.grid, wl.block)) == wl.M
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), m.MHLA_ERR_INVALID_ARG),
+    (dict(H=-1), m.MHLA_ERR_INVALID_ARG),
+    (dict(d=0), m.MHLA_ERR_INVALID_ARG),
+    (dict(phi=2), m.MHLA_ERR_INVALID_ARG),
+    (dict(dtype=7), m.MHLA_ERR_INVALID_ARG),
+    (dict(N=65), m.MHLA_ERR_SHAPE),                               # grid product != N
+    (dict(block=(1, 3, 4)), m.MHLA_ERR_SHAPE),                    # 3 does not divide 8
+    (dict(block=(1, 4, 0)), m.MHLA_ERR_SHAPE),
+    (dict(d=129), m.MHLA_ERR_UNSUPPORTED),
+    (dict(d=20, dtype=1), m.MHLA_ERR_UNSUPPORTED),                # bf16 needs d % 8 == 0
+])
+def test_validate_rejects(kw, code):
+    assert _v(**kw) == code
+    assert m.mhla_last_error() != ""
+
+
+def test_validate_ndim():
+    bs = m.BlockShape.make((8, 8), (4, 4))          # ndim 2
+    assert m.mhla_validate(1, 1, 64, 16, bs, 0, 0) == m.MHLA_OK
+    bs = m.BlockShape.make((1, 8, 8), (1, 4, 4), ndim=2)
+    assert m.mhla_validate(1, 1, 64, 16, bs, 0, 0) == m.MHLA_OK
+    bs = m.BlockShape.make((2, 4, 8), (1, 4, 4), ndim=2)   # a used axis outside ndim
+    assert m.mhla_validate(1, 1, 64, 16, bs, 0, 0) == m.MHLA_ERR_SHAPE
+    bs = m.BlockShape.make((2, 4, 8), (1, 4, 4), ndim=4)
+    assert m.mhla_validate(1, 1, 64, 16, bs, 0, 0) == m.MHLA_ERR_SHAPE
+
+
+def test_fp32_any_d_supported():
+    for d in (1, 5, 17, 128):
+        assert _v(d=d) == m.MHLA_OK
+
+
+def test_plan_and_workspace():
+    wl = WORKLOADS["deit_t"]
+    bs = m.BlockShape.make(wl.grid, wl.block)
+    assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) == m.MHLA_PATH_FUSED
+    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_FUSED) == 0
+    L = wl.d * wl.d + wl.d
+    assert (m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_GENERIC)
+            == 2 * wl.B * wl.H * wl.M * L * 4)
+    # the fused path refuses shapes it cannot hold on chip
+    wl = WORKLOADS["video"]
+    bs = m.BlockShape.make(wl.grid, wl.block)
+    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_FUSED) == 0
+    assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) != m.MHLA_PATH_FUSED
+    assert m.mhla_plan(0, 1, 64, 16, m.BlockShape.make((8, 8), (4, 4)), 0, 0) < 0
+
+
+def test_forward_rejects_null_pointers_before_any_launch():
+    lib = m.load_library()
+    bs = m.BlockShape.make((8, 8), (4, 4))
+    rc = lib.mhla_forward(None, None, None, None, None, 1, 1, 64, 16, ctypes.byref(bs), 0, 0, None)
+    assert rc == m.MHLA_ERR_INVALID_ARG
+    rc = lib.mhla_forward(None, None, None, None, None, 1, 1, 64, 16, None, 0, 0, None)
+    assert rc == m.MHLA_ERR_INVALID_ARG
+    rc = lib.mhla_forward_path(None, None, None, None, None, 1, 1, 64, 16, ctypes.byref(bs), 0, 0,
+                               9, None)
+    assert rc == m.MHLA_ERR_INVALID_ARG
+
+
+def test_forward_rejects_alias_and_misalignment_before_any_launch():
+    """Host pointers are fine here: the checks run before anything touches them."""
+    lib = m.load_library()
+    bs = m.BlockShape.make((8, 8), (4, 4))
+    buf = (ctypes.c_char * (64 * 16 * 4 * 8 + 64))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    sz = 64 * 16 * 4
+    q, k, v, w = base, base + sz, base + 2 * sz, base + 3 * sz
+    rc = lib.mhla_forward(q, k, v, w, q, 1, 1, 64, 16, ctypes.byref(bs), 0, 0, None)
+    assert rc == m.MHLA_ERR_ALIAS
+    rc = lib.mhla_forward(q, k, v, w, w, 1, 1, 64, 16, ctypes.byref(bs), 0, 0, None)
+    assert rc == m.MHLA_ERR_ALIAS   # out overlaps W
+    rc = lib.mhla_forward(q + 4, k, v, w, base + 5 * sz, 1, 1, 64, 16, ctypes.byref(bs), 0, 0,
+                          None)
+    assert rc == m.MHLA_ERR_INVALID_ARG
+    rc = lib.mhla_forward_path(q, k, v, w, base + 5 * sz, 1, 1, 64, 16, ctypes.byref(bs), 0, 0,
+                               m.MHLA_PATH_FUSED, None)
+    assert rc == m.MHLA_ERR_UNSUPPORTED   # fused path is bf16-only

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 oracle.
+
+Gate (floating point): max over (batch, head) slices of
+max|y - y_oracle| / max|y_oracle| <= 1e-5 for fp32 inputs, 1e-2 for bf16
+inputs.  Each test prints the measured error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_level_head_mhla_amd as m
+from mhla_inputs import (DTYPE_BF16, DTYPE_F32, PHI_ELU1, PHI_RELU, WORKLOADS, custom_workload,
+                         make_inputs)
+from gpu_util import TOL, run, slice_error, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED]
+
+
+def _oracle_full(inp):
+    wl = inp.wl
+    return oracle.blockwise(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, wl.grid, wl.block, wl.phi)
+
+
+def _check_sampled(inp, y, n_slices, n_rows, seed=0):
+    """Compare whole sampled slices (blockwise oracle) and brute-force rows."""
+    wl = inp.wl
+    rng = np.random.default_rng(seed)
+    S = wl.B * wl.H
+    picks = sorted(set([0, S - 1] + rng.choice(S, size=min(S, n_slices), replace=False).tolist()))
+    q, k, v = inp.q_f64, inp.k_f64, inp.v_f64
+    err = 0.0
+    for s in picks:
+        b, h = divmod(s, wl.H)
+        ref = oracle.blockwise(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                               inp.w_f64[h:h + 1], wl.grid, wl.block, wl.phi)
+        err = max(err, slice_error(y[b:b + 1, h:h + 1], ref))
+    rows = rng.choice(S * wl.N, size=n_rows, replace=False)
+    ref_rows = oracle.rows(q, k, v, inp.w_f64, wl.grid, wl.block, wl.phi, rows)
+    yr = y.reshape(-1, wl.d)[rows]
+    # rows are judged against their own slice's max (from the sampled slices' scale)
+    scale = np.abs(ref_rows).max()
+    err_rows = float(np.abs(yr - ref_rows).max() / scale)
+    return err, err_rows
+
+
+@pytest.mark.parametrize("name", ["tiny", "deit_t", "dit_xl2", "hires"])
+@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC])
+def test_workload_full(name, path):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, path))
+    ref = _oracle_full(inp)
+    err = slice_error(y, ref)
+    print("PARITY %s path=%d err=%.3e" % (name, path, err))
+    assert np.all(np.isfinite(y))
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC])
+def test_video_sampled(path):
+    wl = WORKLOADS["video"]
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, path))
+    assert np.all(np.isfinite(y))
+    err, err_rows = _check_sampled(inp, y, n_slices=1, n_rows=96)
+    print("PARITY video path=%d slices_err=%.3e rows_err=%.3e" % (path, err, err_rows))
+    assert err <= TOL[wl.dtype]
+    assert err_rows <= TOL[wl.dtype]
+
+
+FUSED_CASES = [
+    # (grid, block, d, phi)
+    ((1, 14, 14), (1, 7, 7), 64, PHI_ELU1),   # DeiT-like, ragged 49-token blocks
+    ((1, 10, 10), (1, 5, 5), 64, PHI_RELU),   # 25-token blocks
+    ((1, 8, 8), (1, 8, 8), 32, PHI_ELU1),     # M = 1: global linear attention
+    ((1, 6, 9), (1, 3, 3), 16, PHI_RELU),     # M = 6, 9 tokens per block
+    ((2, 8, 8), (1, 4, 8), 56, PHI_ELU1),     # 3-D grid, M = 4
+    ((1, 4, 16), (1, 2, 4), 8, PHI_RELU),     # M = 8, d = 8
+    ((1, 12, 12), (1, 6, 4), 40, PHI_ELU1),   # M = 6, 24 tokens, d = 40
+    ((1, 1, 64), (1, 1, 32), 24, PHI_RELU),   # 1-D sequence chunks
+]
+
+
+@pytest.mark.parametrize("grid,block,d,phi", FUSED_CASES)
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_small_shapes(grid, block, d, phi, path):
+    wl = custom_workload(3, 2, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 997)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, path))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY small %s %s d=%d phi=%d path=%d err=%.3e" % (grid, block, d, phi, path, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+@pytest.mark.parametrize("d", [1, 5, 16, 17, 64, 128])
+def test_fp32_generic_any_d(d):
+    wl = custom_workload(2, 2, d, (1, 6, 10), (1, 3, 5), PHI_ELU1, DTYPE_F32, index=d)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_GENERIC))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY fp32 d=%d err=%.3e" % (d, err))
+    assert err <= TOL[DTYPE_F32]
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("kind", ["identity", "sparse_rows", "unnormalised"])
+def test_special_mixing_matrices(path, kind):
+    """W = I (block-local), rows with zeros, and rows that do not sum to 1."""
+    wl = custom_workload(2, 3, 64, (1, 14, 14), (1, 7, 7), PHI_ELU1, DTYPE_BF16, index=5)
+    inp = make_inputs(wl)
+    M = wl.M
+    if kind == "identity":
+        inp.w = np.broadcast_to(np.eye(M, dtype=np.float32), (wl.H, M, M)).copy()
+    elif kind == "sparse_rows":
+        inp.w[:, :, 1] = 0.0
+        inp.w[:, 2, :] = 0.0
+        inp.w[:, 2, 3] = 1.0
+    else:
+        inp.w = (inp.w * np.float32(37.0)).astype(np.float32)
+    y = to_f64(run(inp, path))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY W=%s path=%d err=%.3e" % (kind, path, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_zero_denominator_rows(path):
+    """ReLU query with every coordinate <= 0: phi(q) = 0, the row is written as 0."""
+    wl = custom_workload(1, 2, 32, (1, 8, 8), (1, 4, 4), PHI_RELU, DTYPE_BF16, index=6)
+    inp = make_inputs(wl)
+    from mhla_inputs import bf16_round_bits
+    qf = -np.abs(np.random.default_rng(0).standard_normal((wl.d,))).astype(np.float32)
+    inp.q[0, 1, 7] = bf16_round_bits(qf)
+    inp.q[0, 0, 63] = bf16_round_bits(np.zeros(wl.d, np.float32))
+    y = to_f64(run(inp, path))
+    assert np.all(y[0, 1, 7] == 0.0) and np.all(y[0, 0, 63] == 0.0)
+    err = slice_error(y, _oracle_full(inp))
+    assert err <= TOL[DTYPE_BF16]
+
+
+def test_fp32_zero_denominator_rows():
+    wl = custom_workload(1, 1, 16, (1, 8, 8), (1, 4, 4), PHI_RELU, DTYPE_F32, index=7)
+    inp = make_inputs(wl)
+    inp.q[0, 0, 9] = -np.abs(inp.q[0, 0, 9])
+    y = to_f64(run(inp, m.MHLA_PATH_GENERIC))
+    assert np.all(y[0, 0, 9] == 0.0)
+    assert slice_error(y, _oracle_full(inp)) <= TOL[DTYPE_F32]
+
+
+@pytest.mark.parametrize("name", ["deit_t", "hires"])
+def test_deterministic(name):
+    inp = make_inputs(WORKLOADS[name], B=2)
+    dev = to_device(inp)
+    a = run(inp, dev=dev)
+    b = run(inp, dev=dev)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_side_stream():
+    inp = make_inputs(WORKLOADS["deit_t"], B=4)
+    dev = to_device(inp)
+    ref = run(inp, dev=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = torch.empty_like(dev[0])
+        m.mhla_forward(*dev, out, (inp.wl.grid, inp.wl.block), inp.wl.phi)
+    s.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_errors_enqueue_nothing():
+    inp = make_inputs(WORKLOADS["deit_t"], B=1)
+    q, k, v, w = to_device(inp)
+    before = q.clone()
+    with pytest.raises(m.MhlaError) as ei:
+        m.mhla_forward(q, k, v, w, q, (inp.wl.grid, inp.wl.block), inp.wl.phi)
+    assert ei.value.code == m.MHLA_ERR_ALIAS
+    out = torch.empty_like(q)
+    with pytest.raises(m.MhlaError) as ei:
+        m.mhla_forward(q, k, v, w, out, ((1, 14, 14), (1, 4, 7)), inp.wl.phi)
+    assert ei.value.code == m.MHLA_ERR_SHAPE
+    wl = WORKLOADS["video"]
+    with pytest.raises(m.MhlaError) as ei:   # fused cannot hold 196 tokens x M=49... -> check
+        m.mhla_forward_path(q, k, v, w, out, ((1, 14, 14), (1, 2, 2)), inp.wl.phi,
+                            m.MHLA_PATH_FUSED)
+    assert ei.value.code in (m.MHLA_ERR_UNSUPPORTED, m.MHLA_ERR_ALIAS)
+    torch.cuda.synchronize()
+    assert torch.equal(q.view(torch.int16), before.view(torch.int16))

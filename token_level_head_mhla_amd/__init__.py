@@ -1,0 +1,17 @@
+"""MI355X (gfx950) forward pass of MHLA -- Multi-Head Linear Attention with
+token-level heads ("MHLA: Restoring Expressivity of Linear Attention via
+Token-Level Multi-Head", §4.1).
+
+The compute lives in ``libmhla.so`` (hand-written HIP kernels behind the C
+ABI of ``include/mhla.h``).  This package is a thin ctypes binding whose
+functions carry the C names; it only marshals arguments.  Building the
+library: ``python -m token_level_head_mhla_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    MHLA_DTYPE_BF16, MHLA_DTYPE_F32, MHLA_ERR_ALIAS, MHLA_ERR_HIP, MHLA_ERR_INVALID_ARG,
+    MHLA_ERR_SHAPE, MHLA_ERR_UNSUPPORTED, MHLA_OK, MHLA_PATH_AUTO, MHLA_PATH_FUSED,
+    MHLA_PATH_GENERIC, MHLA_PATH_PAIRS, MHLA_PHI_ELU1, MHLA_PHI_RELU, MhlaError, BlockShape,
+    EXPORTED_SYMBOLS, library_path, load_library, mhla_error_string, mhla_forward,
+    mhla_forward_path, mhla_last_error, mhla_num_blocks, mhla_plan, mhla_release,
+    mhla_validate, mhla_workspace_bytes,
+)

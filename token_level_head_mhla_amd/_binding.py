@@ -1,0 +1,182 @@
+"""ctypes binding of libmhla (names and arguments mirror include/mhla.h).
+
+Tensors are torch tensors already on the GPU; the binding passes their
+device pointers and the current HIP stream.  Nothing here computes: when the
+library is missing the calls raise instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+MHLA_PHI_RELU, MHLA_PHI_ELU1 = 0, 1
+MHLA_DTYPE_F32, MHLA_DTYPE_BF16 = 0, 1
+(MHLA_OK, MHLA_ERR_INVALID_ARG, MHLA_ERR_SHAPE, MHLA_ERR_UNSUPPORTED, MHLA_ERR_HIP,
+ MHLA_ERR_ALIAS) = range(6)
+MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS = range(4)
+
+EXPORTED_SYMBOLS = (
+    "mhla_forward", "mhla_forward_path", "mhla_validate", "mhla_plan", "mhla_num_blocks",
+    "mhla_workspace_bytes", "mhla_error_string", "mhla_last_error", "mhla_release",
+)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmhla.so")
+_lib = None
+
+
+class MhlaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("mhla error %d (%s): %s" % (code, mhla_error_string(code), message))
+        self.code = code
+
+
+class BlockShape(ctypes.Structure):
+    """mhla_block_shape: grid (T, Hg, Wg) and block (bt, bh, bw)."""
+    _fields_ = [("ndim", ctypes.c_int), ("grid", ctypes.c_int * 3), ("block", ctypes.c_int * 3)]
+
+    @classmethod
+    def make(cls, grid: Sequence[int], block: Sequence[int], ndim: Optional[int] = None):
+        g = tuple(int(x) for x in grid)
+        b = tuple(int(x) for x in block)
+        if len(g) != len(b):
+            raise ValueError("grid and block need the same number of axes")
+        if ndim is None:
+            ndim = len(g)
+        g = (1,) * (3 - len(g)) + g
+        b = (1,) * (3 - len(b)) + b
+        return cls(int(ndim), (ctypes.c_int * 3)(*g), (ctypes.c_int * 3)(*b))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmhla.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libmhla.so is not built: run `python -m token_level_head_mhla_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ip = ctypes.c_void_p, ctypes.c_int
+    bsp = ctypes.POINTER(BlockShape)
+    lib.mhla_forward.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, vp]
+    lib.mhla_forward.restype = ip
+    lib.mhla_forward_path.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, vp]
+    lib.mhla_forward_path.restype = ip
+    lib.mhla_validate.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
+    lib.mhla_validate.restype = ip
+    lib.mhla_plan.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
+    lib.mhla_plan.restype = ip
+    lib.mhla_num_blocks.argtypes = [ip, bsp]
+    lib.mhla_num_blocks.restype = ip
+    lib.mhla_workspace_bytes.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
+    lib.mhla_workspace_bytes.restype = ctypes.c_size_t
+    lib.mhla_error_string.argtypes = [ip]
+    lib.mhla_error_string.restype = ctypes.c_char_p
+    lib.mhla_last_error.argtypes = []
+    lib.mhla_last_error.restype = ctypes.c_char_p
+    lib.mhla_release.argtypes = []
+    lib.mhla_release.restype = None
+    _lib = lib
+    return lib
+
+
+def mhla_error_string(code: int) -> str:
+    return load_library().mhla_error_string(int(code)).decode()
+
+
+def mhla_last_error() -> str:
+    return load_library().mhla_last_error().decode()
+
+
+def _shape(block_shape) -> BlockShape:
+    if isinstance(block_shape, BlockShape):
+        return block_shape
+    grid, block = block_shape
+    return BlockShape.make(grid, block)
+
+
+def mhla_validate(B, H, N, d, block_shape, phi_kind, dtype) -> int:
+    return int(load_library().mhla_validate(B, H, N, d, ctypes.byref(_shape(block_shape)),
+                                            phi_kind, dtype))
+
+
+def mhla_plan(B, H, N, d, block_shape, phi_kind, dtype) -> int:
+    return int(load_library().mhla_plan(B, H, N, d, ctypes.byref(_shape(block_shape)), phi_kind,
+                                        dtype))
+
+
+def mhla_num_blocks(N, block_shape) -> int:
+    return int(load_library().mhla_num_blocks(N, ctypes.byref(_shape(block_shape))))
+
+
+def mhla_workspace_bytes(B, H, N, d, block_shape, dtype, path=MHLA_PATH_AUTO) -> int:
+    return int(load_library().mhla_workspace_bytes(B, H, N, d, ctypes.byref(_shape(block_shape)),
+                                                   dtype, path))
+
+
+def mhla_release() -> None:
+    load_library().mhla_release()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MHLA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MHLA_DTYPE_BF16
+    raise TypeError("Q/K/V must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _check_tensors(Q, K, V, W, out):
+    import torch
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("Wmix", W), ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape or out.shape != Q.shape:
+        raise ValueError("Q, K, V, out must share one [B,H,N,d] shape")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype or out.dtype != Q.dtype:
+        raise ValueError("Q, K, V, out must share one dtype")
+    if W.dtype != torch.float32:
+        raise ValueError("Wmix must be float32")
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def mhla_forward_path(Q, K, V, Wmix, out, block_shape, phi_kind, path, stream=None):
+    """Enqueue the forward on `stream` (default: torch's current stream)."""
+    _check_tensors(Q, K, V, Wmix, out)
+    B, H, N, d = Q.shape
+    bs = _shape(block_shape)
+    rc = load_library().mhla_forward_path(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
+        ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(path), _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return out
+
+
+def mhla_forward(Q, K, V, Wmix, out, block_shape, phi_kind, stream=None):
+    """Enqueue the forward with the library's path choice."""
+    _check_tensors(Q, K, V, Wmix, out)
+    B, H, N, d = Q.shape
+    bs = _shape(block_shape)
+    rc = load_library().mhla_forward(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
+        ctypes.byref(bs), int(phi_kind), _dtype_code(Q), _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return out

@@ -1,0 +1,297 @@
+// mhla_api.hip -- C ABI of libmhla: argument checks, path choice, workspace
+// cache and kernel launches for the MHLA forward (gfx950).
+//
+// The operation is the forward pass of "MHLA: Restoring Expressivity of
+// Linear Attention via Token-Level Multi-Head" §4.1 (summaries, multi-head
+// mixing, readout); the entry points are declared and documented in mhla.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "mhla.h"
+#include "mhla_common.hpp"
+#include "k_generic.hpp"
+#include "k_fused.hpp"
+
+namespace mhla {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+struct Problem {
+  int B, H, N, d, phi, dtype;
+  Geo g;
+  long slices() const { return (long)B * H; }
+  size_t elt() const { return dtype == MHLA_DTYPE_F32 ? 4 : 2; }
+  size_t tensor_bytes() const { return (size_t)B * H * N * d * elt(); }
+};
+
+int check(int B, int H, int N, int d, const mhla_block_shape* s, int phi, int dtype,
+          Problem* p) {
+  g_last_error.clear();
+  if (s == nullptr) return fail(MHLA_ERR_INVALID_ARG, "block_shape is NULL");
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(MHLA_ERR_INVALID_ARG, "B=%d H=%d N=%d d=%d: all must be positive", B, H, N, d);
+  if (phi != MHLA_PHI_RELU && phi != MHLA_PHI_ELU1)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown phi_kind %d", phi);
+  if (dtype != MHLA_DTYPE_F32 && dtype != MHLA_DTYPE_BF16)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (s->ndim < 1 || s->ndim > 3)
+    return fail(MHLA_ERR_SHAPE, "block_shape.ndim=%d must be 1, 2 or 3", s->ndim);
+  long n = 1;
+  for (int a = 0; a < 3; ++a) {
+    const int gd = s->grid[a], bd = s->block[a];
+    if (gd <= 0 || bd <= 0)
+      return fail(MHLA_ERR_SHAPE, "grid[%d]=%d block[%d]=%d must be positive", a, gd, a, bd);
+    if (a < 3 - s->ndim && (gd != 1 || bd != 1))
+      return fail(MHLA_ERR_SHAPE, "axis %d is unused for ndim=%d but grid/block are %d/%d", a,
+                  s->ndim, gd, bd);
+    if (gd % bd != 0)
+      return fail(MHLA_ERR_SHAPE, "block[%d]=%d does not divide grid[%d]=%d", a, bd, a, gd);
+    n *= gd;
+  }
+  if (n != N)
+    return fail(MHLA_ERR_SHAPE, "grid %dx%dx%d has %ld tokens but N=%d", s->grid[0], s->grid[1],
+                s->grid[2], n, N);
+  if (d > 128) return fail(MHLA_ERR_UNSUPPORTED, "d=%d > 128 is not supported", d);
+  if (dtype == MHLA_DTYPE_BF16 && d % 8 != 0)
+    return fail(MHLA_ERR_UNSUPPORTED, "bf16 needs d to be a multiple of 8 (d=%d)", d);
+  if ((long)B * H > 0x7fffffffL) return fail(MHLA_ERR_UNSUPPORTED, "too many slices");
+  if (p) {
+    Geo& g = p->g;
+    g.T = s->grid[0]; g.Hg = s->grid[1]; g.Wg = s->grid[2];
+    g.bt = s->block[0]; g.bh = s->block[1]; g.bw = s->block[2];
+    g.nbz = g.T / g.bt; g.nby = g.Hg / g.bh; g.nbx = g.Wg / g.bw;
+    g.M = g.nbz * g.nby * g.nbx;
+    g.nb = g.bt * g.bh * g.bw;
+    p->B = B; p->H = H; p->N = N; p->d = d; p->phi = phi; p->dtype = dtype;
+    if ((long)g.M * g.M * H > 0x7fffffffL)
+      return fail(MHLA_ERR_UNSUPPORTED, "M=%d is too large", g.M);
+  }
+  return MHLA_OK;
+}
+
+bool path_supports(int path, const Problem& p) {
+  switch (path) {
+    case MHLA_PATH_GENERIC: return p.slices() <= 65535;  // slices run along grid y/z
+    case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
+    default: return false;
+  }
+}
+
+int choose_path(const Problem& p) {
+  if (path_supports(MHLA_PATH_FUSED, p)) return MHLA_PATH_FUSED;
+  if (path_supports(MHLA_PATH_GENERIC, p)) return MHLA_PATH_GENERIC;
+  return -MHLA_ERR_UNSUPPORTED;
+}
+
+size_t workspace_for(const Problem& p, int path) {
+  if (path == MHLA_PATH_GENERIC) {
+    const size_t L = (size_t)p.d * p.d + p.d;
+    return 2 * (size_t)p.slices() * p.g.M * L * sizeof(float);
+  }
+  return 0;
+}
+
+// Library-owned workspaces, one per (device, stream): calls on one stream are
+// ordered, so reuse across calls is safe; different streams never share.
+struct Buf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, Buf> g_ws;
+
+int get_workspace(size_t need, hipStream_t stream, void** out) {
+  *out = nullptr;
+  if (need == 0) return MHLA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MHLA_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Buf& b = g_ws[std::make_pair(dev, (void*)stream)];
+  if (b.bytes < need) {
+    if (b.ptr) {
+      // The previous buffer may still be read by work queued on this stream.
+      if (hipStreamSynchronize(stream) != hipSuccess)
+        return fail(MHLA_ERR_HIP, "hipStreamSynchronize failed while growing the workspace");
+      (void)hipFree(b.ptr);
+      b.ptr = nullptr;
+      b.bytes = 0;
+    }
+    size_t want = need + need / 8;
+    hipError_t e = hipMalloc(&b.ptr, want);
+    if (e != hipSuccess) {
+      b.ptr = nullptr;
+      return fail(MHLA_ERR_HIP, "hipMalloc(%zu) for the workspace failed: %s", want,
+                  hipGetErrorString(e));
+    }
+    b.bytes = want;
+  }
+  *out = b.ptr;
+  return MHLA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+template <typename T>
+int launch_generic(const Problem& p, const T* Q, const T* K, const T* V, const float* W,
+                   T* Y, float* ws, hipStream_t st) {
+  const int M = p.g.M, d = p.d;
+  const int L = d * d + d;
+  float* S = ws;
+  float* St = ws + (size_t)p.slices() * M * L;
+  const unsigned nsl = (unsigned)p.slices();
+  k_summary_valu<T><<<dim3(M, nsl), kValuThreads, 0, st>>>(K, V, S, p.g, p.N, d, p.phi);
+  k_mix_valu<<<dim3((L + kValuThreads - 1) / kValuThreads, (M + kMixRows - 1) / kMixRows, nsl),
+               kValuThreads, 0, st>>>(S, W, St, M, L, p.H);
+  k_readout_valu<T><<<dim3(M, nsl), kValuThreads, 0, st>>>(Q, St, Y, p.g, p.N, d, p.phi);
+  return MHLA_OK;
+}
+
+int run(const void* Q, const void* K, const void* V, const float* W, void* out, int B, int H,
+        int N, int d, const mhla_block_shape* shape, int phi, int dtype, int path,
+        void* stream) {
+  Problem p;
+  int rc = check(B, H, N, d, shape, phi, dtype, &p);
+  if (rc != MHLA_OK) return rc;
+  if (!Q || !K || !V || !W || !out)
+    return fail(MHLA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  const void* ptrs[5] = {Q, K, V, W, out};
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return fail(MHLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t tb = p.tensor_bytes();
+  if (overlaps(out, tb, Q, tb) || overlaps(out, tb, K, tb) || overlaps(out, tb, V, tb))
+    return fail(MHLA_ERR_ALIAS, "out overlaps Q, K or V");
+  if (overlaps(out, tb, W, (size_t)H * p.g.M * p.g.M * sizeof(float)))
+    return fail(MHLA_ERR_ALIAS, "out overlaps Wmix");
+  if (path == MHLA_PATH_AUTO) path = choose_path(p);
+  if (path < 0 || !path_supports(path, p))
+    return fail(MHLA_ERR_UNSUPPORTED, "path %d does not support this shape/dtype", path);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  void* ws = nullptr;
+  rc = get_workspace(workspace_for(p, path), st, &ws);
+  if (rc != MHLA_OK) return rc;
+
+  if (path == MHLA_PATH_GENERIC) {
+    if (dtype == MHLA_DTYPE_F32)
+      rc = launch_generic<float>(p, (const float*)Q, (const float*)K, (const float*)V, W,
+                                 (float*)out, (float*)ws, st);
+    else
+      rc = launch_generic<bf16_t>(p, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, W,
+                                  (bf16_t*)out, (float*)ws, st);
+  } else if (path == MHLA_PATH_FUSED) {
+    rc = launch_fused(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
+                      (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, st);
+  }
+  if (rc != MHLA_OK) return rc;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MHLA_OK;
+}
+
+}  // namespace
+}  // namespace mhla
+
+using namespace mhla;
+
+extern "C" {
+
+int mhla_forward(const void* Q, const void* K, const void* V, const float* Wmix, void* out,
+                 int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
+                 int dtype, void* stream) {
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, MHLA_PATH_AUTO,
+             stream);
+}
+
+int mhla_forward_path(const void* Q, const void* K, const void* V, const float* Wmix,
+                      void* out, int B, int H, int N, int d,
+                      const mhla_block_shape* block_shape, int phi_kind, int dtype, int path,
+                      void* stream) {
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_PAIRS)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, path, stream);
+}
+
+int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
+                  int dtype) {
+  Problem p;
+  return check(B, H, N, d, block_shape, phi_kind, dtype, &p);
+}
+
+int mhla_plan(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
+              int dtype) {
+  Problem p;
+  int rc = check(B, H, N, d, block_shape, phi_kind, dtype, &p);
+  if (rc != MHLA_OK) return -rc;
+  return choose_path(p);
+}
+
+int mhla_num_blocks(int N, const mhla_block_shape* block_shape) {
+  Problem p;
+  int rc = check(1, 1, N, 8, block_shape, MHLA_PHI_RELU, MHLA_DTYPE_F32, &p);
+  if (rc != MHLA_OK) return -rc;
+  return p.g.M;
+}
+
+size_t mhla_workspace_bytes(int B, int H, int N, int d, const mhla_block_shape* block_shape,
+                            int dtype, int path) {
+  Problem p;
+  if (check(B, H, N, d, block_shape, MHLA_PHI_RELU, dtype, &p) != MHLA_OK) return 0;
+  if (path == MHLA_PATH_AUTO) path = choose_path(p);
+  if (path < 0 || !path_supports(path, p)) return 0;
+  return workspace_for(p, path);
+}
+
+const char* mhla_error_string(int code) {
+  switch (code) {
+    case MHLA_OK: return "ok";
+    case MHLA_ERR_INVALID_ARG: return "invalid argument";
+    case MHLA_ERR_SHAPE: return "invalid block shape";
+    case MHLA_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case MHLA_ERR_HIP: return "HIP runtime error";
+    case MHLA_ERR_ALIAS: return "output aliases an input";
+    default: return "unknown error code";
+  }
+}
+
+const char* mhla_last_error(void) { return g_last_error.c_str(); }
+
+void mhla_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  const bool have_dev = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    if (hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.ptr);
+    }
+  }
+  g_ws.clear();
+  if (have_dev) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"
