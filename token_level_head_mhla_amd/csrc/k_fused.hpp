@@ -1,294 +1,315 @@
-// k_fused.hpp -- single-kernel MHLA forward for small M (bf16, gfx950 MFMA).
+// k_fused.hpp -- single-kernel MHLA forward for small M (bf16 in/out, gfx950).
 //
-// One workgroup per (batch, head) slice and one wave per block.  The whole
-// forward of "MHLA: Restoring Expressivity of Linear Attention via
-// Token-Level Multi-Head" §4.1 runs on chip:
-//   1. phi(K) and V of every block are staged in LDS, transposed to
-//      [feature][token] so that MFMA operands read 8 consecutive tokens;
-//   2. wave b forms S_b = phi(K_b)^T V_b with v_mfma_f32_16x16x32_bf16
-//      (fp32 accumulate) and z_b by summing its phi(K) rows;
-//   3. the summaries are exchanged through LDS and wave i mixes
-//      S~_i = sum_b W[i,b] S_b, z~_i = sum_b W[i,b] z_b in fp32 registers;
-//   4. wave i reads its query block out as Y^T = S~_i^T phi(Q_i)^T on MFMA,
-//      with the denominator phi(q).z~_i reduced across the wave, and the
-//      divide fused before the bf16 store.
-// S, S~ and z never reach HBM: the kernel reads Q, K, V, W and writes Y.
+// One workgroup of 8 waves per (batch, head) slice.  The whole forward of
+// "MHLA: Restoring Expressivity of Linear Attention via Token-Level
+// Multi-Head" §4.1 runs on chip, and HBM sees only Q, K, V, W and Y:
 //
-// MFMA operand conventions used here (16x16x32 bf16): lane l holds row
-// (l % 16) of A, column (l % 16) of B, and 8 contraction elements chosen by
-// lane group l / 16; A and B share that choice, so any fixed assignment of
-// contraction indices to (group, element) gives the same sum.  The result
-// lane l holds D[4*(l/16) + i][l % 16], i = 0..3.  A result tile can thus be
-// reused as an A operand of a later product whose contraction runs over the
-// tile's rows: two row-adjacent 16x16 tiles give the 8 elements
-// {4g..4g+3} and {16+4g..16+4g+3}; the other operand uses the same indices.
+//   0. token <-> LDS-row tables: the rows of block b are b*NBP .. b*NBP+nb-1
+//      (raster order inside the tile, Fig. 4b numbering of the blocks); rows
+//      nb .. NBP-1 of every block are zero padding.
+//   A. K and V of the slice are read with 16-byte coalesced loads (the slice
+//      is contiguous), phi is applied to K in registers (bf16 result), and
+//      both are written to LDS row-major in block order.
+//   B. Work item (ct, ks) = value columns 16ct..16ct+15 and key features
+//      32ks..32ks+31.  For every key block b the wave forms the two 16x16
+//      tiles of S_b = phi(K_b)^T V_b with v_mfma_f32_16x16x32_bf16, both
+//      operands taken from LDS with transpose reads, and immediately mixes
+//      them into every query block's S~_i += W[i,b] S_b (fp32 registers).
+//      The normaliser z_b = sum phi(K_b) rides along as one more column
+//      tile (B operand = a column of ones), so z~_i = sum_b W[i,b] z_b comes
+//      out of the same mixing.  The mixed tiles are packed to bf16 in the
+//      A-operand layout of the readout and exchanged through LDS.
+//   D. Work item (i, qt) = 16 queries of block i.  Y^T = S~_i^T phi(Q)^T on
+//      MFMA; the extra z~ tile gives the denominator phi(q).z~_i as row d of
+//      the same product; the divide and the bf16 rounding are fused into the
+//      8-byte stores.  Q is prefetched at kernel start.
+//
+// A denominator of exactly 0 (ReLU with phi(q) = 0) writes a zero row.
 #pragma once
 
-#include "mhla_common.hpp"
+#include "mhla_mfma.hpp"
 
 namespace mhla {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16x16x32(const u16x8_t& a, const u16x8_t& b,
-                                                const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
+constexpr int kFusedThreads = 512;
+constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kFusedMaxM = 8;
+constexpr size_t kLdsLimit = 160 * 1024;
 
 template <int DP, int NBP>
-constexpr size_t fused_lds_bytes(int M) {
-  // max(staged phi(K)^T and V^T, exchanged summaries + normalisers)
-  return (size_t)M * ((size_t)2 * DP * (NBP + 8) * 2 > (size_t)DP * DP * 4 + DP * 4
-                          ? (size_t)2 * DP * (NBP + 8) * 2
-                          : (size_t)DP * DP * 4 + DP * 4);
-}
+struct FusedLayout {
+  static constexpr int RS = DP + 8;        // LDS row stride of phi(K) and V (elements)
+  static constexpr int NT = DP / 16;       // value-column tiles
+  static constexpr int DS = DP / 32;       // 32-feature contraction steps
+  static constexpr int KS = NBP / 32;      // 32-token contraction steps per block
+  static constexpr int QT = NBP / 16;      // query tiles per block
+  // byte offsets for M blocks
+  __host__ __device__ static size_t kv_bytes(int M) { return (size_t)2 * M * NBP * RS * 2; }
+  __host__ __device__ static size_t frag_bytes(int M) { return (size_t)M * (NT + 1) * DS * 64 * 16; }
+  __host__ __device__ static size_t tab_off(int M) {
+    const size_t a = kv_bytes(M), b = frag_bytes(M);
+    return (a > b ? a : b);
+  }
+  __host__ __device__ static size_t w_off(int M) { return tab_off(M) + (size_t)2 * 2 * M * NBP; }
+  __host__ __device__ static size_t total(int M) { return w_off(M) + (size_t)4 * M * M; }
+};
 
-// grid = B*H; block = 64*M threads; dynamic LDS = fused_lds_bytes<DP,NBP>(M).
-template <int DP, int NBP>
-__global__ __launch_bounds__(64 * kFusedMaxM) void k_fused(
+template <int DP, int NBP, int MM, int PHI>
+__global__ __launch_bounds__(kFusedThreads) void k_fused(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, int H, int N, int d, int phi) {
+    const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, int H, int N, int d) {
+  using L = FusedLayout<DP, NBP>;
+  constexpr int RS = L::RS, NT = L::NT, DS = L::DS, KS = L::KS, QT = L::QT;
+  constexpr int TPW = (MM * QT + kFusedWaves - 1) / kFusedWaves;  // query tiles per wave
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int RS = NBP + 8;   // LDS row length (bf16) of the transposed tiles
-  constexpr int NT = DP / 16;   // 16-wide tiles along d
-  constexpr int KS = NBP / 32;  // contraction steps of the summary
-  constexpr int DS = DP / 32;   // contraction steps of the readout
-  constexpr int QT = NBP / 16;  // query row tiles
   const int M = g.M, nb = g.nb;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int s = lane & 15, grp = lane >> 4;
   const long slice = blockIdx.x;
   const int h = (int)(slice % H);
-  const bf16_t* Qs = Q + slice * (long)N * d;
-  const bf16_t* Ks = K + slice * (long)N * d;
-  const bf16_t* Vs = V + slice * (long)N * d;
-  bf16_t* Ys = Y + slice * (long)N * d;
+  const size_t off = (size_t)slice * N * d;
 
-  // 0. Prefetch this wave's query rows in the readout's B-operand layout.
-  uint2 qraw[QT][DS][2];
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* sV = sK + (size_t)M * NBP * RS;
+  u16x8_t* frag = reinterpret_cast<u16x8_t*>(smem);  // aliases sK/sV after phase B
+  uint16_t* rowtab = reinterpret_cast<uint16_t*>(smem + L::tab_off(M));  // token -> row
+  uint16_t* toktab = rowtab + M * NBP;                                     // row -> token
+  float* sW = reinterpret_cast<float*>(smem + L::w_off(M));
+
+  // ---- 0. tables, W, zero padding -----------------------------------------
+  for (int r = tid; r < M * NBP; r += kFusedThreads) toktab[r] = 0xffff;
+  for (int e = tid; e < M * M; e += kFusedThreads) sW[e] = W[(size_t)h * M * M + e];
+  if (d < DP) {
+    const int chunks = 2 * M * NBP * RS / 8;
+    for (int e = tid; e < chunks; e += kFusedThreads)
+      reinterpret_cast<uint4*>(sK)[e] = make_uint4(0u, 0u, 0u, 0u);
+  } else if (nb < NBP) {
+    constexpr int F8 = DP / 8;
+    const int pad = NBP - nb;
+    for (int e = tid; e < 2 * M * pad * F8; e += kFusedThreads) {
+      const int f = e % F8, r = (e / F8) % pad, b = e / (F8 * pad);
+      bf16_t* base = b < M ? sK : sV;
+      const int bb = b < M ? b : b - M;
+      *reinterpret_cast<uint4*>(base + (bb * NBP + nb + r) * RS + 8 * f) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < N; t += kFusedThreads) {
+    const int x = t % g.Wg, y = (t / g.Wg) % g.Hg, z = t / (g.Wg * g.Hg);
+    const int b = ((z / g.bt) * g.nby + y / g.bh) * g.nbx + x / g.bw;
+    const int j = ((z % g.bt) * g.bh + y % g.bh) * g.bw + x % g.bw;
+    const int r = b * NBP + j;
+    rowtab[t] = (uint16_t)r;
+    toktab[r] = (uint16_t)t;
+  }
+  __syncthreads();
+
+  // ---- prefetch this wave's queries (acc8 B-operand layout) ----------------
+  uint2 qraw[TPW][DS][2];
 #pragma unroll
-  for (int mt = 0; mt < QT; ++mt) {
-    const int j = 16 * mt + col;
-    const bool ok = j < nb;
-    const long t = ok ? g.token(wave, j) : 0;
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave + u * kFusedWaves;
+    int t = 0xffff;
+    if (tile < M * QT) t = toktab[(tile / QT) * NBP + (tile % QT) * 16 + s];
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
+    for (int ks = 0; ks < DS; ++ks)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int k0 = 32 * ks + 16 * hh + 4 * grp;
-        qraw[mt][ks][hh] = (ok && k0 < d) ? *reinterpret_cast<const uint2*>(Qs + t * d + k0)
-                                          : make_uint2(0u, 0u);
+        qraw[u][ks][hh] = (t != 0xffff && k0 < d)
+                              ? *reinterpret_cast<const uint2*>(Q + off + (size_t)t * d + k0)
+                              : make_uint2(0u, 0u);
       }
-    }
   }
 
-  // 1. Stage phi(K)^T and V^T of all blocks: KT[b][f][j], VT[b][f][j].  Pads
-  //    (j >= nb or f >= d) are zero, which leaves S and z exact.
-  bf16_t* KT = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* VT = KT + (size_t)M * DP * RS;
+  // ---- A. stage phi(K) and V ---------------------------------------------
   {
-    constexpr int F8 = DP / 8;
-    const int total = M * NBP * F8;
-    const int nf8 = d / 8;
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-      const int f8 = e % F8;
-      const int j = (e / F8) % NBP;
-      const int b = e / (F8 * NBP);
-      uint4 kr = make_uint4(0u, 0u, 0u, 0u), vr = kr;
-      const bool ok = j < nb && f8 < nf8;
-      if (ok) {
-        const long t = g.token(b, j);
-        kr = *reinterpret_cast<const uint4*>(Ks + t * d + 8 * f8);
-        vr = *reinterpret_cast<const uint4*>(Vs + t * d + 8 * f8);
-      }
-      const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-      const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
-      bf16_t* kdst = KT + ((size_t)b * DP + 8 * f8) * RS + j;
-      bf16_t* vdst = VT + ((size_t)b * DP + 8 * f8) * RS + j;
+    const int F8 = d >> 3;
+    const int items = N * F8;
+    const float inv = 1.0f / (float)F8;
+    constexpr int U = 4;
+    for (int base = 0; base < items; base += U * kFusedThreads) {
+      uint4 kr[U], vr[U];
+      int it[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bf16_t kb = (bf16_t)(kw[u >> 1] >> (16 * (u & 1)));
-        const bf16_t vb = (bf16_t)(vw[u >> 1] >> (16 * (u & 1)));
-        kdst[u * RS] = ok ? f32_to_bf16(phi_apply(phi, bf16_to_f32(kb))) : (bf16_t)0;
-        vdst[u * RS] = vb;
+      for (int u = 0; u < U; ++u) {
+        // clamped so that every lane loads (straight-line, all loads in flight)
+        it[u] = base + u * kFusedThreads + tid;
+        const size_t src = off + (size_t)min(it[u], items - 1) * 8;
+        kr[u] = *reinterpret_cast<const uint4*>(K + src);
+        vr[u] = *reinterpret_cast<const uint4*>(V + src);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (it[u] < items) {
+          const int t = (int)(((float)it[u] + 0.5f) * inv);
+          const int f = it[u] - t * F8;
+          const int r = rowtab[t];
+          *reinterpret_cast<uint4*>(sK + r * RS + 8 * f) = phi8<PHI>(kr[u]);
+          *reinterpret_cast<uint4*>(sV + r * RS + 8 * f) = vr[u];
+        }
       }
     }
   }
   __syncthreads();
 
-  // 2. Summary of key block b = wave: acc[kt][ct] is the 16x16 tile
-  //    S[16kt .. +15][16ct .. +15] with S[k][c] = sum_j phiK[j][k] V[j][c].
-  f32x4_t acc[NT][NT];
+  // ---- B. summaries, mixing ----------------------------------------------
+  // Each wave owns at most one (ct, ks) item when NT*DS <= 8 (all shapes this
+  // kernel accepts); waves without an item idle until the exchange.
+  const int item = wave;
+  const bool has_item = item < NT * DS;
+  const int ct = item % NT, ksB = item / NT;
+  const bool ztile = has_item && ct == 0;
+  f32x4_t mix[MM][2], zmix[MM][2];
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt)
+  for (int i = 0; i < MM; ++i) {
+    mix[i][0] = mix[i][1] = zero4();
+    zmix[i][0] = zmix[i][1] = zero4();
+  }
+  if (has_item) {
+    const uint16_t one = 0x3f80;  // bf16 1.0
+    const uint16_t ov = s == 0 ? one : (uint16_t)0;
+    const u16x8_t ones = {ov, ov, ov, ov, ov, ov, ov, ov};
+    for (int b = 0; b < M; ++b) {
+      f32x4_t sb[2] = {zero4(), zero4()}, zb[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  {
-    const bf16_t* KTb = KT + (size_t)wave * DP * RS;
-    const bf16_t* VTb = VT + (size_t)wave * DP * RS;
+      for (int st = 0; st < KS; ++st) {
+        const int r0 = b * NBP + 32 * st;
+        const u16x8_t bv = lds_tr8(sV, RS, r0, 16 * ct, lane);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u16x8_t a[NT], bv[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        a[t] = *reinterpret_cast<const u16x8_t*>(KTb + (16 * t + col) * RS + 32 * ks + 8 * grp);
-        bv[t] = *reinterpret_cast<const u16x8_t*>(VTb + (16 * t + col) * RS + 32 * ks + 8 * grp);
+        for (int hh = 0; hh < 2; ++hh) {
+          const u16x8_t a = lds_tr8(sK, RS, r0, 32 * ksB + 16 * hh, lane);
+          sb[hh] = mfma_bf16(a, bv, sb[hh]);
+          if (ztile) zb[hh] = mfma_bf16(a, ones, zb[hh]);
+        }
       }
 #pragma unroll
-      for (int kt = 0; kt < NT; ++kt)
+      for (int i = 0; i < MM; ++i) {
+        if (i < M) {
+          const float w = sW[i * M + b];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) acc[kt][ct] = mfma16x16x32(a[kt], bv[ct], acc[kt][ct]);
+          for (int hh = 0; hh < 2; ++hh) {
+            mix[i][hh] += w * sb[hh];
+            if (ztile) zmix[i][hh] += w * zb[hh];
+          }
+        }
+      }
     }
   }
-  // z_b[k] for k = lane, from the same rounded phi(K) the products used.
-  float zb = 0.0f;
-  if (lane < DP) {
-    const bf16_t* row = KT + ((size_t)wave * DP + lane) * RS;
+  __syncthreads();  // every wave is done reading sK / sV
+  if (has_item) {
 #pragma unroll
-    for (int j8 = 0; j8 < NBP / 8; ++j8) {
-      const u16x8_t v8 = *reinterpret_cast<const u16x8_t*>(row + 8 * j8);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) zb += bf16_to_f32(v8[u]);
+    for (int i = 0; i < MM; ++i) {
+      if (i < M) {
+        frag[((i * (NT + 1) + ct) * DS + ksB) * 64 + lane] = pack_acc8(mix[i][0], mix[i][1]);
+        if (ztile)
+          frag[((i * (NT + 1) + NT) * DS + ksB) * 64 + lane] = pack_acc8(zmix[i][0], zmix[i][1]);
+      }
     }
   }
-  __syncthreads();  // every wave is done with KT/VT; the region is reused below
-
-  // 3. Exchange: SX[b][tile][lane][4] (fp32), ZX[b][k].
-  float* SX = reinterpret_cast<float*>(smem);
-  float* ZX = SX + (size_t)M * NT * NT * 256;
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-      *reinterpret_cast<f32x4_t*>(SX + (((size_t)wave * NT * NT + kt * NT + ct) * 64 + lane) * 4) =
-          acc[kt][ct];
-  if (lane < DP) ZX[wave * DP + lane] = zb;
   __syncthreads();
 
-  // 4. Mixing for query block i = wave (row i of W).
-  const float* Wi = W + ((size_t)h * M + wave) * M;
-  f32x4_t zt[DS][2];
+  // ---- D. readout ----------------------------------------------------------
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[kt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < DS; ++ks) zt[ks][0] = zt[ks][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < M; ++b) {
-    const float w = Wi[b];
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-        acc[kt][ct] += w * *reinterpret_cast<const f32x4_t*>(
-                               SX + (((size_t)b * NT * NT + kt * NT + ct) * 64 + lane) * 4);
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        zt[ks][hh] += w * *reinterpret_cast<const f32x4_t*>(ZX + b * DP + 32 * ks + 16 * hh + 4 * grp);
-  }
-
-  // 5. Readout.  A operand: rows c of S~^T, i.e. S~[k][c] for the lane's
-  //    contraction indices k = 32ks + {4g..4g+3, 16+4g..16+4g+3}.
-  u16x8_t afr[NT][DS];
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        afr[ct][ks][u] = f32_to_bf16(acc[2 * ks][ct][u]);
-        afr[ct][ks][u + 4] = f32_to_bf16(acc[2 * ks + 1][ct][u]);
-      }
-#pragma unroll
-  for (int mt = 0; mt < QT; ++mt) {
-    if (16 * mt >= nb) break;
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave + u * kFusedWaves;
+    if (tile >= M * QT) break;
+    const int i = tile / QT, qt = tile % QT;
+    if (qt * 16 >= nb) continue;
     u16x8_t bq[DS];
-    float den = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
+    for (int ks = 0; ks < DS; ++ks)
+      bq[ks] = from_u2x2(phi4<PHI>(qraw[u][ks][0]), phi4<PHI>(qraw[u][ks][1]));
+    f32x4_t o[NT + 1];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t w2[2] = {qraw[mt][ks][hh].x, qraw[mt][ks][hh].y};
-        const bool kin = 32 * ks + 16 * hh + 4 * grp < d;
+    for (int c = 0; c <= NT; ++c) {
+      o[c] = zero4();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16_t qb = (bf16_t)(w2[u >> 1] >> (16 * (u & 1)));
-          const bf16_t pq = kin ? f32_to_bf16(phi_apply(phi, bf16_to_f32(qb))) : (bf16_t)0;
-          bq[ks][4 * hh + u] = pq;
-          den += bf16_to_f32(pq) * zt[ks][hh][u];
-        }
-      }
+      for (int ks = 0; ks < DS; ++ks)
+        o[c] = mfma_bf16(frag[((i * (NT + 1) + c) * DS + ks) * 64 + lane], bq[ks], o[c]);
     }
-    den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
-    const int j = 16 * mt + col;
-    const bool ok = j < nb;
-    const long t = ok ? g.token(wave, j) : 0;
+    // row d of the product (lane s of group 0, element 0) is phi(q).z~_i
+    const float den = __shfl(o[NT][0], s);
+    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+    const int j = qt * 16 + s;
+    if (j < nb) {
+      const int t = toktab[i * NBP + j];
+      bf16_t* yrow = Y + off + (size_t)t * d;
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DS; ++ks) o = mfma16x16x32(afr[ct][ks], bq[ks], o);
-      const int c = 16 * ct + 4 * grp;
-      if (ok && c < d) {
-        // padded query rows (j >= nb) are computed but never stored
-        uint32_t lo, hi;
-        if (den == 0.0f) {
-          lo = hi = 0u;
-        } else {
-          lo = (uint32_t)f32_to_bf16(o[0] / den) | ((uint32_t)f32_to_bf16(o[1] / den) << 16);
-          hi = (uint32_t)f32_to_bf16(o[2] / den) | ((uint32_t)f32_to_bf16(o[3] / den) << 16);
-        }
-        *reinterpret_cast<uint2*>(Ys + t * d + c) = make_uint2(lo, hi);
+      for (int c = 0; c < NT; ++c) {
+        const int col = 16 * c + 4 * grp;
+        if (col < d)
+          *reinterpret_cast<uint2*>(yrow + col) =
+              make_uint2(pack2(o[c][0] * rd, o[c][1] * rd), pack2(o[c][2] * rd, o[c][3] * rd));
       }
     }
   }
+}
+
+inline int fused_dp(int d) { return d <= 32 ? 32 : 64; }
+inline int fused_nbp(int nb) { return nb <= 32 ? 32 : 64; }
+inline int fused_mm(int M) { return M <= 2 ? 2 : (M <= 4 ? 4 : 8); }
+
+inline size_t fused_lds(int d, int M, int nb) {
+  const int DP = fused_dp(d), NBP = fused_nbp(nb);
+  if (DP == 32)
+    return NBP == 32 ? FusedLayout<32, 32>::total(M) : FusedLayout<32, 64>::total(M);
+  return NBP == 32 ? FusedLayout<64, 32>::total(M) : FusedLayout<64, 64>::total(M);
 }
 
 inline bool fused_supports(int dtype, int d, int M, int nb) {
   if (dtype != 1 || d % 8 != 0 || d > 64 || M < 1 || M > kFusedMaxM || nb > 64) return false;
-  const int DP = d <= 32 ? 32 : 64;
-  const int NBP = nb <= 32 ? 32 : 64;
-  const size_t lds = (size_t)M * ((size_t)2 * DP * (NBP + 8) * 2 > (size_t)DP * DP * 4 + DP * 4
-                                      ? (size_t)2 * DP * (NBP + 8) * 2
-                                      : (size_t)DP * DP * 4 + DP * 4);
-  return lds <= 160 * 1024;
+  return fused_lds(d, M, nb) <= kLdsLimit;
 }
 
-template <int DP, int NBP>
-int launch_fused_t(long slices, int H, int N, int d, const Geo& g, int phi, const bf16_t* Q,
+template <int DP, int NBP, int MM, int PHI>
+int launch_fused_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
                    const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
-  const size_t lds = fused_lds_bytes<DP, NBP>(g.M);
+  const size_t lds = FusedLayout<DP, NBP>::total(g.M);
   static bool attr_set[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused<DP, NBP>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return MHLA_ERR_HIP;
-    attr_set[dev] = true;
+  const void* fn = reinterpret_cast<const void*>(&k_fused<DP, NBP, MM, PHI>);
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) !=
+        hipSuccess)
+      return -1;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  k_fused<DP, NBP><<<dim3((unsigned)slices), dim3(64 * g.M), lds, st>>>(Q, K, V, W, Y, g, H, N, d,
-                                                                       phi);
+  k_fused<DP, NBP, MM, PHI><<<dim3((unsigned)slices), dim3(kFusedThreads), lds, st>>>(
+      Q, K, V, W, Y, g, H, N, d);
   return 0;
+}
+
+template <int DP, int NBP, int PHI>
+int launch_fused_m(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                   const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
+  switch (fused_mm(g.M)) {
+    case 2: return launch_fused_t<DP, NBP, 2, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 4: return launch_fused_t<DP, NBP, 4, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    default: return launch_fused_t<DP, NBP, 8, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  }
+}
+
+template <int PHI>
+int launch_fused_p(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                   const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
+  const int DP = fused_dp(d), NBP = fused_nbp(g.nb);
+  if (DP == 32 && NBP == 32)
+    return launch_fused_m<32, 32, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  if (DP == 32) return launch_fused_m<32, 64, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  if (NBP == 32) return launch_fused_m<64, 32, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  return launch_fused_m<64, 64, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
 }
 
 inline int launch_fused(long slices, int H, int N, int d, const Geo& g, int phi, const bf16_t* Q,
                         const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y,
                         hipStream_t st) {
-  const bool d32 = d <= 32, n32 = g.nb <= 32;
-  if (d32 && n32) return launch_fused_t<32, 32>(slices, H, N, d, g, phi, Q, K, V, W, Y, st);
-  if (d32) return launch_fused_t<32, 64>(slices, H, N, d, g, phi, Q, K, V, W, Y, st);
-  if (n32) return launch_fused_t<64, 32>(slices, H, N, d, g, phi, Q, K, V, W, Y, st);
-  return launch_fused_t<64, 64>(slices, H, N, d, g, phi, Q, K, V, W, Y, st);
+  if (phi == PHI_RELU)
+    return launch_fused_p<PHI_RELU>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  return launch_fused_p<PHI_ELU1>(slices, H, N, d, g, Q, K, V, W, Y, st);
 }
 
 }  // namespace mhla

@@ -1,0 +1,106 @@
+// mhla_mfma.hpp -- gfx950 building blocks shared by the MFMA kernels:
+// packed bf16 conversions, the feature map on packed bf16, the
+// v_mfma_f32_16x16x32_bf16 wrapper and LDS transpose reads.
+//
+// MFMA 16x16x32 bf16 operand layout (lane l, s = l % 16, g = l / 16):
+//   A: row s, 8 contraction elements owned by lane group g
+//   B: column s, the same 8 contraction elements of group g
+//   D: lane l holds D[4g + r][s], r = 0..3
+// Only the pairing of A and B elements matters, so every kernel here picks
+// the assignment of contraction indices to (group, element) that suits its
+// data: "tr8" operands take tokens 8g..8g+7 of a 32-token step; "acc8"
+// operands take features {4g..4g+3} and {16+4g..16+4g+3} of a 32-feature
+// step, which is the layout two row-adjacent accumulator tiles already have.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), within each 16-lane group: lane s
+// supplies an address of four consecutive 16-bit values and receives value
+// (s % 4) of the four supplied by lane 4e + s / 4, e = 0..3.  If lane s points
+// at row R(s / 4), column c0 + 4 (s % 4) of a row-major 16-bit matrix, lane s
+// receives rows R(0..3) of column c0 + s: a column slice, i.e. a transpose.
+#pragma once
+
+#include "mhla_common.hpp"
+
+namespace mhla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b,
+                                             const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), low first.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ float lo_f32(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Feature map on two packed bf16 values; the result is rounded to bf16.
+// ReLU is exact on the bit patterns (signed 16-bit max with 0 clears every
+// value whose sign bit is set).  elu(x)+1 is x+1 for x > 0, exp(x) otherwise.
+template <int PHI>
+__device__ __forceinline__ uint32_t phi2(uint32_t x) {
+  if constexpr (PHI == PHI_RELU) {
+    const i16x2_t v = __builtin_bit_cast(i16x2_t, x);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, i16x2_t{0, 0}));
+  } else {
+    const float a = lo_f32(x), b = hi_f32(x);
+    return pack2(a > 0.f ? a + 1.f : __expf(a), b > 0.f ? b + 1.f : __expf(b));
+  }
+}
+
+template <int PHI>
+__device__ __forceinline__ uint4 phi8(uint4 x) {
+  return make_uint4(phi2<PHI>(x.x), phi2<PHI>(x.y), phi2<PHI>(x.z), phi2<PHI>(x.w));
+}
+
+template <int PHI>
+__device__ __forceinline__ uint2 phi4(uint2 x) {
+  return make_uint2(phi2<PHI>(x.x), phi2<PHI>(x.y));
+}
+
+__device__ __forceinline__ i16x4_t lds_tr4(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
+
+// "tr8" operand of one 16-column slice of a row-major bf16 LDS matrix with
+// row stride rs (elements): lane (s, g) receives column c0 + s of rows
+// r0 + 8g .. r0 + 8g + 7.  Rows r0 .. r0+31 and columns c0 .. c0+15 must exist.
+__device__ __forceinline__ u16x8_t lds_tr8(const bf16_t* base, int rs, int r0, int c0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const bf16_t* p = base + (r0 + 8 * g + (s >> 2)) * rs + c0 + 4 * (s & 3);
+  const i16x4_t lo = lds_tr4(p);
+  const i16x4_t hi = lds_tr4(p + 4 * rs);
+  u16x8_t r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Packs two accumulator tiles (rows 4g..4g+3 of each) into an "acc8" operand.
+__device__ __forceinline__ u16x8_t pack_acc8(const f32x4_t& a, const f32x4_t& b) {
+  const uint32_t w0 = pack2(a[0], a[1]), w1 = pack2(a[2], a[3]);
+  const uint32_t w2 = pack2(b[0], b[1]), w3 = pack2(b[2], b[3]);
+  return __builtin_bit_cast(u16x8_t, u32x4_t{w0, w1, w2, w3});
+}
+
+__device__ __forceinline__ u16x8_t from_u2x2(uint2 a, uint2 b) {
+  return __builtin_bit_cast(u16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
+}
+
+}  // namespace mhla
