@@ -65,13 +65,21 @@ __device__ __forceinline__ uint32_t phi2(uint32_t x) {
 }
 
 template <int PHI>
-__device__ __forceinline__ uint4 phi8(uint4 x) {
-  return make_uint4(phi2<PHI>(x.x), phi2<PHI>(x.y), phi2<PHI>(x.z), phi2<PHI>(x.w));
+__device__ __forceinline__ u32x4_t phi8(u32x4_t x) {
+  return u32x4_t{phi2<PHI>(x[0]), phi2<PHI>(x[1]), phi2<PHI>(x[2]), phi2<PHI>(x[3])};
 }
 
 template <int PHI>
 __device__ __forceinline__ uint2 phi4(uint2 x) {
   return make_uint2(phi2<PHI>(x.x), phi2<PHI>(x.y));
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads issued before
+// it stay in flight (a full __syncthreads also waits for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ i16x4_t lds_tr4(const bf16_t* p) {
@@ -86,10 +94,18 @@ __device__ __forceinline__ u16x8_t lds_tr8(const bf16_t* base, int rs, int r0, i
   const bf16_t* p = base + (r0 + 8 * g + (s >> 2)) * rs + c0 + 4 * (s & 3);
   const i16x4_t lo = lds_tr4(p);
   const i16x4_t hi = lds_tr4(p + 4 * rs);
-  u16x8_t r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// "tr8" operand gathered from arbitrary rows: lane (s, g) passes the rows of
+// its quad (s / 4) for the two transpose reads, r0 and r1, and `base` must
+// already point at column c0 + 4 (s % 4).  Lane (s, g) then receives column
+// c0 + s of the rows passed by quads 0..3 of its group for r0 (elements 0..3)
+// and for r1 (elements 4..7).
+__device__ __forceinline__ u16x8_t lds_tr8_rows(const bf16_t* base, int rs, int r0, int r1) {
+  const i16x4_t lo = lds_tr4(base + r0 * rs);
+  const i16x4_t hi = lds_tr4(base + r1 * rs);
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Packs two accumulator tiles (rows 4g..4g+3 of each) into an "acc8" operand.
