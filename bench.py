@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="deit_t")
-    ap.add_argument("--path", default="auto", choices=["auto", "generic", "fused", "pairs"])
+    ap.add_argument("--path", default="auto", choices=["auto", "generic", "fused", "pairs", "blocked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -53,12 +53,13 @@ def main():
 
     wl = WORKLOADS[args.workload]
     path = {"auto": m.MHLA_PATH_AUTO, "generic": m.MHLA_PATH_GENERIC,
-            "fused": m.MHLA_PATH_FUSED, "pairs": m.MHLA_PATH_PAIRS}[args.path]
+            "fused": m.MHLA_PATH_FUSED, "pairs": m.MHLA_PATH_PAIRS,
+            "blocked": m.MHLA_PATH_BLOCKED}[args.path]
     shape = (wl.grid, wl.block)
     if path == m.MHLA_PATH_AUTO:
         path = m.mhla_plan(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi, wl.dtype)
-    path_name = {1: "generic", 2: "fused", 3: "pairs"}[path]
-    n_kernels = {1: 3, 2: 1, 3: 1}[path]
+    path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked"}[path]
+    n_kernels = {1: 3, 2: 1, 3: 1, 4: 3}[path]
 
     inp = make_inputs(wl)
 

@@ -69,7 +69,8 @@ enum {
   MHLA_PATH_AUTO = 0,       /* the library's choice for the shape            */
   MHLA_PATH_GENERIC = 1,    /* summary -> mixing -> readout, three kernels   */
   MHLA_PATH_FUSED = 2,      /* one workgroup per slice, summaries kept in LDS */
-  MHLA_PATH_PAIRS = 3       /* token-pair form of Eq. 5, no summaries        */
+  MHLA_PATH_PAIRS = 3,      /* token-pair form of Eq. 5, no summaries        */
+  MHLA_PATH_BLOCKED = 4     /* summary, mixing GEMM, readout on bf16 MFMA     */
 };
 
 /* Forward pass (MHLA paper §4.1).  Returns MHLA_OK or an MHLA_ERR_* code. */

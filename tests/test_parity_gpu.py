@@ -16,7 +16,7 @@ from gpu_util import TOL, run, slice_error, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
-ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED]
+ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED, m.MHLA_PATH_BLOCKED]
 
 
 def _oracle_full(inp):
@@ -47,8 +47,10 @@ def _check_sampled(inp, y, n_slices, n_rows, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "deit_t", "dit_xl2", "hires"])
-@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC])
+@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC, m.MHLA_PATH_BLOCKED])
 def test_workload_full(name, path):
+    if path == m.MHLA_PATH_BLOCKED and WORKLOADS[name].dtype != DTYPE_BF16:
+        pytest.skip("the MFMA paths take bf16 inputs")
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
     y = to_f64(run(inp, path))
@@ -59,7 +61,7 @@ def test_workload_full(name, path):
     assert err <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC])
+@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC, m.MHLA_PATH_BLOCKED])
 def test_video_sampled(path):
     wl = WORKLOADS["video"]
     inp = make_inputs(wl)
@@ -92,6 +94,29 @@ def test_small_shapes(grid, block, d, phi, path):
     y = to_f64(run(inp, path))
     err = slice_error(y, _oracle_full(inp))
     print("PARITY small %s %s d=%d phi=%d path=%d err=%.3e" % (grid, block, d, phi, path, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+BLOCKED_CASES = [
+    # (grid, block, d, phi): shapes the three-kernel MFMA path must handle
+    ((1, 16, 16), (1, 16, 8), 64, PHI_ELU1),   # 128-token blocks: two staging chunks
+    ((1, 16, 16), (1, 4, 4), 72, PHI_RELU),    # d = 72 padded to 96 (DiT-like)
+    ((1, 12, 12), (1, 3, 4), 96, PHI_ELU1),    # d = 96, 12-token blocks
+    ((1, 40, 52), (1, 4, 4), 32, PHI_RELU),    # M = 130: partial mixing tiles
+    ((4, 16, 16), (2, 4, 4), 64, PHI_ELU1),    # 3-D blocks, M = 32
+    ((1, 1, 300), (1, 1, 5), 16, PHI_RELU),    # 1-D, M = 60, d = 16 padded to 32
+    ((3, 8, 8), (1, 8, 8), 48, PHI_ELU1),      # whole-frame blocks, M = 3
+]
+
+
+@pytest.mark.parametrize("grid,block,d,phi", BLOCKED_CASES)
+def test_blocked_shapes(grid, block, d, phi):
+    wl = custom_workload(2, 2, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 991)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_BLOCKED))
+    assert np.all(np.isfinite(y))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY blocked %s %s d=%d phi=%d M=%d err=%.3e" % (grid, block, d, phi, wl.M, err))
     assert err <= TOL[DTYPE_BF16]
 
 

@@ -1,0 +1,370 @@
+// k_blocked.hpp -- three-kernel MHLA forward for any number of blocks M
+// (bf16 in/out, gfx950 MFMA), the three steps of "MHLA: Restoring
+// Expressivity of Linear Attention via Token-Level Multi-Head" §4.1:
+//
+//   k_summary_mfma : S_b = phi(K_b)^T V_b and z_b = sum_j phi(K_b)[j]
+//                    (one wave per key block, operands through LDS with
+//                    transpose reads, fp32 accumulation, bf16 result)
+//   k_mix_mfma     : S~_i = sum_b W[i,b] S_b, z~_i = sum_b W[i,b] z_b, one
+//                    GEMM per (batch, head) slice over all d*d + d entries
+//   k_readout_mfma : Y_q = phi(Q_q) S~_i / (phi(Q_q) . z~_i), one wave per
+//                    query block, operands straight from global memory
+//
+// Workspace rows: one row of EP bf16 per (slice, block).  Entry c*DP + k holds
+// S[k][c] (value column c, key feature k: the transpose of the summary, so
+// that the readout's A operand reads 8 consecutive features of one column),
+// entries DP*DP + k hold z[k], the rest up to EP is padding that is computed
+// but never read.  The same layout serves S (summary -> mixing) and S~
+// (mixing -> readout); the mixing GEMM treats the rows as plain vectors.
+#pragma once
+
+#include "mhla_mfma.hpp"
+
+namespace mhla {
+
+constexpr int kBlkThreads = 256;
+constexpr int kBlkWaves = kBlkThreads / 64;
+constexpr int kMixEB = 128;  // entries per mixing workgroup
+constexpr int kMixIB = 128;  // query blocks per mixing workgroup
+constexpr int kMixKB = 32;   // key blocks per mixing step
+
+template <int DP>
+struct BlockedDims {
+  static constexpr int NT = DP / 16;   // 16-wide tiles along d
+  static constexpr int DS = DP / 32;   // 32-feature contraction steps
+  static constexpr int RS = DP + 16;   // LDS row stride (elements) of staged K, V
+  static constexpr int E = DP * DP + DP;
+  static constexpr int EP = (E + kMixEB - 1) / kMixEB * kMixEB;
+};
+
+inline int blocked_dp(int d) { return (d + 31) / 32 * 32; }
+
+// ---------------------------------------------------------------------------
+// Summaries.  grid = (ceil(M / 4), slices), block = 256; wave w takes key
+// block 4*blockIdx.x + w and walks its tokens in chunks of 64.
+template <int DP, int PHI>
+__global__ __launch_bounds__(kBlkThreads) void k_summary_mfma(
+    const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, bf16_t* __restrict__ S, Geo g,
+    int N, int d) {
+  using D = BlockedDims<DP>;
+  constexpr int NT = D::NT, RS = D::RS, EP = D::EP;
+  constexpr int F8P = DP / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kBlkWaves][2][64 * RS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.y;
+  const int b = blockIdx.x * kBlkWaves + wave;
+  const bool valid = b < g.M;
+  const size_t off = (size_t)slice * N * d;
+  bf16_t* sk = lds[wave][0];
+  bf16_t* sv = lds[wave][1];
+  const int F8 = d >> 3;
+  const float inv8 = 1.0f / (float)F8;
+  const int bb = valid ? g.blockbase(b) : 0;
+
+  if (d < DP) {  // feature columns d .. DP-1 stay zero for every chunk
+    for (int e = lane; e < 2 * 64 * RS / 8; e += 64)
+      reinterpret_cast<u32x4_t*>(sk)[e] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  f32x4_t acc[NT][NT], zacc[NT];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    zacc[kt] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[kt][ct] = zero4();
+  }
+  const u16x8_t ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
+
+  for (int c0 = 0; c0 < g.nb; c0 += 64) {
+    // Stage tokens c0 .. c0+63 of the block: 16-byte chunk it = lane + 64u is
+    // chunk f of chunk-local token jl.  Rows past the block are zero.
+    u32x4_t kr[F8P], vr[F8P];
+#pragma unroll
+    for (int u = 0; u < F8P; ++u) {
+      const int it = lane + 64 * u;
+      const int jl = (int)(((float)it + 0.5f) * inv8);
+      const int f = it - jl * F8;
+      const int j = c0 + jl;
+      kr[u] = vr[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (valid && u < F8 && j < g.nb) {
+        const size_t src = off + (size_t)(bb + g.tokoff(j)) * d + 8 * f;
+        kr[u] = *reinterpret_cast<const u32x4_t*>(K + src);
+        vr[u] = *reinterpret_cast<const u32x4_t*>(V + src);
+      }
+    }
+    lds_barrier();  // the previous chunk's reads are done
+#pragma unroll
+    for (int u = 0; u < F8P; ++u) {
+      if (u < F8) {
+        const int it = lane + 64 * u;
+        const int jl = (int)(((float)it + 0.5f) * inv8);
+        const int f = it - jl * F8;
+        const bool real = valid && c0 + jl < g.nb;
+        *reinterpret_cast<u32x4_t*>(sk + jl * RS + 8 * f) =
+            real ? phi8<PHI>(kr[u]) : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(sv + jl * RS + 8 * f) = vr[u];
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u16x8_t a[NT];
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) a[kt] = lds_tr8(sk, RS, 32 * st, 16 * kt, lane);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const u16x8_t bv = lds_tr8(sv, RS, 32 * st, 16 * ct, lane);
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt) acc[kt][ct] = mfma_bf16(a[kt], bv, acc[kt][ct]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < NT; ++kt) zacc[kt] = mfma_bf16(a[kt], ones, zacc[kt]);
+    }
+  }
+  if (!valid) return;  // no barrier follows
+  // acc[kt][ct] lane (s, grp) element r = S[16kt + 4grp + r][16ct + s]:
+  // four consecutive features of value column 16ct + s.
+  bf16_t* row = S + ((size_t)slice * g.M + b) * EP;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) {
+      const f32x4_t v = acc[kt][ct];
+      *reinterpret_cast<uint2*>(row + (16 * ct + s) * DP + 16 * kt + 4 * grp) =
+          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    }
+  if (s == 0) {
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) {
+      const f32x4_t v = zacc[kt];
+      *reinterpret_cast<uint2*>(row + DP * DP + 16 * kt + 4 * grp) =
+          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mixing: per slice, S~[i][e] = sum_b W[h][i][b] S[b][e], computed as the
+// transposed product S~^T = S^T W^T so that each lane stores four
+// consecutive entries.  grid = (EP / 128, ceil(M / 128), slices), block = 256;
+// wave (we, wi) owns entries 64we .. 64we+63 and query blocks 64wi .. 64wi+63
+// of the workgroup's 128 x 128 tile.
+template <int EP>
+__global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
+                                                          const float* __restrict__ W,
+                                                          bf16_t* __restrict__ St, int M, int H) {
+  constexpr int EB = kMixEB, IB = kMixIB, KB = kMixKB;
+  constexpr int SRS = EB + 16;  // LDS row stride of the S tile (rows = key blocks)
+  constexpr int WRS = KB + 8;   // LDS row stride of the W tile (rows = query blocks)
+  __shared__ __attribute__((aligned(16))) bf16_t sS[KB * SRS];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[IB * WRS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int we = wave & 1, wi = wave >> 1;
+  const int e0 = blockIdx.x * EB, i0 = blockIdx.y * IB;
+  const long slice = blockIdx.z;
+  const int h = (int)(slice % H);
+  const bf16_t* Ss = S + (size_t)slice * M * EP;
+  const float* Wh = W + (size_t)h * M * M;
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = zero4();
+
+  for (int b0 = 0; b0 < M; b0 += KB) {
+    // S tile: KB rows x EB entries = 512 chunks of 8 bf16, 2 per thread
+    u32x4_t sr[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c >> 4, f = c & 15;
+      sr[u] = b0 + r < M
+                  ? *reinterpret_cast<const u32x4_t*>(Ss + (size_t)(b0 + r) * EP + e0 + 8 * f)
+                  : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    // W tile: IB rows x KB columns (fp32) = 1024 chunks of 4, 4 per thread
+    f32x4_t wr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c >> 3, f = c & 7;
+      const int i = i0 + r, bcol = b0 + 4 * f;
+      f32x4_t v = zero4();
+      if (i < M) {
+        if (bcol + 3 < M && (M & 3) == 0) {
+          v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bcol);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (bcol + q < M) v[q] = Wh[(size_t)i * M + bcol + q];
+        }
+      }
+      wr[u] = v;
+    }
+    lds_barrier();  // the previous step's reads are done
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c >> 4, f = c & 15;
+      *reinterpret_cast<u32x4_t*>(sS + r * SRS + 8 * f) = sr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c >> 3, f = c & 7;
+      *reinterpret_cast<uint2*>(sW + r * WRS + 4 * f) =
+          make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));
+    }
+    lds_barrier();
+    // A = S^T (rows e, contraction b via transpose reads: b = 8grp .. 8grp+7),
+    // B = W^T (column i, the same b: W[i][8grp .. 8grp+7] is contiguous).
+    u16x8_t af[4], bw[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) af[a] = lds_tr8(sS, SRS, 0, 64 * we + 16 * a, lane);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bw[c] = *reinterpret_cast<const u16x8_t*>(sW + (64 * wi + 16 * c + s) * WRS + 8 * grp);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+  }
+  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = i0 + 64 * wi + 16 * c + s;
+    if (i < M) {
+      bf16_t* row = St + ((size_t)slice * M + i) * EP + e0 + 64 * we;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<uint2*>(row + 16 * a + 4 * grp) =
+            make_uint2(pack2(acc[a][c][0], acc[a][c][1]), pack2(acc[a][c][2], acc[a][c][3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Readout.  grid = (ceil(M / 4), slices), block = 256; wave w reads out query
+// block 4*blockIdx.x + w, 16 queries per step.  Y^T = S~_i^T phi(Q)^T with the
+// contraction split as features 32ks + 8grp .. +7 on both operands; the z~
+// row (row 0 of one more A tile) gives phi(q).z~_i.
+template <int DP, int PHI>
+__global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ St, bf16_t* __restrict__ Y, Geo g,
+    int N, int d) {
+  using D = BlockedDims<DP>;
+  constexpr int NT = D::NT, DS = D::DS, EP = D::EP;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.y;
+  const int i = blockIdx.x * kBlkWaves + wave;
+  if (i >= g.M) return;  // this kernel has no barrier
+  const size_t off = (size_t)slice * N * d;
+  const bf16_t* row = St + ((size_t)slice * g.M + i) * EP;
+  u16x8_t af[NT][DS], az[DS];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks)
+      af[ct][ks] = *reinterpret_cast<const u16x8_t*>(row + (16 * ct + s) * DP + 32 * ks + 8 * grp);
+#pragma unroll
+  for (int ks = 0; ks < DS; ++ks)
+    az[ks] = s == 0 ? *reinterpret_cast<const u16x8_t*>(row + DP * DP + 32 * ks + 8 * grp)
+                    : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  const int bb = g.blockbase(i);
+  for (int q0 = 0; q0 < g.nb; q0 += 16) {
+    const int j = q0 + s;
+    const int t = j < g.nb ? bb + g.tokoff(j) : -1;
+    u16x8_t bq[DS];
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const int k0 = 32 * ks + 8 * grp;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (t >= 0 && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)t * d + k0);
+      bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
+    }
+    f32x4_t o[NT], oz = zero4();
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      o[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) o[ct] = mfma_bf16(af[ct][ks], bq[ks], o[ct]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[ks], oz);
+    const float den = __shfl(oz[0], s);
+    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+    if (t >= 0) {
+      bf16_t* yrow = Y + off + (size_t)t * d;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int c = 16 * ct + 4 * grp;
+        if (c < d)
+          *reinterpret_cast<uint2*>(yrow + c) = make_uint2(pack2(o[ct][0] * rd, o[ct][1] * rd),
+                                                           pack2(o[ct][2] * rd, o[ct][3] * rd));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+inline bool blocked_supports(int dtype, int d, long slices) {
+  return dtype == 1 && d % 8 == 0 && d <= 96 && slices <= 65535;
+}
+
+inline size_t blocked_ws_elems(int d) {
+  switch (blocked_dp(d)) {
+    case 32: return BlockedDims<32>::EP;
+    case 64: return BlockedDims<64>::EP;
+    default: return BlockedDims<96>::EP;
+  }
+}
+
+// Workspace: S and S~, [slices][M][EP] bf16 each.
+inline size_t blocked_workspace(long slices, int M, int d) {
+  return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
+}
+
+template <int DP, int PHI>
+int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                     const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
+                     hipStream_t st) {
+  using D = BlockedDims<DP>;
+  bf16_t* S = ws;
+  bf16_t* St = ws + (size_t)slices * g.M * D::EP;
+  const unsigned nsl = (unsigned)slices;
+  const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
+  k_summary_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, V, S, g, N, d);
+  k_mix_mfma<D::EP><<<dim3(D::EP / kMixEB, (g.M + kMixIB - 1) / kMixIB, nsl), kBlkThreads, 0,
+                      st>>>(S, W, St, g.M, H);
+  k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
+  return 0;
+}
+
+template <int PHI>
+int launch_blocked_p(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                     const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
+                     hipStream_t st) {
+  switch (blocked_dp(d)) {
+    case 32: return launch_blocked_t<32, PHI>(slices, H, N, d, g, Q, K, V, W, Y, ws, st);
+    case 64: return launch_blocked_t<64, PHI>(slices, H, N, d, g, Q, K, V, W, Y, ws, st);
+    default: return launch_blocked_t<96, PHI>(slices, H, N, d, g, Q, K, V, W, Y, ws, st);
+  }
+}
+
+inline int launch_blocked(long slices, int H, int N, int d, const Geo& g, int phi,
+                          const bf16_t* Q, const bf16_t* K, const bf16_t* V, const float* W,
+                          bf16_t* Y, bf16_t* ws, hipStream_t st) {
+  if (phi == PHI_RELU)
+    return launch_blocked_p<PHI_RELU>(slices, H, N, d, g, Q, K, V, W, Y, ws, st);
+  return launch_blocked_p<PHI_ELU1>(slices, H, N, d, g, Q, K, V, W, Y, ws, st);
+}
+
+}  // namespace mhla

@@ -140,22 +140,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
     }
   }
 
-  // token offset of member j inside its block (raster order within the tile)
-  const int bhw = g.bh * g.bw;
-  const float inv_bw = 1.0f / (float)g.bw, inv_bhw = 1.0f / (float)bhw;
-  auto tokoff = [&](int j) {
-    const int jz = small_div(j, inv_bhw);
-    const int r = j - jz * bhw;
-    const int jy = small_div(r, inv_bw);
-    return (jz * g.Hg + jy) * g.Wg + (r - jy * g.bw);
-  };
-  // first token of block b (uniform)
-  auto blockbase = [&](int b) {
-    const int nyx = g.nby * g.nbx;
-    const int bz = b / nyx, r = b - bz * nyx;
-    const int by = r / g.nbx, bx = r - by * g.nbx;
-    return ((bz * g.bt) * g.Hg + by * g.bh) * g.Wg + bx * g.bw;
-  };
+  auto tokoff = [&](int j) { return g.tokoff(j); };
+  auto blockbase = [&](int b) { return g.blockbase(b); };
   lds_barrier();
 
   // ---- B. summaries and mixing ------------------------------------------------

@@ -18,6 +18,7 @@
 #include "mhla_common.hpp"
 #include "k_generic.hpp"
 #include "k_fused.hpp"
+#include "k_blocked.hpp"
 
 namespace mhla {
 namespace {
@@ -80,7 +81,11 @@ int check(int B, int H, int N, int d, const mhla_block_shape* s, int phi, int dt
     g.nbz = g.T / g.bt; g.nby = g.Hg / g.bh; g.nbx = g.Wg / g.bw;
     g.M = g.nbz * g.nby * g.nbx;
     g.nb = g.bt * g.bh * g.bw;
+    g.inv_bw = 1.0f / (float)g.bw;
+    g.inv_bhw = 1.0f / (float)(g.bh * g.bw);
     p->B = B; p->H = H; p->N = N; p->d = d; p->phi = phi; p->dtype = dtype;
+    if (g.nb >= (1 << 22))
+      return fail(MHLA_ERR_UNSUPPORTED, "blocks of %d tokens are too large (limit 2^22)", g.nb);
     if ((long)g.M * g.M * H > 0x7fffffffL)
       return fail(MHLA_ERR_UNSUPPORTED, "M=%d is too large", g.M);
   }
@@ -91,12 +96,14 @@ bool path_supports(int path, const Problem& p) {
   switch (path) {
     case MHLA_PATH_GENERIC: return p.slices() <= 65535;  // slices run along grid y/z
     case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
+    case MHLA_PATH_BLOCKED: return blocked_supports(p.dtype, p.d, p.slices());
     default: return false;
   }
 }
 
 int choose_path(const Problem& p) {
   if (path_supports(MHLA_PATH_FUSED, p)) return MHLA_PATH_FUSED;
+  if (path_supports(MHLA_PATH_BLOCKED, p)) return MHLA_PATH_BLOCKED;
   if (path_supports(MHLA_PATH_GENERIC, p)) return MHLA_PATH_GENERIC;
   return -MHLA_ERR_UNSUPPORTED;
 }
@@ -106,6 +113,7 @@ size_t workspace_for(const Problem& p, int path) {
     const size_t L = (size_t)p.d * p.d + p.d;
     return 2 * (size_t)p.slices() * p.g.M * L * sizeof(float);
   }
+  if (path == MHLA_PATH_BLOCKED) return blocked_workspace(p.slices(), p.g.M, p.d);
   return 0;
 }
 
@@ -205,6 +213,9 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
   } else if (path == MHLA_PATH_FUSED) {
     rc = launch_fused(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
                       (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, st);
+  } else if (path == MHLA_PATH_BLOCKED) {
+    rc = launch_blocked(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
+                        (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, (bf16_t*)ws, st);
   }
   if (rc != MHLA_OK) return rc;
   hipError_t e = hipGetLastError();
@@ -230,7 +241,7 @@ int mhla_forward_path(const void* Q, const void* K, const void* V, const float* 
                       void* out, int B, int H, int N, int d,
                       const mhla_block_shape* block_shape, int phi_kind, int dtype, int path,
                       void* stream) {
-  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_PAIRS)
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
   return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, path, stream);
 }

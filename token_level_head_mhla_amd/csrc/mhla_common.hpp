@@ -20,16 +20,29 @@ struct Geo {
   int nbz, nby, nbx;    // block grid
   int M;                // number of blocks
   int nb;               // tokens per block
+  float inv_bw, inv_bhw;  // 1/bw and 1/(bh*bw), for exact small-integer division
 
   // Token index of member j (raster order inside the tile) of block b.
   __host__ __device__ __forceinline__ int token(int b, int j) const {
-    const int bx = b % nbx;
-    const int by = (b / nbx) % nby;
-    const int bz = b / (nbx * nby);
-    const int jx = j % bw;
-    const int jy = (j / bw) % bh;
-    const int jz = j / (bw * bh);
-    return ((bz * bt + jz) * Hg + by * bh + jy) * Wg + bx * bw + jx;
+    return blockbase(b) + tokoff(j);
+  }
+  // First token of block b (blocks in raster order of the block grid).
+  __host__ __device__ __forceinline__ int blockbase(int b) const {
+    const int nyx = nby * nbx;
+    const int bz = b / nyx, r = b - bz * nyx;
+    const int by = r / nbx, bx = r - by * nbx;
+    return ((bz * bt) * Hg + by * bh) * Wg + bx * bw;
+  }
+  // Offset of member j from the block's first token.  floor(a / b) is taken
+  // as (int)((a + 0.5) * fl(1/b)): the true quotient is at least 0.5/b away
+  // from an integer and the rounding error is below 2^-23 (a + 0.5)/b, so the
+  // result is exact for 0 <= a < 2^22 (the library rejects larger blocks).
+  __host__ __device__ __forceinline__ int tokoff(int j) const {
+    const int bhw = bh * bw;
+    const int jz = (int)(((float)j + 0.5f) * inv_bhw);
+    const int r = j - jz * bhw;
+    const int jy = (int)(((float)r + 0.5f) * inv_bw);
+    return (jz * Hg + jy) * Wg + (r - jy * bw);
   }
 };
 
