@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the MHLA forward on one MI355X.
 
-One step = one mhla_forward call (the whole hot path: block summaries,
-multi-head mixing and readout) over one batch of seeded synthetic input that
-is already resident in HBM.  Prints ONE JSON line.
+One step = one mhla_forward call: the whole hot path (block summaries,
+multi-head mixing, readout) over one batch of seeded synthetic input that is
+already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload deit_t] [--path auto]
 
 The default workload is the DeiT-T-shaped bf16 case (B64 H3 N196 as a 14x14
-grid, 7x7 blocks so M=4, d64, elu+1).  Other workloads (tiny, dit_xl2, hires,
-video) can be selected for study; they are parity-test cases, not the
-reported line.
+grid of 7x7 blocks, so M=4; d64; elu+1).  The other workloads (tiny,
+dit_xl2, hires, video) can be selected for study.
+
+  python bench.py --copy-mb 256
+
+times a plain device copy of that size instead (the reference kernel for
+scaling the HBM byte counters of a profiler run).
 """
 from __future__ import annotations
 
@@ -22,7 +26,9 @@ import time
 
 import numpy as np
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+METRIC = "MHLA fwd tokens/s per GPU and % of bf16 MFMA / HBM roofline"
 
 
 def parse():
@@ -31,11 +37,35 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="deit_t")
-    ap.add_argument("--path", default="auto", choices=["auto", "generic", "fused", "pairs", "blocked"])
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "generic", "fused", "pairs", "blocked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="time a plain device copy of this many MB instead")
     return ap.parse_args()
+
+
+def copy_bench(args):
+    import torch
+    n = args.copy_mb * 1000 * 1000 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"copy_bytes_each_way": n * 4, "steps": args.steps, "ms_per_copy": ms,
+                      "GBs_read_plus_write": 2 * n * 4 / (ms / 1e3) / 1e9}), flush=True)
+    return 0
 
 
 def main():
@@ -43,9 +73,11 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the (batch, head) slices shard across GPUs with no communication, but that "
-              "launcher is not part of this build)" % args.gpus, file=sys.stderr)
+              "(the (batch, head) slices would shard across GPUs with no communication, but "
+              "that launcher is not part of this build)" % args.gpus, file=sys.stderr)
         return 2
+    if args.copy_mb:
+        return copy_bench(args)
 
     import torch
     import token_level_head_mhla_amd as m
@@ -59,7 +91,8 @@ def main():
     if path == m.MHLA_PATH_AUTO:
         path = m.mhla_plan(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi, wl.dtype)
     path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked"}[path]
-    n_kernels = {1: 3, 2: 1, 3: 1, 4: 3}[path]
+    kernels = {1: ["k_summary_valu", "k_mix_valu", "k_readout_valu"], 2: ["k_fused"],
+               3: ["k_pairs"], 4: ["k_summary_mfma", "k_mix_mfma", "k_readout_mfma"]}[path]
 
     inp = make_inputs(wl)
 
@@ -72,43 +105,50 @@ def main():
     w = torch.from_numpy(inp.w).cuda()
     out = torch.empty_like(q)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()  # the stream the library launches on
 
     def step():
-        m.mhla_forward_path(q, k, v, w, out, shape, wl.phi, path)
+        m.mhla_forward_path(q, k, v, w, out, shape, wl.phi, path, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # HIP events recorded on the launch stream bracket exactly the K steps.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
+    start.record(stream)
     for _ in range(args.steps):
         step()
-    end.record()
+    end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / args.steps
+    ms = start.elapsed_time(end) / args.steps
     tokens = wl.B * wl.N
     value = tokens / (ms / 1e3)
 
     alg_bytes = wl.algorithmic_bytes()
-    achieved = alg_bytes / (ms / 1e3) / 1e9
+    alg_flops = wl.algorithmic_flops()
+    hbm_frac = alg_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+    mfma_frac = alg_flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+    bound = "hbm" if hbm_frac >= mfma_frac else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = alg_bytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = alg_flops / (ms / 1e3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     roofline = {
-        "bound": "hbm",
-        "kernel": "k_fused (whole forward)" if n_kernels == 1 else
-                  "whole step (%d kernels: summary, mixing, readout)" % n_kernels,
+        "bound": bound,
+        "kernel": kernels[0] if len(kernels) == 1 else "+".join(kernels),
         "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(kernels[0], wl.name) if len(kernels) == 1 else None,
         "algorithmic_bytes_per_launch": alg_bytes,
+        "algorithmic_flops_per_launch": alg_flops,
         "avg_launch_us": round(ms * 1e3, 3),
     }
 
     result = {
-        "metric": "MHLA fwd tokens/s per GPU and % of bf16 MFMA / HBM roofline",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -119,7 +159,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == 1 else "f32",
-        "data": "synthetic (seeded N(0,1) Q/K/V, row-softmax W)",
+        "data": "synthetic (seeded N(0,1) Q/K/V, row-softmax W; stand-in for the pages' image and "
+                "video workloads)",
         "config": {
             "workload": "%s: B%d H%d N%d (%s grid, %s blocks, M=%d) d%d phi=%s" % (
                 wl.name, wl.B, wl.H, wl.N, "x".join(map(str, wl.grid)),
@@ -137,18 +178,45 @@ def main():
     return 0
 
 
+# Sources that define each roofline kernel; a committed byte count applies only
+# while these files are unchanged.
+KERNEL_SOURCES = {"k_fused": ["k_fused.hpp", "mhla_mfma.hpp", "mhla_common.hpp"]}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary for this kernel and workload, or None when there is none or the
+    kernel's sources changed since it was taken."""
+    import hashlib
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    summary = os.path.join(root, "profiles", "%s_%s_hbm_bytes.md" % (kernel, workload))
+    if kernel not in KERNEL_SOURCES or not os.path.exists(summary):
+        return None
+    text = open(summary).read()
+    nbytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    digest = re.search(r"source_sha256_16: ([0-9a-f]{16})", text)
+    if not nbytes or not digest:
+        return None
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(root, "token_level_head_mhla_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return int(nbytes.group(1)) if h.hexdigest()[:16] == digest.group(1) else None
+
+
 def cpu_baseline(inp, out_dev, target_s):
-    """The fp64 oracle (blockwise C, OpenMP) timed on this host on a bounded
-    sample of the same workload; also reports the GPU output's error on it."""
+    """The fp64 oracle (blockwise C, OpenMP over slices) timed on this host on
+    a bounded sample of the same workload; also reports the GPU output's error
+    on that sample."""
     import oracle
     wl = inp.wl
     q, k, v, w = inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64
-    # sample: whole slices, enough of them for about target_s of CPU time
-    S = wl.B * wl.H
+    threads = oracle.threads()
+    # size the sample (whole batch items, all heads) for about target_s seconds
     t0 = time.perf_counter()
     oracle.blockwise(q[:1, :1], k[:1, :1], v[:1, :1], w[:1], wl.grid, wl.block, wl.phi)
     per_slice = max(time.perf_counter() - t0, 1e-6)
-    threads = oracle.threads()
     n_b = max(1, min(wl.B, int(target_s * threads / per_slice / wl.H)))
     reps, elapsed, ref = 0, 0.0, None
     while True:
@@ -156,7 +224,7 @@ def cpu_baseline(inp, out_dev, target_s):
         ref = oracle.blockwise(q[:n_b], k[:n_b], v[:n_b], w, wl.grid, wl.block, wl.phi)
         elapsed += time.perf_counter() - t0
         reps += 1
-        if elapsed >= target_s or reps >= 50:
+        if elapsed >= 0.8 * target_s or reps >= 2000:
             break
     tokens = reps * n_b * wl.N
     y = out_dev[:n_b].float().cpu().numpy().astype(np.float64)
@@ -168,8 +236,8 @@ def cpu_baseline(inp, out_dev, target_s):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "first %d of %d batch items (all %d heads), %d run(s), %.1f s" % (
-            n_b, wl.B, wl.H, reps, elapsed),
+        "sample": "fp64 blockwise oracle on batch items 0..%d of %d (all %d heads), %d run(s), "
+                  "%.1f s wall" % (n_b - 1, wl.B, wl.H, reps, elapsed),
     }
     parity = {"max_slice_rel_err": err, "slices_checked": n_b * wl.H,
               "gate": 1e-5 if wl.dtype == 0 else 1e-2}
