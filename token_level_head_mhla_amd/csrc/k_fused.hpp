@@ -32,8 +32,10 @@
 
 namespace mhla {
 
-constexpr int kFusedThreads = 512;
-constexpr int kFusedWaves = kFusedThreads / 64;
+// Waves per workgroup: 16 when M <= 4 (waves 8..15 stage phi(Q) while waves
+// 0..7 form the summaries), 8 otherwise (the mixing registers of M = 5..8 need
+// the larger per-wave register budget).
+__host__ __device__ constexpr int fused_waves(int MM) { return MM <= 4 ? 16 : 8; }
 constexpr int kFusedMaxM = 8;
 constexpr size_t kLdsLimit = 160 * 1024;
 
@@ -55,23 +57,37 @@ struct FusedLayout {
     return kv > fr ? kv : fr;
   }
   __host__ __device__ static size_t z_off(int N, int M) { return q_bytes(N) + kv_bytes(N, M); }
-  __host__ __device__ static size_t total(int N, int M) { return z_off(N, M) + (size_t)2 * M * DP * 4; }
+  // zraw [M][DP], zmix [M][DP], W [M][M] (fp32)
+  __host__ __device__ static size_t total(int N, int M) {
+    return z_off(N, M) + (size_t)2 * M * DP * 4 + (size_t)M * M * 4;
+  }
 };
 
-// floor(a / b) for 0 <= a < 2^16 and 1 <= b <= 2^12 with inv = 1/b.
+// First token of every block, computed on the host (uniform kernel argument).
+struct FusedBases {
+  int b[kFusedMaxM];
+};
+
+// floor(a / b) for 0 <= a < 2^22 with inv = fl(1/b) (see Geo::tokoff).
 __device__ __forceinline__ int small_div(int a, float inv) {
   return (int)(((float)a + 0.5f) * inv);
 }
 
 template <int DP, int NBP, int MM, int PHI>
-__global__ __launch_bounds__(kFusedThreads) void k_fused(
+__global__ __launch_bounds__(64 * fused_waves(MM)) void k_fused(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, int H, int N, int d) {
+    const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, FusedBases fb, int H, int N,
+    int d) {
   using L = FusedLayout<DP>;
   constexpr int RSQ = L::RSQ, RS = L::RS, NT = L::NT, DS = L::DS;
   constexpr int KS = NBP / 32;  // 32-token contraction steps per block
   constexpr int QT = NBP / 16;  // 16-query tiles per block
-  constexpr int U = 4;          // 16-byte chunks per thread and tensor per batch
+  constexpr int NWAVE = fused_waves(MM), NTHR = 64 * NWAVE;
+  constexpr int TPW = (MM * QT + NWAVE - 1) / NWAVE;  // max query tiles per wave
+  constexpr int QW0 = NWAVE == 16 ? 8 : 0;  // first wave that stages phi(Q)
+  constexpr int QTHR = NTHR - 64 * QW0;     // threads that stage phi(Q)
+  constexpr int UKV = 2048 / NTHR;          // 16-byte K, V chunks per thread per batch
+  constexpr int UQ = 2048 / QTHR;           // 16-byte Q chunks per thread per batch
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int M = g.M, nb = g.nb;
   const int tid = threadIdx.x;
@@ -89,26 +105,40 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
   u16x8_t* frag = reinterpret_cast<u16x8_t*>(sK);  // after step B
   float* zraw = reinterpret_cast<float*>(smem + L::z_off(N, M));
   float* zmix = zraw + M * DP;
+  float* sW = zmix + M * DP;
 
-  // ---- A. loads: K and V first, then Q; stage phi(K) and V --------------------
+  // ---- A. loads: K and V first, then Q; W; stage phi(K) and V -----------------
   const int F8 = d >> 3;
   const int items = N * F8;
   const float inv8 = 1.0f / (float)F8;
-  u32x4_t qr[U], kr[U], vr[U];
-#define MHLA_LOAD(dst, src_ptr, base)                                                     \
-  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
-    /* clamped so that every lane loads: straight-line code, all loads in flight */       \
-    const size_t o = off + (size_t)min((base) + u * kFusedThreads + tid, items - 1) * 8;  \
-    dst[u] = *reinterpret_cast<const u32x4_t*>(src_ptr + o);                               \
+  const bool qwave = wave >= QW0;
+  const int qtid = tid - QW0 * 64;
+  u32x4_t qr[UQ], kr[UKV], vr[UKV];
+#define MHLA_LOAD(dst, src_ptr, base, U, stride, id)                                     \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                         \
+    /* clamped so that every lane loads: straight-line code, all loads in flight */      \
+    const size_t o = off + (size_t)min((base) + u * (stride) + (id), items - 1) * 8;     \
+    dst[u] = *reinterpret_cast<const u32x4_t*>(src_ptr + o);                              \
   }
-  MHLA_LOAD(kr, K, 0)
-  MHLA_LOAD(vr, V, 0)
-  MHLA_LOAD(qr, Q, 0)
+  MHLA_LOAD(kr, K, 0, UKV, NTHR, tid)
+  MHLA_LOAD(vr, V, 0, UKV, NTHR, tid)
+  if (qwave) { MHLA_LOAD(qr, Q, 0, UQ, QTHR, qtid) }
+  // W through the scalar cache (uniform), clamped in range and masked to 0
+  // for the padding rows / columns i, b >= M.
+  float wr[MM][MM];
+#pragma unroll
+  for (int i = 0; i < MM; ++i)
+#pragma unroll
+    for (int b = 0; b < MM; ++b) {
+      const float w = Wh[min(i, M - 1) * M + min(b, M - 1)];
+      wr[i][b] = (i < M && b < M) ? w : 0.0f;
+    }
+  const float wv = tid < M * M ? Wh[tid] : 0.0f;
 
   // zero row N (and every pad column when d < DP)
   if (d < DP) {
     const int chunks = (int)((L::q_bytes(N) + (size_t)2 * (N + 1) * RS * 2) / 16);
-    for (int e = tid; e < chunks; e += kFusedThreads)
+    for (int e = tid; e < chunks; e += NTHR)
       reinterpret_cast<u32x4_t*>(smem)[e] = u32x4_t{0u, 0u, 0u, 0u};
     lds_barrier();
   } else if (tid < 3 * (DP / 8)) {
@@ -117,19 +147,19 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
     *reinterpret_cast<u32x4_t*>(row + 8 * f) = u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // N * d / 8 <= 8 * 64 * 64 / 8 = 2 * U * kFusedThreads chunks for every
-  // shape this kernel accepts, so two batches cover the slice.
+  // N * d / 8 <= 8 * 64 * 64 / 8 = 4096 chunks for every shape this kernel
+  // accepts, so two batches of 2048 chunks cover the slice.
 #pragma unroll
   for (int bt = 0; bt < 2; ++bt) {
-    const int base = bt * U * kFusedThreads;
+    const int base = bt * UKV * NTHR;
     if (base < items) {
       if (bt > 0) {
-        MHLA_LOAD(kr, K, base)
-        MHLA_LOAD(vr, V, base)
+        MHLA_LOAD(kr, K, base, UKV, NTHR, tid)
+        MHLA_LOAD(vr, V, base, UKV, NTHR, tid)
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int it = base + u * kFusedThreads + tid;
+      for (int u = 0; u < UKV; ++u) {
+        const int it = base + u * NTHR + tid;
         if (it < items) {
           const int t = small_div(it, inv8);
           const int f = it - t * F8;
@@ -139,52 +169,63 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
       }
     }
   }
-
-  auto tokoff = [&](int j) { return g.tokoff(j); };
-  auto blockbase = [&](int b) { return g.blockbase(b); };
   lds_barrier();
 
   // ---- B. summaries and mixing ------------------------------------------------
-  // Blocks b = M .. MM-1 (present when M is not a power of two) gather only the
-  // zero row and have W = 0, so they add nothing; the loop is fully static.
-  int bbase[MM];
-  float wr[MM][MM];
-#pragma unroll
-  for (int b = 0; b < MM; ++b) {
-    bbase[b] = b < M ? blockbase(b) : -1;
-#pragma unroll
-    for (int i = 0; i < MM; ++i) wr[i][b] = (i < M && b < M) ? Wh[i * M + b] : 0.0f;
-  }
+  // Wave w owns item (ct, ks) = (w % NT, w / NT): value columns 16ct..16ct+15
+  // and key features 32ks..32ks+31 of every S_b, mixed into every S~_i in
+  // registers.  Blocks b = M .. MM-1 (when M is not a power of two) gather the
+  // zero row and have W = 0.  The fragments of block b+1 are read while block
+  // b is multiplied.  The wave with ct = b % NT also forms z_b for its
+  // features (a ones B operand puts z_b in every column).
   const bool has_item = wave < NT * DS;
   const int ct = wave % NT, ksB = wave / NT;
   f32x4_t mix[MM][2];
 #pragma unroll
   for (int i = 0; i < MM; ++i) mix[i][0] = mix[i][1] = zero4();
   if (has_item) {
-    // this lane's tokens: member j = 32 st + 8 grp + 4 th + s / 4 of each block
-    int toff[KS][2];
+    int toff[KS][2];  // this lane's tokens: member 32 st + 8 grp + 4 th + s / 4
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const int j = 32 * st + 8 * grp + 4 * th + (s >> 2);
-        toff[st][th] = j < nb ? tokoff(j) : -1;
+        toff[st][th] = j < nb ? g.tokoff(j) : -1;
       }
-    auto row = [&](int b, int st, int th) {
-      return (bbase[b] >= 0 && toff[st][th] >= 0) ? bbase[b] + toff[st][th] : N;
-    };
     const bf16_t* kb = sK + 4 * (s & 3) + 32 * ksB;
     const bf16_t* vb = sV + 4 * (s & 3) + 16 * ct;
+    const u16x8_t ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
+    u16x8_t fa[2][KS][2], fv[2][KS];
+#define MHLA_FRAGS(bk, buf)                                                                  \
+  _Pragma("unroll") for (int st = 0; st < KS; ++st) {                                        \
+    const int bb_ = (bk) < M ? fb.b[bk] : -1;                                                \
+    const int r0 = (bb_ >= 0 && toff[st][0] >= 0) ? bb_ + toff[st][0] : N;                   \
+    const int r1 = (bb_ >= 0 && toff[st][1] >= 0) ? bb_ + toff[st][1] : N;                   \
+    fv[buf][st] = lds_tr8_rows(vb, RS, r0, r1);                                              \
+    fa[buf][st][0] = lds_tr8_rows(kb, RS, r0, r1);                                           \
+    fa[buf][st][1] = lds_tr8_rows(kb + 16, RS, r0, r1);                                      \
+  }
+    MHLA_FRAGS(0, 0)
 #pragma unroll
     for (int b = 0; b < MM; ++b) {
+      const int cb = b & 1;
+      if (b + 1 < MM) { MHLA_FRAGS(b + 1, cb ^ 1) }
       f32x4_t sb[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int r0 = row(b, st, 0), r1 = row(b, st, 1);
-        const u16x8_t bv = lds_tr8_rows(vb, RS, r0, r1);
+      for (int st = 0; st < KS; ++st)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          sb[hh] = mfma_bf16(lds_tr8_rows(kb + 16 * hh, RS, r0, r1), bv, sb[hh]);
+        for (int hh = 0; hh < 2; ++hh) sb[hh] = mfma_bf16(fa[cb][st][hh], fv[cb][st], sb[hh]);
+      if (b < M && b % NT == ct) {
+        f32x4_t zb[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) zb[hh] = mfma_bf16(fa[cb][st][hh], ones, zb[hh]);
+        if (s == 0) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            *reinterpret_cast<f32x4_t*>(zraw + b * DP + 32 * ksB + 16 * hh + 4 * grp) = zb[hh];
+        }
       }
 #pragma unroll
       for (int i = 0; i < MM; ++i) {
@@ -192,45 +233,29 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
         mix[i][1] += wr[i][b] * sb[1];
       }
     }
-    // z_b = sum_j phi(K_b)[j] for this item's 32 features, blocks b = ct, ct+NT, ..
-    // (a ones B operand puts z_b in every column)
-    const u16x8_t ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
-    for (int b = ct; b < M; b += NT) {
-      const int bb = blockbase(b);
-      f32x4_t zb[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int r0 = toff[st][0] >= 0 ? bb + toff[st][0] : N;
-        const int r1 = toff[st][1] >= 0 ? bb + toff[st][1] : N;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          zb[hh] = mfma_bf16(lds_tr8_rows(kb + 16 * hh, RS, r0, r1), ones, zb[hh]);
-      }
-      if (s == 0) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          *reinterpret_cast<f32x4_t*>(zraw + b * DP + 32 * ksB + 16 * hh + 4 * grp) = zb[hh];
-      }
-    }
+#undef MHLA_FRAGS
   }
 
-  // ---- stage phi(Q) (its loads were issued with K and V) -------------------
+  // ---- waves 8..15 stage phi(Q) meanwhile (loads issued at the start) -------
+  if (qwave) {
 #pragma unroll
-  for (int bt = 0; bt < 2; ++bt) {
-    const int base = bt * U * kFusedThreads;
-    if (base < items) {
-      if (bt > 0) { MHLA_LOAD(qr, Q, base) }
+    for (int bt = 0; bt < 2; ++bt) {
+      const int base = bt * UQ * QTHR;
+      if (base < items) {
+        if (bt > 0) { MHLA_LOAD(qr, Q, base, UQ, QTHR, qtid) }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int it = base + u * kFusedThreads + tid;
-        if (it < items) {
-          const int t = small_div(it, inv8);
-          const int f = it - t * F8;
-          *reinterpret_cast<u32x4_t*>(sQ + t * RSQ + 8 * f) = phi8<PHI>(qr[u]);
+        for (int u = 0; u < UQ; ++u) {
+          const int it = base + u * QTHR + qtid;
+          if (it < items) {
+            const int t = small_div(it, inv8);
+            const int f = it - t * F8;
+            *reinterpret_cast<u32x4_t*>(sQ + t * RSQ + 8 * f) = phi8<PHI>(qr[u]);
+          }
         }
       }
     }
   }
+  if (tid < M * M) sW[tid] = wv;
 #undef MHLA_LOAD
   lds_barrier();  // phi(K) / V are no longer read; z_b and phi(Q) are complete
 
@@ -240,29 +265,45 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
     for (int i = 0; i < MM; ++i)
       if (i < M) frag[((i * NT + ct) * DS + ksB) * 64 + lane] = pack_acc8(mix[i][0], mix[i][1]);
   }
-  for (int e = tid; e < M * DP; e += kFusedThreads) {
+  for (int e = tid; e < M * DP; e += NTHR) {
     const int i = e / DP, k = e - i * DP;
     float acc = 0.0f;
-    for (int b = 0; b < M; ++b) acc += Wh[i * M + b] * zraw[b * DP + k];
+    for (int b = 0; b < M; ++b) acc += sW[i * M + b] * zraw[b * DP + k];
     zmix[e] = acc;
   }
   lds_barrier();
 
   // ---- D. readout ------------------------------------------------------------
   // Wave w takes tiles w*tpw .. w*tpw+tpw-1 (16 queries each; consecutive tiles
-  // share a block), so the S~_i fragments are read once per block and wave.
+  // share a block).  All of the wave's phi(Q) operands are read first.
   const int ntile = M * QT;
-  const int tpw = (ntile + kFusedWaves - 1) / kFusedWaves;
-  int cur = -1, bb = 0;
-  u16x8_t af[NT][DS], az[DS];
-  for (int u = 0; u < tpw; ++u) {
+  const int tpw = (ntile + NWAVE - 1) / NWAVE;
+  u16x8_t bq[TPW][DS];
+  int tok[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
     const int tile = wave * tpw + u;
-    if (tile >= ntile) break;
+    const int i = tile / QT, j = (tile - i * QT) * 16 + s;
+    const bool real = u < tpw && tile < ntile && j < nb;
+    tok[u] = real ? fb.b[i] + g.tokoff(j) : -1;
+    const int row = real ? tok[u] : N;
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const bf16_t* p = sQ + row * RSQ + 32 * ks + 4 * grp;
+      bq[u][ks] = from_u2x2(*reinterpret_cast<const uint2*>(p),
+                            *reinterpret_cast<const uint2*>(p + 16));
+    }
+  }
+  int cur = -1;
+  u16x8_t af[NT][DS], az[DS];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = wave * tpw + u;
+    if (u >= tpw || tile >= ntile) break;
     const int i = tile / QT, qt = tile - i * QT;
     if (qt * 16 >= nb) continue;
     if (i != cur) {
       cur = i;
-      bb = blockbase(i);
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
@@ -276,29 +317,20 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(
                         : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    const int j = qt * 16 + s;
-    const int t = j < nb ? bb + tokoff(j) : N;
-    u16x8_t bq[DS];
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
-      const bf16_t* p = sQ + t * RSQ + 32 * ks + 4 * grp;
-      bq[ks] = from_u2x2(*reinterpret_cast<const uint2*>(p),
-                         *reinterpret_cast<const uint2*>(p + 16));
-    }
     f32x4_t o[NT], oz = zero4();
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       o[c] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks) o[c] = mfma_bf16(af[c][ks], bq[ks], o[c]);
+      for (int ks = 0; ks < DS; ++ks) o[c] = mfma_bf16(af[c][ks], bq[u][ks], o[c]);
     }
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[ks], oz);
+    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
     // row 0 of the z~ tile (lane s of group 0, element 0) is phi(q).z~_i
     const float den = __shfl(oz[0], s);
     const float rd = den == 0.0f ? 0.0f : 1.0f / den;
-    if (j < nb) {
-      bf16_t* yrow = Y + off + (size_t)t * d;
+    if (tok[u] >= 0) {
+      bf16_t* yrow = Y + off + (size_t)tok[u] * d;
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         const int cl = 16 * c + 4 * grp;
@@ -338,8 +370,10 @@ int launch_fused_t(long slices, int H, int N, int d, const Geo& g, const bf16_t*
       return -1;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  k_fused<DP, NBP, MM, PHI><<<dim3((unsigned)slices), dim3(kFusedThreads), lds, st>>>(
-      Q, K, V, W, Y, g, H, N, d);
+  FusedBases fb;
+  for (int b = 0; b < kFusedMaxM; ++b) fb.b[b] = b < g.M ? g.blockbase(b) : 0;
+  k_fused<DP, NBP, MM, PHI><<<dim3((unsigned)slices), dim3(64 * fused_waves(MM)), lds, st>>>(
+      Q, K, V, W, Y, g, fb, H, N, d);
   return 0;
 }
 
