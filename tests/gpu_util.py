@@ -20,11 +20,19 @@ def to_device(inp: Inputs):
     return t(inp.q), t(inp.k), t(inp.v), torch.from_numpy(inp.w).cuda()
 
 
-def run(inp: Inputs, path=m.MHLA_PATH_AUTO, dev=None, stream=None):
+def run(inp: Inputs, path=m.MHLA_PATH_AUTO, dev=None, stream=None, skip_unsupported=False):
+    """Run one path through the C ABI.  With skip_unsupported, a path that
+    rejects the shape (MHLA_ERR_UNSUPPORTED, nothing enqueued) skips the test."""
     q, k, v, w = dev if dev is not None else to_device(inp)
     out = torch.empty_like(q)
-    m.mhla_forward_path(q, k, v, w, out, (inp.wl.grid, inp.wl.block), inp.wl.phi, path,
-                        stream=stream)
+    try:
+        m.mhla_forward_path(q, k, v, w, out, (inp.wl.grid, inp.wl.block), inp.wl.phi, path,
+                            stream=stream)
+    except m.MhlaError as e:
+        if skip_unsupported and e.code == m.MHLA_ERR_UNSUPPORTED:
+            import pytest
+            pytest.skip("path %d does not take this shape" % path)
+        raise
     torch.cuda.synchronize()
     return out
 

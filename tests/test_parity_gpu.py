@@ -16,7 +16,7 @@ from gpu_util import TOL, run, slice_error, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
-ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED, m.MHLA_PATH_BLOCKED]
+ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED, m.MHLA_PATH_BLOCKED, m.MHLA_PATH_PAIRS]
 
 
 def _oracle_full(inp):
@@ -47,13 +47,14 @@ def _check_sampled(inp, y, n_slices, n_rows, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "deit_t", "dit_xl2", "hires"])
-@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC, m.MHLA_PATH_BLOCKED])
+@pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC, m.MHLA_PATH_BLOCKED,
+                                  m.MHLA_PATH_PAIRS])
 def test_workload_full(name, path):
-    if path == m.MHLA_PATH_BLOCKED and WORKLOADS[name].dtype != DTYPE_BF16:
+    if path in (m.MHLA_PATH_BLOCKED, m.MHLA_PATH_PAIRS) and WORKLOADS[name].dtype != DTYPE_BF16:
         pytest.skip("the MFMA paths take bf16 inputs")
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
-    y = to_f64(run(inp, path))
+    y = to_f64(run(inp, path, skip_unsupported=(path == m.MHLA_PATH_PAIRS)))
     ref = _oracle_full(inp)
     err = slice_error(y, ref)
     print("PARITY %s path=%d err=%.3e" % (name, path, err))
@@ -91,7 +92,7 @@ FUSED_CASES = [
 def test_small_shapes(grid, block, d, phi, path):
     wl = custom_workload(3, 2, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 997)
     inp = make_inputs(wl)
-    y = to_f64(run(inp, path))
+    y = to_f64(run(inp, path, skip_unsupported=(path == m.MHLA_PATH_PAIRS)))
     err = slice_error(y, _oracle_full(inp))
     print("PARITY small %s %s d=%d phi=%d path=%d err=%.3e" % (grid, block, d, phi, path, err))
     assert err <= TOL[DTYPE_BF16]
@@ -120,6 +121,48 @@ def test_blocked_shapes(grid, block, d, phi):
     assert err <= TOL[DTYPE_BF16]
 
 
+PAIRS_CASES = [
+    # (grid, block, d, phi): blocks of at most 16 tokens, the token-pair order
+    ((1, 16, 16), (1, 4, 4), 72, PHI_ELU1),    # DiT-like, d = 72 (16-wide tail step)
+    ((1, 12, 20), (1, 3, 4), 64, PHI_RELU),    # 12-token blocks, M = 20 (odd pairs)
+    ((1, 9, 9), (1, 3, 3), 96, PHI_ELU1),      # 9-token blocks, M = 9 (odd M)
+    ((4, 8, 8), (1, 2, 4), 32, PHI_RELU),      # 3-D grid, M = 32 (4 query blocks per wave)
+    ((1, 4, 4), (1, 1, 1), 16, PHI_ELU1),      # one token per block, M = 16
+    ((1, 8, 8), (1, 4, 4), 48, PHI_RELU),      # M = 4 (waves without a query block)
+    ((1, 10, 16), (1, 2, 8), 80, PHI_ELU1),    # d = 80: a second O^T row tile
+]
+
+
+@pytest.mark.parametrize("grid,block,d,phi", PAIRS_CASES)
+def test_pairs_shapes(grid, block, d, phi):
+    wl = custom_workload(2, 3, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 983)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_PAIRS))
+    assert np.all(np.isfinite(y))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY pairs %s %s d=%d phi=%d M=%d err=%.3e" % (grid, block, d, phi, wl.M, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+@pytest.mark.parametrize("kind", ["identity", "sparse_rows", "unnormalised"])
+def test_pairs_special_mixing_matrices(kind):
+    wl = custom_workload(2, 2, 72, (1, 16, 16), (1, 4, 4), PHI_RELU, DTYPE_BF16, index=8)
+    inp = make_inputs(wl)
+    M = wl.M
+    if kind == "identity":
+        inp.w = np.broadcast_to(np.eye(M, dtype=np.float32), (wl.H, M, M)).copy()
+    elif kind == "sparse_rows":
+        inp.w[:, :, 3] = 0.0
+        inp.w[:, 5, :] = 0.0
+        inp.w[:, 5, 11] = 1.0
+    else:
+        inp.w = (inp.w * np.float32(11.0)).astype(np.float32)
+    y = to_f64(run(inp, m.MHLA_PATH_PAIRS))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY pairs W=%s err=%.3e" % (kind, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
 @pytest.mark.parametrize("d", [1, 5, 16, 17, 64, 128])
 def test_fp32_generic_any_d(d):
     wl = custom_workload(2, 2, d, (1, 6, 10), (1, 3, 5), PHI_ELU1, DTYPE_F32, index=d)
@@ -130,7 +173,7 @@ def test_fp32_generic_any_d(d):
     assert err <= TOL[DTYPE_F32]
 
 
-@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("path", [p for p in ALL_PATHS if p != m.MHLA_PATH_PAIRS])
 @pytest.mark.parametrize("kind", ["identity", "sparse_rows", "unnormalised"])
 def test_special_mixing_matrices(path, kind):
     """W = I (block-local), rows with zeros, and rows that do not sum to 1."""
@@ -153,6 +196,8 @@ def test_special_mixing_matrices(path, kind):
 
 @pytest.mark.parametrize("path", ALL_PATHS)
 def test_zero_denominator_rows(path):
+    if path == m.MHLA_PATH_PAIRS:
+        pytest.skip("covered with 16-token blocks in test_pairs_zero_denominator_rows")
     """ReLU query with every coordinate <= 0: phi(q) = 0, the row is written as 0."""
     wl = custom_workload(1, 2, 32, (1, 8, 8), (1, 4, 4), PHI_RELU, DTYPE_BF16, index=6)
     inp = make_inputs(wl)
@@ -164,6 +209,16 @@ def test_zero_denominator_rows(path):
     assert np.all(y[0, 1, 7] == 0.0) and np.all(y[0, 0, 63] == 0.0)
     err = slice_error(y, _oracle_full(inp))
     assert err <= TOL[DTYPE_BF16]
+
+
+def test_pairs_zero_denominator_rows():
+    wl = custom_workload(1, 2, 32, (1, 8, 8), (1, 4, 4), PHI_RELU, DTYPE_BF16, index=9)
+    inp = make_inputs(wl)
+    from mhla_inputs import bf16_round_bits
+    inp.q[0, 1, 7] = bf16_round_bits(-np.abs(np.random.default_rng(1).standard_normal(wl.d)).astype(np.float32))
+    y = to_f64(run(inp, m.MHLA_PATH_PAIRS))
+    assert np.all(y[0, 1, 7] == 0.0)
+    assert slice_error(y, _oracle_full(inp)) <= TOL[DTYPE_BF16]
 
 
 def test_fp32_zero_denominator_rows():

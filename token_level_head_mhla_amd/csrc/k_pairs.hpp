@@ -1,0 +1,306 @@
+// k_pairs.hpp -- MHLA forward in the token-pair order of "MHLA: Restoring
+// Expressivity of Linear Attention via Token-Level Multi-Head" §4.2 Eq. 5
+// (bf16 in/out, gfx950 MFMA), for blocks of at most 16 tokens:
+//
+//   Y_q = sum_b W[i,b] sum_{j in b} (phi(q).phi(k_j)) v_j
+//         / sum_b W[i,b] sum_{j in b} phi(q).phi(k_j),      q in block i.
+//
+// This is the same result as the summary order up to rounding (the
+// summaries S_b are never formed), and it is the cheaper order when a block
+// has fewer tokens than d, because it needs no d x d state per block and no
+// workspace at all.
+//
+// One workgroup of 8 waves per (batch, head) slice; each wave owns query
+// blocks i = wave, wave + 8, ...  K and V of the slice are staged in LDS
+// (phi applied to K; V gets an extra column of ones at index d, so the
+// denominator falls out of the same product as row d of O^T).  For every
+// pair of key blocks (b0, b1):
+//   P^T[j][q] = phi(K_b) phi(Q_i)^T          (16x16 per block, MFMA over d)
+//   P'^T      = W[i,b] P^T, packed to bf16 -- already the B-operand layout
+//               of the next product (contraction over the 32 keys)
+//   O^T      += V_{b0,b1}^T P'^T             (MFMA 16x16x32, V^T from LDS
+//                                             transpose reads)
+// Finally Y_q = O^T[0..d-1][q] / O^T[d][q], with a zero row when O^T[d][q] = 0.
+#pragma once
+
+#include "mhla_mfma.hpp"
+
+namespace mhla {
+
+constexpr int kPairsThreads = 512;
+constexpr int kPairsWaves = kPairsThreads / 64;
+constexpr int kPairsMaxQB = 4;  // query blocks per wave (M <= 32)
+
+typedef short i16x4v_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16_k16(const i16x4v_t& a, const i16x4v_t& b,
+                                                 const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4v_t, a),
+                                                   __builtin_bit_cast(i16x4v_t, b), c, 0, 0, 0);
+}
+
+// DK: contraction width over features (multiple of 16: 32-steps plus an
+// optional 16-step tail).  DO: rows of O^T (multiple of 16, > d: the row d
+// holds the denominator).
+template <int DK, int DO>
+struct PairsLayout {
+  static constexpr int RSK = DK + 8;   // LDS row stride of phi(K)
+  static constexpr int RSV = DO;       // LDS row stride of V (+ ones column)
+  static constexpr int KS = DK / 32;   // 32-feature steps
+  static constexpr bool TAIL = (DK % 32) != 0;
+  static constexpr int CT = DO / 16;   // O^T row tiles
+  __host__ __device__ static size_t k_bytes(int N) { return (size_t)(N + 1) * RSK * 2; }
+  __host__ __device__ static size_t v_bytes(int N) { return (size_t)(N + 1) * RSV * 2; }
+  __host__ __device__ static size_t total(int N, int M) {
+    return k_bytes(N) + v_bytes(N) + (size_t)M * M * 4 + (size_t)kPairsMaxM * 4;
+  }
+  static constexpr int kPairsMaxM = 32;
+};
+
+template <int DK, int DO, int QB, int PHI>
+__global__ __launch_bounds__(kPairsThreads) void k_pairs(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, int H, int N, int d) {
+  using L = PairsLayout<DK, DO>;
+  constexpr int RSK = L::RSK, RSV = L::RSV, KS = L::KS, CT = L::CT;
+  constexpr bool TAIL = L::TAIL;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int M = g.M, nb = g.nb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.x;
+  const int h = (int)(slice % H);
+  const size_t off = (size_t)slice * N * d;
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + L::k_bytes(N));
+  float* sW = reinterpret_cast<float*>(smem + L::k_bytes(N) + L::v_bytes(N));
+  int* sB = reinterpret_cast<int*>(sW + M * M);  // first token of every block
+
+  // ---- stage: zero pad columns and row N, then phi(K), V, ones column ------
+  for (int e = tid; e < (int)((L::k_bytes(N) + L::v_bytes(N)) / 16); e += kPairsThreads)
+    reinterpret_cast<u32x4_t*>(smem)[e] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int e = tid; e < M * M; e += kPairsThreads) sW[e] = W[(size_t)h * M * M + e];
+  for (int b = tid; b < M; b += kPairsThreads) sB[b] = g.blockbase(b);
+  lds_barrier();
+  {
+    const int F8 = d >> 3;
+    const float inv8 = 1.0f / (float)F8;
+    for (int it = tid; it < N * F8; it += kPairsThreads) {
+      const int t = (int)(((float)it + 0.5f) * inv8);
+      const int f = it - t * F8;
+      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + off + (size_t)it * 8);
+      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + off + (size_t)it * 8);
+      *reinterpret_cast<u32x4_t*>(sK + t * RSK + 8 * f) = phi8<PHI>(kr);
+      *reinterpret_cast<u32x4_t*>(sV + t * RSV + 8 * f) = vr;
+    }
+    for (int t = tid; t < N; t += kPairsThreads) sV[t * RSV + d] = 0x3f80;  // bf16 1.0
+  }
+  lds_barrier();
+
+  // ---- this wave's query blocks: phi(Q) operands straight from global -------
+  // B operand of P^T = phi(K) phi(Q)^T: lane (s, grp) holds query s of the
+  // block, features 32ks + 8grp .. +7 (and 32KS + 4grp .. +3 for the tail).
+  const int myq = (M - wave + kPairsWaves - 1) / kPairsWaves;  // query blocks of this wave
+  int qtok[QB];
+  u16x8_t qf[QB][KS > 0 ? KS : 1];
+  i16x4v_t qt[QB];
+#pragma unroll
+  for (int u = 0; u < QB; ++u) {
+    const int i = wave + u * kPairsWaves;
+    const bool real = u < myq && s < nb;
+    qtok[u] = real ? sB[i] + g.tokoff(s) : -1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k0 = 32 * ks + 8 * grp;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (real && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)qtok[u] * d + k0);
+      qf[u][ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
+    }
+    if constexpr (TAIL) {
+      const int k0 = 32 * KS + 4 * grp;
+      uint2 v = make_uint2(0u, 0u);
+      if (real && k0 < d) v = *reinterpret_cast<const uint2*>(Q + off + (size_t)qtok[u] * d + k0);
+      const uint2 p = phi4<PHI>(v);
+      // features past d must be 0 in at least one operand: phi(0) = 1 for
+      // elu+1, so mask them here (phi(K) has zero pad columns anyway)
+      qt[u] = __builtin_bit_cast(i16x4v_t, k0 < d ? p : make_uint2(0u, 0u));
+    }
+  }
+
+  f32x4_t o[QB][CT];
+#pragma unroll
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) o[u][c] = zero4();
+
+  // key member s of a block: row of this lane for the phi(K) A operand;
+  // key member 4grp + s/4: row supplied to the V^T transpose reads
+  const int koff = s < nb ? g.tokoff(s) : -1;
+  const int vj = 4 * grp + (s >> 2);
+  const int voff = vj < nb ? g.tokoff(vj) : -1;
+  for (int b0 = 0; b0 < M; b0 += 2) {
+    const int b1 = b0 + 1;
+    int kr[2], vr[2];
+    float wb[2][QB];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int b = b0 + hb;
+      const bool real = b < M;
+      const int bb = real ? sB[b] : 0;
+      kr[hb] = (real && koff >= 0) ? bb + koff : N;
+      vr[hb] = (real && voff >= 0) ? bb + voff : N;
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int i = wave + u * kPairsWaves;
+        wb[hb][u] = (real && u < myq) ? sW[i * M + b] : 0.0f;
+      }
+    }
+    (void)b1;
+    // phi(K) A operands of the two key blocks (row = key member s)
+    u16x8_t ka[2][KS > 0 ? KS : 1];
+    i16x4v_t kt[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[hb][ks] = *reinterpret_cast<const u16x8_t*>(sK + kr[hb] * RSK + 32 * ks + 8 * grp);
+      if constexpr (TAIL)
+        kt[hb] = *reinterpret_cast<const i16x4v_t*>(sK + kr[hb] * RSK + 32 * KS + 4 * grp);
+    }
+    // V^T A operands: rows c = 16ct + s, keys {4grp..4grp+3} of b0 then of b1
+    u16x8_t va[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      va[c] = lds_tr8_rows(sV + 16 * c + 4 * (s & 3), RSV, vr[0], vr[1]);
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      if (u >= myq) break;
+      f32x4_t p[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        p[hb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) p[hb] = mfma_bf16(ka[hb][ks], qf[u][ks], p[hb]);
+        if constexpr (TAIL) p[hb] = mfma_bf16_k16(kt[hb], qt[u], p[hb]);
+        p[hb] *= wb[hb][u];
+      }
+      // p[hb] lane (s, grp) element r = P'^T[key 4grp + r of block b0+hb][query s]
+      const u16x8_t pb = pack_acc8(p[0], p[1]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[u][c] = mfma_bf16(va[c], pb, o[u][c]);
+    }
+  }
+
+  // ---- epilogue: row d of O^T is the denominator ------------------------------
+  const int dct = d >> 4, dg = (d & 15) >> 2, dr = d & 3;
+#pragma unroll
+  for (int u = 0; u < QB; ++u) {
+    if (u >= myq) break;
+    float dv = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      if (c == dct) dv = o[u][c][dr];
+    const float den = __shfl(dv, 16 * dg + s);
+    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+    if (qtok[u] >= 0) {
+      bf16_t* yrow = Y + off + (size_t)qtok[u] * d;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int cl = 16 * c + 4 * grp;
+        if (cl < d)
+          *reinterpret_cast<uint2*>(yrow + cl) = make_uint2(pack2(o[u][c][0] * rd, o[u][c][1] * rd),
+                                                            pack2(o[u][c][2] * rd, o[u][c][3] * rd));
+      }
+    }
+  }
+}
+
+inline int pairs_dk(int d) { return (d + 15) / 16 * 16; }
+inline int pairs_do(int d) { return (d + 1 + 15) / 16 * 16; }
+
+template <int DK, int DO>
+inline size_t pairs_lds_t(int N, int M) { return PairsLayout<DK, DO>::total(N, M); }
+
+// (DK, DO) pairs compiled: d = 16 (16, 32), 32 (32, 48), 48 (48, 64), 64 (64, 80),
+// 72 (80, 80), 80 (80, 96), 96 (96, 112).
+inline bool pairs_dims(int d, int* dk, int* dout) {
+  *dk = pairs_dk(d);
+  *dout = pairs_do(d);
+  switch (d) {
+    case 16: case 32: case 48: case 64: case 72: case 80: case 96: return true;
+    default: return false;
+  }
+}
+
+inline size_t pairs_lds(int d, int N, int M) {
+  switch (d) {
+    case 16: return pairs_lds_t<16, 32>(N, M);
+    case 32: return pairs_lds_t<32, 48>(N, M);
+    case 48: return pairs_lds_t<48, 64>(N, M);
+    case 64: return pairs_lds_t<64, 80>(N, M);
+    case 72: return pairs_lds_t<80, 80>(N, M);
+    case 80: return pairs_lds_t<80, 96>(N, M);
+    default: return pairs_lds_t<96, 112>(N, M);
+  }
+}
+
+inline bool pairs_supports(int dtype, int d, int M, int nb, int N) {
+  int dk, dout;
+  if (dtype != 1 || !pairs_dims(d, &dk, &dout)) return false;
+  if (nb > 16 || M > kPairsWaves * kPairsMaxQB) return false;
+  return pairs_lds(d, N, M) <= 160 * 1024;
+}
+
+template <int DK, int DO, int QB, int PHI>
+int launch_pairs_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                   const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
+  const size_t lds = PairsLayout<DK, DO>::total(N, g.M);
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const void* fn = reinterpret_cast<const void*>(&k_pairs<DK, DO, QB, PHI>);
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+        hipSuccess)
+      return -1;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  k_pairs<DK, DO, QB, PHI><<<dim3((unsigned)slices), dim3(kPairsThreads), lds, st>>>(
+      Q, K, V, W, Y, g, H, N, d);
+  return 0;
+}
+
+template <int DK, int DO, int PHI>
+int launch_pairs_q(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                   const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
+  const int qb = (g.M + kPairsWaves - 1) / kPairsWaves;
+  if (qb <= 1) return launch_pairs_t<DK, DO, 1, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  if (qb <= 2) return launch_pairs_t<DK, DO, 2, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  return launch_pairs_t<DK, DO, 4, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+}
+
+template <int PHI>
+int launch_pairs_p(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                   const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
+  switch (d) {
+    case 16: return launch_pairs_q<16, 32, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 32: return launch_pairs_q<32, 48, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 48: return launch_pairs_q<48, 64, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 64: return launch_pairs_q<64, 80, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 72: return launch_pairs_q<80, 80, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    case 80: return launch_pairs_q<80, 96, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+    default: return launch_pairs_q<96, 112, PHI>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  }
+}
+
+inline int launch_pairs(long slices, int H, int N, int d, const Geo& g, int phi, const bf16_t* Q,
+                        const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y,
+                        hipStream_t st) {
+  if (phi == PHI_RELU) return launch_pairs_p<PHI_RELU>(slices, H, N, d, g, Q, K, V, W, Y, st);
+  return launch_pairs_p<PHI_ELU1>(slices, H, N, d, g, Q, K, V, W, Y, st);
+}
+
+}  // namespace mhla

@@ -19,6 +19,7 @@
 #include "k_generic.hpp"
 #include "k_fused.hpp"
 #include "k_blocked.hpp"
+#include "k_pairs.hpp"
 
 namespace mhla {
 namespace {
@@ -97,12 +98,14 @@ bool path_supports(int path, const Problem& p) {
     case MHLA_PATH_GENERIC: return p.slices() <= 65535;  // slices run along grid y/z
     case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
     case MHLA_PATH_BLOCKED: return blocked_supports(p.dtype, p.d, p.slices());
+    case MHLA_PATH_PAIRS: return pairs_supports(p.dtype, p.d, p.g.M, p.g.nb, p.N);
     default: return false;
   }
 }
 
 int choose_path(const Problem& p) {
   if (path_supports(MHLA_PATH_FUSED, p)) return MHLA_PATH_FUSED;
+  if (path_supports(MHLA_PATH_PAIRS, p)) return MHLA_PATH_PAIRS;
   if (path_supports(MHLA_PATH_BLOCKED, p)) return MHLA_PATH_BLOCKED;
   if (path_supports(MHLA_PATH_GENERIC, p)) return MHLA_PATH_GENERIC;
   return -MHLA_ERR_UNSUPPORTED;
@@ -213,6 +216,9 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
   } else if (path == MHLA_PATH_FUSED) {
     rc = launch_fused(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
                       (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, st);
+  } else if (path == MHLA_PATH_PAIRS) {
+    rc = launch_pairs(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
+                      (const bf16_t*)V, W, (bf16_t*)out, st);
   } else if (path == MHLA_PATH_BLOCKED) {
     rc = launch_blocked(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
                         (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, (bf16_t*)ws, st);
