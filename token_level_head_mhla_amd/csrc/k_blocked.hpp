@@ -25,7 +25,6 @@ namespace mhla {
 constexpr int kBlkThreads = 256;
 constexpr int kBlkWaves = kBlkThreads / 64;
 constexpr int kMixEB = 128;  // entries per mixing workgroup
-constexpr int kMixIB = 128;  // query blocks per mixing workgroup
 constexpr int kMixKB = 32;   // key blocks per mixing step
 
 template <int DP>
@@ -147,102 +146,128 @@ __global__ __launch_bounds__(kBlkThreads) void k_summary_mfma(
 
 // ---------------------------------------------------------------------------
 // Mixing: per slice, S~[i][e] = sum_b W[h][i][b] S[b][e], computed as the
-// transposed product S~^T = S^T W^T so that each lane stores four
-// consecutive entries.  grid = (EP / 128, ceil(M / 128), slices), block = 256;
-// wave (we, wi) owns entries 64we .. 64we+63 and query blocks 64wi .. 64wi+63
-// of the workgroup's 128 x 128 tile.
-template <int EP>
+// transposed product S~^T = S^T W^T so that each lane stores four consecutive
+// entries.  1-D grid of 8 * ceil(slices / 8) * nE * nI workgroups (nE = EP /
+// 128 entry tiles, nI = ceil(M / IB) query-block tiles), block = 256.
+// Workgroups are dealt to the 8 XCDs round-robin (id % 8), so workgroup id
+// maps to XCD x = id % 8 and that XCD walks slices x, x + 8, ... in turn;
+// within a slice the nI query-block tiles of one entry tile are adjacent.
+// A slice's W (and each S entry column) is therefore fetched into one XCD's
+// L2 and reused there.  The workgroup tile is 128 entries x IB query blocks;
+// wave (we, wi) owns EW entries x IW query blocks: (EW, IW) = (64, 64) for
+// IB = 128 and (32, 64) for IB = 64.  The key
+// blocks are walked in steps of 32: the next step's S and W tiles are loaded
+// into registers while the current step's tiles (double-buffered in LDS) feed
+// the MFMAs, so there is one barrier per step.
+template <int EP, int IB>
 __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
                                                           const float* __restrict__ W,
-                                                          bf16_t* __restrict__ St, int M, int H) {
-  constexpr int EB = kMixEB, IB = kMixIB, KB = kMixKB;
+                                                          bf16_t* __restrict__ St, int M, int H,
+                                                          long nslices) {
+  constexpr int EB = kMixEB, KB = kMixKB;
+  constexpr int EW = IB == 64 ? 32 : 64, IW = 64;
+  constexpr int AT = EW / 16, BT = IW / 16;        // MFMA tiles per wave along e and i
+  constexpr int NWE = EB / EW;                      // waves along e
   constexpr int SRS = EB + 16;  // LDS row stride of the S tile (rows = key blocks)
-  constexpr int WRS = KB + 8;   // LDS row stride of the W tile (rows = query blocks)
-  __shared__ __attribute__((aligned(16))) bf16_t sS[KB * SRS];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[IB * WRS];
+  constexpr int WRS = KB + 16;  // LDS row stride of the W tile: 16-byte reads of 16
+                                // consecutive rows are free of bank conflicts
+  constexpr int SCH = KB * EB / 8 / kBlkThreads;   // 16-byte S chunks per thread per step
+  constexpr int WCH = IB * KB / 4 / kBlkThreads;   // 4-float W chunks per thread per step
+  static_assert(SCH * 8 * kBlkThreads == KB * EB && WCH * 4 * kBlkThreads == IB * KB, "tiles");
+  __shared__ __attribute__((aligned(16))) bf16_t sS[2][KB * SRS];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][IB * WRS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = lane & 15, grp = lane >> 4;
-  const int we = wave & 1, wi = wave >> 1;
-  const int e0 = blockIdx.x * EB, i0 = blockIdx.y * IB;
-  const long slice = blockIdx.z;
+  const int we = wave % NWE, wi = wave / NWE;
+  const int nE = EP / EB, nI = (M + IB - 1) / IB;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int per = nE * nI;
+  const long slice = (long)(j / per) * 8 + xcd;
+  if (slice >= nslices) return;  // no barrier has been reached yet
+  const int rem = j - (j / per) * per;
+  const int e0 = (rem / nI) * EB, i0 = (rem - (rem / nI) * nI) * IB;
   const int h = (int)(slice % H);
   const bf16_t* Ss = S + (size_t)slice * M * EP;
   const float* Wh = W + (size_t)h * M * M;
+  const bool wvec = (M & 3) == 0;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[AT][BT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < AT; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = zero4();
+    for (int c = 0; c < BT; ++c) acc[a][c] = zero4();
 
-  for (int b0 = 0; b0 < M; b0 += KB) {
-    // S tile: KB rows x EB entries = 512 chunks of 8 bf16, 2 per thread
-    u32x4_t sr[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + kBlkThreads * u;
-      const int r = c >> 4, f = c & 15;
-      sr[u] = b0 + r < M
-                  ? *reinterpret_cast<const u32x4_t*>(Ss + (size_t)(b0 + r) * EP + e0 + 8 * f)
-                  : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    // W tile: IB rows x KB columns (fp32) = 1024 chunks of 4, 4 per thread
-    f32x4_t wr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + kBlkThreads * u;
-      const int r = c >> 3, f = c & 7;
-      const int i = i0 + r, bcol = b0 + 4 * f;
-      f32x4_t v = zero4();
-      if (i < M) {
-        if (bcol + 3 < M && (M & 3) == 0) {
-          v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bcol);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (bcol + q < M) v[q] = Wh[(size_t)i * M + bcol + q];
-        }
-      }
-      wr[u] = v;
-    }
-    lds_barrier();  // the previous step's reads are done
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + kBlkThreads * u;
-      const int r = c >> 4, f = c & 15;
-      *reinterpret_cast<u32x4_t*>(sS + r * SRS + 8 * f) = sr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + kBlkThreads * u;
-      const int r = c >> 3, f = c & 7;
-      *reinterpret_cast<uint2*>(sW + r * WRS + 4 * f) =
-          make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));
-    }
-    lds_barrier();
+  u32x4_t sr[SCH];
+  f32x4_t wr[WCH];
+#define MHLA_MIX_GLOAD(b0)                                                                \
+  _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (EB / 8), f = c % (EB / 8);                                         \
+    sr[u] = (b0) + r < M                                                                  \
+                ? *reinterpret_cast<const u32x4_t*>(Ss + (size_t)((b0) + r) * EP + e0 + 8 * f) \
+                : u32x4_t{0u, 0u, 0u, 0u};                                                \
+  }                                                                                       \
+  _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (KB / 4), f = c % (KB / 4);                                         \
+    const int i = i0 + r, bc = (b0) + 4 * f;                                              \
+    f32x4_t v = zero4();                                                                  \
+    if (i < M) {                                                                          \
+      if (wvec && bc + 3 < M) {                                                           \
+        v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bc);                   \
+      } else {                                                                            \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M) v[q] = Wh[(size_t)i * M + bc + q]; \
+      }                                                                                   \
+    }                                                                                     \
+    wr[u] = v;                                                                            \
+  }
+#define MHLA_MIX_LSTORE(buf)                                                              \
+  _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (EB / 8), f = c % (EB / 8);                                         \
+    *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) = sr[u];                       \
+  }                                                                                       \
+  _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (KB / 4), f = c % (KB / 4);                                         \
+    *reinterpret_cast<uint2*>(sW[buf] + r * WRS + 4 * f) =                                \
+        make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));                 \
+  }
+
+  const int nk = (M + KB - 1) / KB;
+  MHLA_MIX_GLOAD(0)
+  MHLA_MIX_LSTORE(0)
+  lds_barrier();
+  for (int k = 0; k < nk; ++k) {
+    const int buf = k & 1;
+    if (k + 1 < nk) { MHLA_MIX_GLOAD((k + 1) * KB) }
     // A = S^T (rows e, contraction b via transpose reads: b = 8grp .. 8grp+7),
     // B = W^T (column i, the same b: W[i][8grp .. 8grp+7] is contiguous).
-    u16x8_t af[4], bw[4];
+    u16x8_t af[AT], bw[BT];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[a] = lds_tr8(sS, SRS, 0, 64 * we + 16 * a, lane);
+    for (int a = 0; a < AT; ++a) af[a] = lds_tr8(sS[buf], SRS, 0, EW * we + 16 * a, lane);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      bw[c] = *reinterpret_cast<const u16x8_t*>(sW + (64 * wi + 16 * c + s) * WRS + 8 * grp);
+    for (int c = 0; c < BT; ++c)
+      bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf] + (IW * wi + 16 * c + s) * WRS + 8 * grp);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+      for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+    if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1) }
+    lds_barrier();
   }
+#undef MHLA_MIX_GLOAD
+#undef MHLA_MIX_LSTORE
   // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int i = i0 + 64 * wi + 16 * c + s;
+  for (int c = 0; c < BT; ++c) {
+    const int i = i0 + IW * wi + 16 * c + s;
     if (i < M) {
-      bf16_t* row = St + ((size_t)slice * M + i) * EP + e0 + 64 * we;
+      bf16_t* row = St + ((size_t)slice * M + i) * EP + e0 + EW * we;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < AT; ++a)
         *reinterpret_cast<uint2*>(row + 16 * a + 4 * grp) =
             make_uint2(pack2(acc[a][c][0], acc[a][c][1]), pack2(acc[a][c][2], acc[a][c][3]));
     }
@@ -315,8 +340,17 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
 }
 
 // ---------------------------------------------------------------------------
-inline bool blocked_supports(int dtype, int d, long slices) {
-  return dtype == 1 && d % 8 == 0 && d <= 96 && slices <= 65535;
+inline size_t blocked_ws_elems(int d);
+
+// Query blocks per mixing workgroup.
+inline int mix_ib(int M) { return M <= 64 ? 64 : 128; }
+
+inline bool blocked_supports(int dtype, int d, int M, long slices) {
+  if (dtype != 1 || d % 8 != 0 || d > 96 || slices > 65535) return false;
+  // the mixing grid is 1-D: keep its thread count below 2^31
+  const int ib = mix_ib(M);
+  const long n = (slices + 7) / 8 * 8 * (long)(blocked_ws_elems(d) / kMixEB) * ((M + ib - 1) / ib);
+  return n * kBlkThreads < (1L << 31);
 }
 
 inline size_t blocked_ws_elems(int d) {
@@ -342,8 +376,13 @@ int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_
   const unsigned nsl = (unsigned)slices;
   const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
   k_summary_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, V, S, g, N, d);
-  k_mix_mfma<D::EP><<<dim3(D::EP / kMixEB, (g.M + kMixIB - 1) / kMixIB, nsl), kBlkThreads, 0,
-                      st>>>(S, W, St, g.M, H);
+  const long xslices = (slices + 7) / 8 * 8;
+  const int ib = mix_ib(g.M);
+  const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((g.M + ib - 1) / ib));
+  if (ib == 64)
+    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices);
+  else
+    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices);
   k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
   return 0;
 }

@@ -97,7 +97,7 @@ bool path_supports(int path, const Problem& p) {
   switch (path) {
     case MHLA_PATH_GENERIC: return p.slices() <= 65535;  // slices run along grid y/z
     case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
-    case MHLA_PATH_BLOCKED: return blocked_supports(p.dtype, p.d, p.slices());
+    case MHLA_PATH_BLOCKED: return blocked_supports(p.dtype, p.d, p.g.M, p.slices());
     case MHLA_PATH_PAIRS: return pairs_supports(p.dtype, p.d, p.g.M, p.g.nb, p.N);
     default: return false;
   }
