@@ -39,108 +39,97 @@ struct BlockedDims {
 inline int blocked_dp(int d) { return (d + 31) / 32 * 32; }
 
 // ---------------------------------------------------------------------------
-// Summaries.  grid = (ceil(M / 4), slices), block = 256; wave w takes key
-// block 4*blockIdx.x + w and walks its tokens in chunks of 64.
+// Summaries.  grid = (M, slices), block = 64 * NT: one workgroup per key block
+// and one wave per 16-column tile ct of the value dimension.  The block's
+// tokens are staged in LDS (phi applied to K) 64 at a time; wave ct forms
+// S[:, 16ct .. 16ct+15] from transpose-read operands, and wave 0 also forms
+// z_b (a ones B operand).  Small LDS and register footprints keep ~24 waves
+// per CU, which hides the load latency of this bandwidth-bound kernel.
 template <int DP, int PHI>
-__global__ __launch_bounds__(kBlkThreads) void k_summary_mfma(
+__global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
     const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, bf16_t* __restrict__ S, Geo g,
     int N, int d) {
   using D = BlockedDims<DP>;
   constexpr int NT = D::NT, RS = D::RS, EP = D::EP;
+  constexpr int NTHR = 64 * NT;
   constexpr int F8P = DP / 8;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kBlkWaves][2][64 * RS];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s = lane & 15, grp = lane >> 4;
+  constexpr int UCH = 64 * F8P / NTHR;  // 16-byte chunks per thread and tensor (= 2)
+  __shared__ __attribute__((aligned(16))) bf16_t sk[64 * RS];
+  __shared__ __attribute__((aligned(16))) bf16_t sv[64 * RS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int ct = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long slice = blockIdx.y;
-  const int b = blockIdx.x * kBlkWaves + wave;
-  const bool valid = b < g.M;
+  const int b = blockIdx.x;
   const size_t off = (size_t)slice * N * d;
-  bf16_t* sk = lds[wave][0];
-  bf16_t* sv = lds[wave][1];
   const int F8 = d >> 3;
   const float inv8 = 1.0f / (float)F8;
-  const int bb = valid ? g.blockbase(b) : 0;
+  const int bb = g.blockbase(b);
 
   if (d < DP) {  // feature columns d .. DP-1 stay zero for every chunk
-    for (int e = lane; e < 2 * 64 * RS / 8; e += 64)
+    for (int e = tid; e < 64 * RS / 8; e += NTHR) {
       reinterpret_cast<u32x4_t*>(sk)[e] = u32x4_t{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4_t*>(sv)[e] = u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
-
-  f32x4_t acc[NT][NT], zacc[NT];
+  f32x4_t acc[NT], zacc[NT];
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    zacc[kt] = zero4();
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[kt][ct] = zero4();
-  }
+  for (int kt = 0; kt < NT; ++kt) acc[kt] = zacc[kt] = zero4();
   const u16x8_t ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
 
   for (int c0 = 0; c0 < g.nb; c0 += 64) {
-    // Stage tokens c0 .. c0+63 of the block: 16-byte chunk it = lane + 64u is
-    // chunk f of chunk-local token jl.  Rows past the block are zero.
-    u32x4_t kr[F8P], vr[F8P];
+    // chunk it = tid + NTHR u of the 64-token chunk: token jl = it / F8, chunk f
+    u32x4_t kr[UCH], vr[UCH];
+    int dst[UCH];
 #pragma unroll
-    for (int u = 0; u < F8P; ++u) {
-      const int it = lane + 64 * u;
+    for (int u = 0; u < UCH; ++u) {
+      const int it = tid + NTHR * u;
       const int jl = (int)(((float)it + 0.5f) * inv8);
       const int f = it - jl * F8;
       const int j = c0 + jl;
+      dst[u] = (it < 64 * F8) ? jl * RS + 8 * f : -1;
       kr[u] = vr[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (valid && u < F8 && j < g.nb) {
+      if (it < 64 * F8 && j < g.nb) {
         const size_t src = off + (size_t)(bb + g.tokoff(j)) * d + 8 * f;
         kr[u] = *reinterpret_cast<const u32x4_t*>(K + src);
         vr[u] = *reinterpret_cast<const u32x4_t*>(V + src);
       }
     }
-    lds_barrier();  // the previous chunk's reads are done
+    // the previous chunk's reads (or, for d < DP, the zero fill) are done
+    if (c0 > 0 || d < DP) lds_barrier();
 #pragma unroll
-    for (int u = 0; u < F8P; ++u) {
-      if (u < F8) {
-        const int it = lane + 64 * u;
-        const int jl = (int)(((float)it + 0.5f) * inv8);
-        const int f = it - jl * F8;
-        const bool real = valid && c0 + jl < g.nb;
-        *reinterpret_cast<u32x4_t*>(sk + jl * RS + 8 * f) =
-            real ? phi8<PHI>(kr[u]) : u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(sv + jl * RS + 8 * f) = vr[u];
+    for (int u = 0; u < UCH; ++u) {
+      if (dst[u] >= 0) {
+        const bool real = c0 + (int)(((float)(tid + NTHR * u) + 0.5f) * inv8) < g.nb;
+        *reinterpret_cast<u32x4_t*>(sk + dst[u]) = real ? phi8<PHI>(kr[u]) : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(sv + dst[u]) = vr[u];
       }
     }
     lds_barrier();
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      u16x8_t a[NT];
+      const u16x8_t bv = lds_tr8(sv, RS, 32 * st, 16 * ct, lane);
 #pragma unroll
-      for (int kt = 0; kt < NT; ++kt) a[kt] = lds_tr8(sk, RS, 32 * st, 16 * kt, lane);
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
-        const u16x8_t bv = lds_tr8(sv, RS, 32 * st, 16 * ct, lane);
-#pragma unroll
-        for (int kt = 0; kt < NT; ++kt) acc[kt][ct] = mfma_bf16(a[kt], bv, acc[kt][ct]);
+      for (int kt = 0; kt < NT; ++kt) {
+        const u16x8_t a = lds_tr8(sk, RS, 32 * st, 16 * kt, lane);
+        acc[kt] = mfma_bf16(a, bv, acc[kt]);
+        if (ct == 0) zacc[kt] = mfma_bf16(a, ones, zacc[kt]);
       }
-#pragma unroll
-      for (int kt = 0; kt < NT; ++kt) zacc[kt] = mfma_bf16(a[kt], ones, zacc[kt]);
     }
   }
-  if (!valid) return;  // no barrier follows
-  // acc[kt][ct] lane (s, grp) element r = S[16kt + 4grp + r][16ct + s]:
-  // four consecutive features of value column 16ct + s.
+  // acc[kt] lane (s, grp) element r = S[16kt + 4grp + r][16ct + s]: four
+  // consecutive features of value column 16ct + s.
+  const int s = lane & 15, grp = lane >> 4;
   bf16_t* row = S + ((size_t)slice * g.M + b) * EP;
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
+  for (int kt = 0; kt < NT; ++kt)
+    *reinterpret_cast<uint2*>(row + (16 * ct + s) * DP + 16 * kt + 4 * grp) =
+        make_uint2(pack2(acc[kt][0], acc[kt][1]), pack2(acc[kt][2], acc[kt][3]));
+  if (ct == 0 && s == 0) {
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
-      const f32x4_t v = acc[kt][ct];
-      *reinterpret_cast<uint2*>(row + (16 * ct + s) * DP + 16 * kt + 4 * grp) =
-          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-    }
-  if (s == 0) {
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
-      const f32x4_t v = zacc[kt];
+    for (int kt = 0; kt < NT; ++kt)
       *reinterpret_cast<uint2*>(row + DP * DP + 16 * kt + 4 * grp) =
-          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-    }
+          make_uint2(pack2(zacc[kt][0], zacc[kt][1]), pack2(zacc[kt][2], zacc[kt][3]));
   }
 }
 
@@ -304,36 +293,51 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
     az[ks] = s == 0 ? *reinterpret_cast<const u16x8_t*>(row + DP * DP + 32 * ks + 8 * grp)
                     : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   const int bb = g.blockbase(i);
-  for (int q0 = 0; q0 < g.nb; q0 += 16) {
-    const int j = q0 + s;
-    const int t = j < g.nb ? bb + g.tokoff(j) : -1;
-    u16x8_t bq[DS];
+  // Query tiles of 16, loaded QP tiles at a time before any of them is used,
+  // so that their transfers overlap.
+  constexpr int QP = 4;
+  for (int q0 = 0; q0 < g.nb; q0 += 16 * QP) {
+    int tq[QP];
+    u16x8_t bq[QP][DS];
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
-      const int k0 = 32 * ks + 8 * grp;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (t >= 0 && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)t * d + k0);
-      bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
+    for (int u = 0; u < QP; ++u) {
+      const int j = q0 + 16 * u + s;
+      tq[u] = j < g.nb ? bb + g.tokoff(j) : -1;
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) {
+        const int k0 = 32 * ks + 8 * grp;
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (tq[u] >= 0 && k0 < d)
+          v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)tq[u] * d + k0);
+        bq[u][ks] = __builtin_bit_cast(u16x8_t, v);
+      }
     }
-    f32x4_t o[NT], oz = zero4();
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      o[ct] = zero4();
+    for (int u = 0; u < QP; ++u) {
+      if (q0 + 16 * u >= g.nb) break;
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks) o[ct] = mfma_bf16(af[ct][ks], bq[ks], o[ct]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[ks], oz);
-    const float den = __shfl(oz[0], s);
-    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
-    if (t >= 0) {
-      bf16_t* yrow = Y + off + (size_t)t * d;
+      for (int ks = 0; ks < DS; ++ks)
+        bq[u][ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(__builtin_bit_cast(u32x4_t, bq[u][ks])));
+      f32x4_t o[NT], oz = zero4();
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        const int c = 16 * ct + 4 * grp;
-        if (c < d)
-          *reinterpret_cast<uint2*>(yrow + c) = make_uint2(pack2(o[ct][0] * rd, o[ct][1] * rd),
-                                                           pack2(o[ct][2] * rd, o[ct][3] * rd));
+        o[ct] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) o[ct] = mfma_bf16(af[ct][ks], bq[u][ks], o[ct]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
+      const float den = __shfl(oz[0], s);
+      const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+      if (tq[u] >= 0) {
+        bf16_t* yrow = Y + off + (size_t)tq[u] * d;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const int c = 16 * ct + 4 * grp;
+          if (c < d)
+            *reinterpret_cast<uint2*>(yrow + c) = make_uint2(pack2(o[ct][0] * rd, o[ct][1] * rd),
+                                                             pack2(o[ct][2] * rd, o[ct][3] * rd));
+        }
       }
     }
   }
@@ -375,7 +379,7 @@ int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_
   bf16_t* St = ws + (size_t)slices * g.M * D::EP;
   const unsigned nsl = (unsigned)slices;
   const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
-  k_summary_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, V, S, g, N, d);
+  k_summary_mfma<DP, PHI><<<dim3((unsigned)g.M, nsl), 64 * D::NT, 0, st>>>(K, V, S, g, N, d);
   const long xslices = (slices + 7) / 8 * 8;
   const int ib = mix_ib(g.M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((g.M + ib - 1) / ib));
