@@ -13,6 +13,16 @@ Two independent implementations live here:
   of the explicit token-pair matrix of §4.2 Eq. 5.
 * ``numpy_bruteforce`` (NumPy fp64): the same explicit matrix, built whole,
   for tiny inputs -- a second witness written without the C code.
+
+Both take the two options of the method: ``norm=False`` drops the denominator
+(the MHLA paper omits it for language modelling and very long video), and
+``causal=True`` is the chunkwise causal form of §4.2 ("Chunkwise parallel form
+of MHLA", App. C): blocks are consecutive chunks, query chunk i mixes the
+summaries of chunks b < i with W[i,b] and its own chunk's keys j <= q with
+W[i,i]; in the explicit matrix that is the mask A[q,j] = 0 for j > q.
+
+``np_lb_init`` is the locality-biased initial mixing matrix of §4.2
+(m0[i,j] proportional to 1 - dist(i,j) / max_k dist(i,k), rows summing to 1).
 """
 from __future__ import annotations
 
@@ -27,6 +37,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mhla_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_mhla.so")
 _lib = None
+
+NO_NORM = 1   # option bits of blockwise / rows
+CAUSAL = 2
 
 
 def build(force: bool = True) -> str:
@@ -45,10 +58,10 @@ def _configure(lib):
     lp = ctypes.POINTER(ctypes.c_long)
     lib.oracle_mhla_blockwise.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ip, ip,
-                                          ctypes.c_int, ctypes.c_int]
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_mhla_rows.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ip, ip, ctypes.c_int,
-                                     lp, ctypes.c_int]
+                                     ctypes.c_int, lp, ctypes.c_int]
     lib.oracle_block_of_token.argtypes = [ip, ip, ctypes.c_long]
     lib.oracle_num_blocks.argtypes = [ip, ip]
     lib.oracle_phi.argtypes = [ctypes.c_int, ctypes.c_double]
@@ -105,20 +118,26 @@ def block_of_token(grid, block, t: int) -> int:
     return int(_load().oracle_block_of_token(_g3(grid), _g3(block), int(t)))
 
 
-def blockwise(Q, K, V, W, grid, block, phi_kind: int, nthreads: int = 0) -> np.ndarray:
+def _flags(norm: bool, causal: bool) -> int:
+    return (0 if norm else NO_NORM) | (CAUSAL if causal else 0)
+
+
+def blockwise(Q, K, V, W, grid, block, phi_kind: int, nthreads: int = 0, norm: bool = True,
+              causal: bool = False) -> np.ndarray:
     """Q,K,V: [B,H,N,d]; W: [H,M,M].  Returns Y [B,H,N,d] fp64."""
     Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
     B, H, N, d = Q.shape
     Y = np.empty_like(Q)
     rc = _load().oracle_mhla_blockwise(_dptr(Q), _dptr(K), _dptr(V), _dptr(W), _dptr(Y),
                                        B, H, N, d, _g3(grid), _g3(block), int(phi_kind),
-                                       int(nthreads))
+                                       _flags(norm, causal), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_mhla_blockwise rejected the arguments")
     return Y
 
 
-def rows(Q, K, V, W, grid, block, phi_kind: int, flat_rows) -> np.ndarray:
+def rows(Q, K, V, W, grid, block, phi_kind: int, flat_rows, norm: bool = True,
+         causal: bool = False) -> np.ndarray:
     """Brute-force rows.  flat_rows[r] = (b*H + h)*N + q.  Returns [nrows, d]."""
     Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
     B, H, N, d = Q.shape
@@ -126,6 +145,7 @@ def rows(Q, K, V, W, grid, block, phi_kind: int, flat_rows) -> np.ndarray:
     out = np.empty((len(r), d), dtype=np.float64)
     rc = _load().oracle_mhla_rows(_dptr(Q), _dptr(K), _dptr(V), _dptr(W), _dptr(out),
                                   B, H, N, d, _g3(grid), _g3(block), int(phi_kind),
+                                  _flags(norm, causal),
                                   r.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), len(r))
     if rc != 0:
         raise ValueError("oracle_mhla_rows rejected the arguments")
@@ -151,22 +171,46 @@ def np_block_map(grid, block) -> np.ndarray:
     return np.ravel_multi_index(bc, tuple(gi // bi for gi, bi in zip(g, b)))
 
 
-def np_attention_matrix(q, k, w, grid, block, phi_kind) -> np.ndarray:
-    """Explicit A[q,j] = W[blk(q), blk(j)] * phi(q).phi(k_j) for one slice."""
+def np_attention_matrix(q, k, w, grid, block, phi_kind, causal=False) -> np.ndarray:
+    """Explicit A[q,j] = W[blk(q), blk(j)] * phi(q).phi(k_j) for one slice
+    (zero above the diagonal in the causal form)."""
     bm = np_block_map(grid, block)
     kern = np_phi(phi_kind, q) @ np_phi(phi_kind, k).T
-    return w[np.ix_(bm, bm)] * kern
+    A = w[np.ix_(bm, bm)] * kern
+    return np.tril(A) if causal else A
 
 
-def numpy_bruteforce(Q, K, V, W, grid, block, phi_kind) -> np.ndarray:
+def numpy_bruteforce(Q, K, V, W, grid, block, phi_kind, norm=True, causal=False) -> np.ndarray:
     Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
     B, H, N, d = Q.shape
     Y = np.zeros_like(Q)
     for b in range(B):
         for h in range(H):
-            A = np_attention_matrix(Q[b, h], K[b, h], W[h], grid, block, phi_kind)
-            den = A.sum(axis=1)
+            A = np_attention_matrix(Q[b, h], K[b, h], W[h], grid, block, phi_kind, causal)
             num = A @ V[b, h]
+            if not norm:
+                Y[b, h] = num
+                continue
+            den = A.sum(axis=1)
             safe = np.where(den == 0.0, 1.0, den)
             Y[b, h] = np.where((den == 0.0)[:, None], 0.0, num / safe[:, None])
     return Y
+
+
+def np_lb_init(grid, block) -> np.ndarray:
+    """Locality-biased initial mixing matrix [M, M] (MHLA paper §4.2): blocks sit
+    at their integer coordinates on the block grid (raster order, x fastest);
+    m0[i,j] is proportional to 1 - dist(i,j) / max_k dist(i,k) with dist the
+    Euclidean distance, and each row is scaled to sum to 1.  With one block the
+    matrix is [[1]]."""
+    g = (1,) * (3 - len(grid)) + tuple(grid)
+    b = (1,) * (3 - len(block)) + tuple(block)
+    shape = tuple(gi // bi for gi, bi in zip(g, b))
+    M = shape[0] * shape[1] * shape[2]
+    pos = np.stack(np.unravel_index(np.arange(M), shape), axis=1).astype(np.float64)
+    dist = np.sqrt(((pos[:, None, :] - pos[None, :, :]) ** 2).sum(-1))
+    far = dist.max(axis=1, keepdims=True)
+    if M == 1:
+        return np.ones((1, 1))
+    m = 1.0 - dist / far
+    return m / m.sum(axis=1, keepdims=True)

@@ -36,6 +36,19 @@
  *                             matrix A[q,j] = W[blk(q),blk(j)] phi(q).phi(k_j)
  *                             (the token-expanded form, §4.2 Eq. 5):
  *                             Y_q = sum_j A[q,j] V_j / sum_j A[q,j].
+ *
+ * Option bits (`flags`):
+ *   1  no normaliser: Y_q is the numerator alone (the MHLA paper drops the
+ *      denominator for language modelling and very long video; the blog
+ *      review §2.2 stresses that the switch is part of the method).
+ *   2  causal: the blocks must be consecutive runs of tokens (chunks, in
+ *      sequence order).  Query chunk i mixes only the summaries of earlier
+ *      chunks, S^<_i = sum_{b<i} W[i,b] S_b, and adds the causal part of its
+ *      own chunk weighted by W[i,i] (MHLA paper §4.2 "Chunkwise parallel form
+ *      of MHLA" and App. C; the appendix formula is garbled, so this is the
+ *      token form of Eq. 5 with the mask j <= q, split at the chunk border).
+ *      In brute force: A[q,j] = 0 for j > q.  Entries W[i,b] with b > i are
+ *      never used.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -81,10 +94,22 @@ double oracle_phi(int kind, double x) {
   return x > 0.0 ? x + 1.0 : exp(x);
 }
 
+enum { ORACLE_NO_NORM = 1, ORACLE_CAUSAL = 2 };
+
+/* Output row from numerator and denominator: divide (0 when the denominator is
+ * exactly 0), or the numerator alone when the normaliser is switched off. */
+static void finish_row(double* y, const double* num, double den, int d, int flags) {
+  if (flags & ORACLE_NO_NORM) {
+    for (int c = 0; c < d; ++c) y[c] = num[c];
+    return;
+  }
+  for (int c = 0; c < d; ++c) y[c] = den == 0.0 ? 0.0 : num[c] / den;
+}
+
 /* One (batch, head) slice: q,k,v,y point at [N,d]; w at [M,M]. */
 static void blockwise_slice(const double* q, const double* k, const double* v,
                             const double* w, double* y, int N, int d, int M,
-                            const int* blk, int phi) {
+                            const int* blk, int phi, int flags) {
   size_t dd = (size_t)d * d;
   double* S = (double*)calloc((size_t)M * dd, sizeof(double));
   double* z = (double*)calloc((size_t)M * d, sizeof(double));
@@ -103,11 +128,13 @@ static void blockwise_slice(const double* q, const double* k, const double* v,
       for (int c = 0; c < d; ++c) Sb[(size_t)a * d + c] += pk[a] * v[(size_t)t * d + c];
     }
   }
-  /* Steps 2 and 3 per query block i: mix, then read out its queries. */
+  /* Steps 2 and 3 per query block i: mix, then read out its queries.  In the
+   * causal form only the earlier chunks b < i are mixed here. */
+  const int causal = (flags & ORACLE_CAUSAL) != 0;
   for (int i = 0; i < M; ++i) {
     memset(St, 0, dd * sizeof(double));
     memset(zt, 0, (size_t)d * sizeof(double));
-    for (int b = 0; b < M; ++b) {
+    for (int b = 0; b < (causal ? i : M); ++b) {
       double m = w[(size_t)i * M + b];
       const double* Sb = S + (size_t)b * dd;
       for (size_t e = 0; e < dd; ++e) St[e] += m * Sb[e];
@@ -122,19 +149,41 @@ static void blockwise_slice(const double* q, const double* k, const double* v,
         den += pq * zt[a];
         for (int c = 0; c < d; ++c) num[c] += pq * St[(size_t)a * d + c];
       }
-      for (int c = 0; c < d; ++c) y[(size_t)t * d + c] = den == 0.0 ? 0.0 : num[c] / den;
+      if (causal) {
+        /* own chunk: keys t2 <= t of block i, weight W[i,i] */
+        double mii = w[(size_t)i * M + i];
+        for (int t2 = 0; t2 <= t; ++t2) {
+          if (blk[t2] != i) continue;
+          double dot = 0.0;
+          for (int a = 0; a < d; ++a)
+            dot += oracle_phi(phi, q[(size_t)t * d + a]) * oracle_phi(phi, k[(size_t)t2 * d + a]);
+          den += mii * dot;
+          for (int c = 0; c < d; ++c) num[c] += mii * dot * v[(size_t)t2 * d + c];
+        }
+      }
+      finish_row(y + (size_t)t * d, num, den, d, flags);
     }
   }
   free(S); free(z); free(St); free(zt); free(pk); free(num);
+}
+
+/* Causal form needs every block to be one run of consecutive tokens, in block
+ * order: block b = tokens [b*nb, (b+1)*nb). */
+static int chunks_contiguous(const int* blk, int N, int M) {
+  int nb = N / M;
+  for (int t = 0; t < N; ++t)
+    if (blk[t] != t / nb) return 0;
+  return 1;
 }
 
 /* Q,K,V,Y: [B,H,N,d] fp64 row-major.  W: [H,M,M] fp64.  Returns 0, or -1 on a
  * bad shape.  nthreads <= 0 means all available threads. */
 int oracle_mhla_blockwise(const double* Q, const double* K, const double* V,
                           const double* W, double* Y, int B, int H, int N, int d,
-                          const int grid[3], const int block[3], int phi,
+                          const int grid[3], const int block[3], int phi, int flags,
                           int nthreads) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || (phi != 0 && phi != 1)) return -1;
+  if (flags & ~(ORACLE_NO_NORM | ORACLE_CAUSAL)) return -1;
   if (!geom_ok(N, grid, block)) return -1;
   int M = oracle_num_blocks(grid, block);
   int* blk = (int*)malloc((size_t)N * sizeof(int));
@@ -142,6 +191,7 @@ int oracle_mhla_blockwise(const double* Q, const double* K, const double* V,
     blk[t] = oracle_block_of_token(grid, block, t);
     if (blk[t] < 0 || blk[t] >= M) { free(blk); return -1; }
   }
+  if ((flags & ORACLE_CAUSAL) && !chunks_contiguous(blk, N, M)) { free(blk); return -1; }
   long nslices = (long)B * H;
   size_t sl = (size_t)N * d;
 #ifdef _OPENMP
@@ -151,7 +201,7 @@ int oracle_mhla_blockwise(const double* Q, const double* K, const double* V,
   for (long s = 0; s < nslices; ++s) {
     int h = (int)(s % H);
     blockwise_slice(Q + s * sl, K + s * sl, V + s * sl, W + (size_t)h * M * M,
-                    Y + s * sl, N, d, M, blk, phi);
+                    Y + s * sl, N, d, M, blk, phi, flags);
   }
   (void)nthreads;
   free(blk);
@@ -162,11 +212,15 @@ int oracle_mhla_blockwise(const double* Q, const double* K, const double* V,
  * b*H + h.  Yrows: [nrows, d].  Returns 0 or -1. */
 int oracle_mhla_rows(const double* Q, const double* K, const double* V,
                      const double* W, double* Yrows, int B, int H, int N, int d,
-                     const int grid[3], const int block[3], int phi,
+                     const int grid[3], const int block[3], int phi, int flags,
                      const long* rows, int nrows) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || (phi != 0 && phi != 1)) return -1;
+  if (flags & ~(ORACLE_NO_NORM | ORACLE_CAUSAL)) return -1;
   if (!geom_ok(N, grid, block)) return -1;
   int M = oracle_num_blocks(grid, block);
+  /* the causal mask is on token order; it is the chunkwise form only when the
+   * blocks are consecutive runs, which the caller checks with blockwise */
+  const int jmax_causal = (flags & ORACLE_CAUSAL) != 0;
   size_t sl = (size_t)N * d;
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 1)
@@ -184,7 +238,7 @@ int oracle_mhla_rows(const double* Q, const double* K, const double* V,
     double* out = Yrows + (size_t)r * d;
     double den = 0.0;
     for (int c = 0; c < d; ++c) out[c] = 0.0;
-    for (int j = 0; j < N; ++j) {
+    for (int j = 0; j < (jmax_causal ? qi + 1 : N); ++j) {
       double dot = 0.0;
       for (int a = 0; a < d; ++a)
         dot += oracle_phi(phi, q[a]) * oracle_phi(phi, k[(size_t)j * d + a]);
@@ -194,7 +248,8 @@ int oracle_mhla_rows(const double* Q, const double* K, const double* V,
       den += A;
       for (int c = 0; c < d; ++c) out[c] += A * v[(size_t)j * d + c];
     }
-    for (int c = 0; c < d; ++c) out[c] = den == 0.0 ? 0.0 : out[c] / den;
+    if (!(flags & ORACLE_NO_NORM))
+      for (int c = 0; c < d; ++c) out[c] = den == 0.0 ? 0.0 : out[c] / den;
   }
   return 0;
 }

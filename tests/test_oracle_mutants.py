@@ -36,8 +36,18 @@ MUTANTS = {
                       "z[(size_t)b * d + a] += k[(size_t)t * d + a];"),
     "query_phi_dropped": ("double pq = oracle_phi(phi, q[(size_t)t * d + a]);",
                           "double pq = q[(size_t)t * d + a];"),
-    "mix_skips_last_block": ("for (int b = 0; b < M; ++b) {\n      double m",
-                             "for (int b = 0; b < M - 1; ++b) {\n      double m"),
+    "mix_skips_last_block": ("for (int b = 0; b < (causal ? i : M); ++b) {",
+                             "for (int b = 0; b < (causal ? i : M - 1); ++b) {"),
+    # options: normaliser switch and the chunkwise causal form
+    "nonorm_ignored": ("  if (flags & ORACLE_NO_NORM) {\n    for (int c = 0; c < d; ++c) y[c] = num[c];",
+                       "  if (0) {\n    for (int c = 0; c < d; ++c) y[c] = num[c];"),
+    "causal_prefix_includes_own": ("b < (causal ? i : M)", "b < (causal ? i + 1 : M)"),
+    "causal_own_chunk_strict": ("for (int t2 = 0; t2 <= t; ++t2)", "for (int t2 = 0; t2 < t; ++t2)"),
+    "causal_own_chunk_unweighted": ("double mii = w[(size_t)i * M + i];", "double mii = 1.0;"),
+    "causal_own_chunk_wrong_weight": ("double mii = w[(size_t)i * M + i];",
+                                      "double mii = w[(size_t)(i > 0 ? i - 1 : 0) * M + i];"),
+    "rows_causal_strict": ("(jmax_causal ? qi + 1 : N)", "(jmax_causal ? qi : N)"),
+    "rows_nonorm_ignored": ("    if (!(flags & ORACLE_NO_NORM))\n      for", "    if (1)\n      for"),
 }
 
 
@@ -76,6 +86,32 @@ def _pins_hold_inner() -> bool:
             Yb = oracle.blockwise(Q, K, V, W, grid, block, phi)
             ok &= bool(np.allclose(Yb, oracle.numpy_bruteforce(Q, K, V, W, grid, block, phi),
                                    rtol=1e-10, atol=1e-10))
+    # the options: hand-derived numerators and the chunkwise causal example
+    g = json.load(open(os.path.join(GOLDEN, "worked_relu_2x2.json")))
+    arr = lambda k: np.array(g[k], dtype=np.float64)[None, None]
+    args = (arr("Q"), arr("K"), arr("V"), np.array(g["W"])[None], g["grid"], g["block"], g["phi"])
+    num = np.array(g["numerator"])
+    ok &= bool(np.allclose(oracle.blockwise(*args, norm=False)[0, 0], num, rtol=0, atol=1e-12))
+    ok &= bool(np.allclose(oracle.rows(*args, np.arange(4), norm=False), num, rtol=0, atol=1e-12))
+    g = json.load(open(os.path.join(GOLDEN, "worked_causal_relu_1x4.json")))
+    args = (arr("Q"), arr("K"), arr("V"), np.array(g["W"])[None], g["grid"], g["block"], g["phi"])
+    num, den = np.array(g["numerator"]), np.array(g["denominator"])[:, None]
+    for norm, exp in ((True, num / den), (False, num)):
+        ok &= bool(np.allclose(oracle.blockwise(*args, norm=norm, causal=True)[0, 0], exp,
+                               rtol=0, atol=1e-12))
+        ok &= bool(np.allclose(oracle.rows(*args, np.arange(4), norm=norm, causal=True), exp,
+                               rtol=0, atol=1e-12))
+    for grid, block in [((1, 1, 24), (1, 1, 6)), ((2, 3, 4), (1, 3, 4))]:
+        N, M = int(np.prod(grid)), oracle.num_blocks(grid, block)
+        Q, K, V = (rng.standard_normal((1, 2, N, 4)) for _ in range(3))
+        W = rng.uniform(0.2, 1.0, (2, M, M))
+        for norm in (True, False):
+            ref = oracle.numpy_bruteforce(Q, K, V, W, grid, block, PHI_ELU1, norm=norm, causal=True)
+            Yb = oracle.blockwise(Q, K, V, W, grid, block, PHI_ELU1, norm=norm, causal=True)
+            Yr = oracle.rows(Q, K, V, W, grid, block, PHI_ELU1, np.arange(2 * N), norm=norm,
+                             causal=True).reshape(ref.shape)
+            ok &= bool(np.allclose(Yb, ref, rtol=1e-10, atol=1e-10))
+            ok &= bool(np.allclose(Yr, ref, rtol=1e-10, atol=1e-10))
     # softmax reduction with one token per block
     q, k, v = (rng.standard_normal((12, 4)) for _ in range(3))
     pq, pk = oracle.np_phi(PHI_ELU1, q), oracle.np_phi(PHI_ELU1, k)
