@@ -89,10 +89,13 @@ def main():
             "blocked": m.MHLA_PATH_BLOCKED}[args.path]
     shape = (wl.grid, wl.block)
     if path == m.MHLA_PATH_AUTO:
-        path = m.mhla_plan(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi, wl.dtype)
+        path = m.mhla_plan_ex(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi,
+                              wl.dtype, wl.flags)
     path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked"}[path]
     kernels = {1: ["k_summary_valu", "k_mix_valu", "k_readout_valu"], 2: ["k_fused"],
                3: ["k_pairs"], 4: ["k_summary_mfma", "k_mix_mfma", "k_readout_mfma"]}[path]
+    if wl.causal:
+        kernels = ["k_summary_mfma", "k_mix_mfma", "k_readout_causal"]
 
     inp = make_inputs(wl)
 
@@ -108,7 +111,7 @@ def main():
     stream = torch.cuda.current_stream()  # the stream the library launches on
 
     def step():
-        m.mhla_forward_path(q, k, v, w, out, shape, wl.phi, path, stream=stream)
+        m.mhla_forward_ex(q, k, v, w, out, shape, wl.phi, wl.flags, path, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -162,9 +165,10 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, row-softmax W; stand-in for the pages' image and "
                 "video workloads)",
         "config": {
-            "workload": "%s: B%d H%d N%d (%s grid, %s blocks, M=%d) d%d phi=%s" % (
+            "workload": "%s: B%d H%d N%d (%s grid, %s blocks, M=%d) d%d phi=%s%s%s" % (
                 wl.name, wl.B, wl.H, wl.N, "x".join(map(str, wl.grid)),
-                "x".join(map(str, wl.block)), wl.M, wl.d, "relu" if wl.phi == 0 else "elu+1"),
+                "x".join(map(str, wl.block)), wl.M, wl.d, "relu" if wl.phi == 0 else "elu+1",
+                " causal" if wl.causal else "", "" if wl.norm else " no-norm"),
             "path": path_name,
             "parallelism": "single GPU",
         },
@@ -215,13 +219,15 @@ def cpu_baseline(inp, out_dev, target_s):
     threads = oracle.threads()
     # size the sample (whole batch items, all heads) for about target_s seconds
     t0 = time.perf_counter()
-    oracle.blockwise(q[:1, :1], k[:1, :1], v[:1, :1], w[:1], wl.grid, wl.block, wl.phi)
+    oracle.blockwise(q[:1, :1], k[:1, :1], v[:1, :1], w[:1], wl.grid, wl.block, wl.phi,
+                     norm=wl.norm, causal=wl.causal)
     per_slice = max(time.perf_counter() - t0, 1e-6)
     n_b = max(1, min(wl.B, int(target_s * threads / per_slice / wl.H)))
     reps, elapsed, ref = 0, 0.0, None
     while True:
         t0 = time.perf_counter()
-        ref = oracle.blockwise(q[:n_b], k[:n_b], v[:n_b], w, wl.grid, wl.block, wl.phi)
+        ref = oracle.blockwise(q[:n_b], k[:n_b], v[:n_b], w, wl.grid, wl.block, wl.phi,
+                               norm=wl.norm, causal=wl.causal)
         elapsed += time.perf_counter() - t0
         reps += 1
         if elapsed >= 0.8 * target_s or reps >= 2000:

@@ -73,6 +73,26 @@ enum {
   MHLA_PATH_BLOCKED = 4     /* summary, mixing GEMM, readout on bf16 MFMA     */
 };
 
+/* Option bits for mhla_forward_ex (any combination). */
+enum {
+  /* Y_q = phi(Q_q) S~_i: the denominator is dropped.  The MHLA paper runs its
+   * language-modelling and very long video models this way (blog review
+   * §2.2: the normaliser switch is part of the method). */
+  MHLA_FLAG_NO_NORM = 1,
+  /* Chunkwise causal form (MHLA paper §4.2 "Chunkwise parallel form of MHLA",
+   * App. C).  Every block must be a run of consecutive tokens (for a grid:
+   * full rows of the x axis, or full frames), so blocks are chunks in
+   * sequence order.  Query chunk i mixes only earlier chunks,
+   *   S^<_i = sum_{b<i} W[h][i][b] S_b,  z^<_i likewise,
+   * and adds its own chunk causally with weight W[h][i][i]:
+   *   Y_q = (phi(Q_q) S^<_i + W_ii sum_{j<=q in chunk i} (phi(Q_q).phi(K_j)) V_j)
+   *       / (phi(Q_q).z^<_i + W_ii sum_{j<=q in chunk i}  phi(Q_q).phi(K_j)),
+   * i.e. the token form of Eq. 5 with the mask j <= q.  Entries W[h][i][b]
+   * with b > i are ignored.  Supported for bf16, d a multiple of 8 up to 96,
+   * chunks of at most 256 tokens (MHLA_PATH_BLOCKED). */
+  MHLA_FLAG_CAUSAL = 2
+};
+
 /* Forward pass (MHLA paper §4.1).  Returns MHLA_OK or an MHLA_ERR_* code. */
 int mhla_forward(const void* Q, const void* K, const void* V, const float* Wmix,
                  void* out, int B, int H, int N, int d,
@@ -85,6 +105,32 @@ int mhla_forward_path(const void* Q, const void* K, const void* V,
                       const float* Wmix, void* out, int B, int H, int N, int d,
                       const mhla_block_shape* block_shape, int phi_kind,
                       int dtype, int path, void* stream);
+
+/* mhla_forward_path with option bits (MHLA_FLAG_*; 0 = mhla_forward_path).
+ * Unknown bits return MHLA_ERR_INVALID_ARG; a causal call whose blocks are not
+ * runs of consecutive tokens returns MHLA_ERR_SHAPE; a path that cannot run
+ * the options returns MHLA_ERR_UNSUPPORTED.  Nothing is enqueued on error. */
+int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wmix,
+                    void* out, int B, int H, int N, int d,
+                    const mhla_block_shape* block_shape, int phi_kind, int dtype,
+                    int flags, int path, void* stream);
+
+/* The path MHLA_PATH_AUTO picks for these sizes and option bits (host only),
+ * or -code for the error mhla_forward_ex would return before any launch. */
+int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape,
+                 int phi_kind, int dtype, int flags);
+
+/* Locality-biased initial mixing matrix m0 of the MHLA paper (§4.2; Fig. 4b
+ * shows it): blocks sit at their integer coordinates (bz, by, bx) on the
+ * block grid, dist is the Euclidean distance between those coordinates, and
+ * m0[i][j] = (1 - dist(i,j) / max_k dist(i,k)) / (sum over j of the same),
+ * so every row sums to 1, the block itself has the largest weight and the
+ * farthest block gets 0.  With one block, m0 = [[1]].  Host-only: writes
+ * M*M floats row-major into the caller's host buffer W (M = number of blocks;
+ * replicate it per head for Wmix).  Returns MHLA_OK, MHLA_ERR_SHAPE for an
+ * invalid block shape, or MHLA_ERR_INVALID_ARG when W is NULL or `capacity`
+ * (in floats) is below M*M. */
+int mhla_lb_init(const mhla_block_shape* block_shape, float* W, size_t capacity);
 
 /* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
  * would return for these sizes. */

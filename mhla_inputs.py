@@ -14,6 +14,9 @@ no dataset or trained weight is involved):
   dit_xl2   bf16  B32 H16 N256   (16x16 grid, 4x4 blocks, M=16)    d72 relu
   hires     bf16  B4  H16 N4096  (64x64 grid, 8x8 blocks, M=64)    d64 relu
   video     bf16  B1  H24 N32768 (8x64x64 grid, 1x8x8 blocks, M=512) d64 elu+1
+  lm_causal bf16  B16 H16 N2048  (1-D, chunks of 64, M=32)         d64 elu+1,
+            chunkwise causal form without the normaliser (§5.4: context 2048,
+            M = 32; the paper drops the denominator for language modelling)
 
 Draw order per workload (numpy PCG64, seed = 20260 + index): Q, K, V as
 standard normal fp32 [B,H,N,d] in C order, then the coefficient logits [H,M,M]
@@ -31,6 +34,8 @@ PHI_RELU = 0
 PHI_ELU1 = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+FLAG_NO_NORM = 1   # option bits, the values of the C ABI's MHLA_FLAG_*
+FLAG_CAUSAL = 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -45,6 +50,19 @@ class Workload:
     phi: int
     dtype: int
     diag_boost: float = 0.0
+    flags: int = 0
+
+    @property
+    def norm(self) -> bool:
+        return not (self.flags & FLAG_NO_NORM)
+
+    @property
+    def causal(self) -> bool:
+        return bool(self.flags & FLAG_CAUSAL)
+
+    @property
+    def nb(self) -> int:
+        return self.block[0] * self.block[1] * self.block[2]
 
     @property
     def N(self) -> int:
@@ -77,8 +95,13 @@ class Workload:
         return qkvy + self.H * self.M * self.M * 4
 
     def algorithmic_flops(self) -> int:
-        """B*H*(4*N*d^2 + 2*M^2*d^2): summaries + readout + mixing."""
+        """B*H*(4*N*d^2 + 2*M^2*d^2): summaries + readout + mixing.  The causal
+        form mixes only the lower triangle (M^2 d^2) and adds its own chunk's
+        masked token pairs (two products over nb^2/2 pairs: 2*N*nb*d)."""
         d2 = self.d * self.d
+        if self.causal:
+            return self.B * self.H * (4 * self.N * d2 + self.M * self.M * d2
+                                      + 2 * self.N * self.nb * self.d)
         return self.B * self.H * (4 * self.N * d2 + 2 * self.M * self.M * d2)
 
 
@@ -90,6 +113,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("dit_xl2", 2, 32, 16, 72, (1, 16, 16), (1, 4, 4), PHI_RELU, DTYPE_BF16),
         Workload("hires", 3, 4, 16, 64, (1, 64, 64), (1, 8, 8), PHI_RELU, DTYPE_BF16),
         Workload("video", 4, 1, 24, 64, (8, 64, 64), (1, 8, 8), PHI_ELU1, DTYPE_BF16),
+        Workload("lm_causal", 5, 16, 16, 64, (1, 1, 2048), (1, 1, 64), PHI_ELU1, DTYPE_BF16,
+                 flags=FLAG_NO_NORM | FLAG_CAUSAL),
     ]
 }
 
@@ -166,9 +191,9 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, B: Optional[int] = Non
 
 
 def custom_workload(B: int, H: int, d: int, grid, block, phi: int, dtype: int,
-                    name: str = "custom", index: int = 100) -> Workload:
+                    name: str = "custom", index: int = 100, flags: int = 0) -> Workload:
     g = tuple(int(x) for x in grid)
     b = tuple(int(x) for x in block)
     g = (1,) * (3 - len(g)) + g
     b = (1,) * (3 - len(b)) + b
-    return Workload(name, index, B, H, d, g, b, phi, dtype)
+    return Workload(name, index, B, H, d, g, b, phi, dtype, flags=flags)

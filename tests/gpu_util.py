@@ -26,8 +26,12 @@ def run(inp: Inputs, path=m.MHLA_PATH_AUTO, dev=None, stream=None, skip_unsuppor
     q, k, v, w = dev if dev is not None else to_device(inp)
     out = torch.empty_like(q)
     try:
-        m.mhla_forward_path(q, k, v, w, out, (inp.wl.grid, inp.wl.block), inp.wl.phi, path,
-                            stream=stream)
+        if inp.wl.flags:
+            m.mhla_forward_ex(q, k, v, w, out, (inp.wl.grid, inp.wl.block), inp.wl.phi,
+                              inp.wl.flags, path, stream=stream)
+        else:
+            m.mhla_forward_path(q, k, v, w, out, (inp.wl.grid, inp.wl.block), inp.wl.phi, path,
+                                stream=stream)
     except m.MhlaError as e:
         if skip_unsupported and e.code == m.MHLA_ERR_UNSUPPORTED:
             import pytest

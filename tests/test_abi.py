@@ -126,3 +126,90 @@ def test_forward_rejects_alias_and_misalignment_before_any_launch():
     rc = lib.mhla_forward_path(q, k, v, w, base + 5 * sz, 1, 1, 64, 16, ctypes.byref(bs), 0, 0,
                                m.MHLA_PATH_FUSED, None)
     assert rc == m.MHLA_ERR_UNSUPPORTED   # fused path is bf16-only
+
+
+# ---------------------------------------------------------------- option bits
+
+def _plan_ex(wl_name=None, flags=0, **kw):
+    if wl_name:
+        wl = WORKLOADS[wl_name]
+        kw = dict(dict(B=wl.B, H=wl.H, N=wl.N, d=wl.d, grid=wl.grid, block=wl.block, phi=wl.phi,
+                       dtype=wl.dtype), **kw)
+    return m.mhla_plan_ex(kw["B"], kw["H"], kw["N"], kw["d"],
+                          m.BlockShape.make(kw["grid"], kw["block"]), kw["phi"], kw["dtype"],
+                          flags)
+
+
+def test_plan_ex_paths():
+    C, NN = m.MHLA_FLAG_CAUSAL, m.MHLA_FLAG_NO_NORM
+    assert _plan_ex("lm_causal", C | NN) == m.MHLA_PATH_BLOCKED
+    assert _plan_ex("lm_causal", C) == m.MHLA_PATH_BLOCKED
+    # the normaliser switch keeps every path
+    assert _plan_ex("deit_t", NN) == m.MHLA_PATH_FUSED
+    assert _plan_ex("dit_xl2", NN) == m.MHLA_PATH_PAIRS
+    assert _plan_ex("video", NN) == m.MHLA_PATH_BLOCKED
+    assert _plan_ex("tiny", NN) == m.MHLA_PATH_GENERIC
+    assert _plan_ex("tiny", 0) == m.mhla_plan(1, 1, 64, 16, m.BlockShape.make((1, 8, 8), (1, 4, 4)),
+                                              0, 0)
+
+
+def test_plan_ex_rejects():
+    C = m.MHLA_FLAG_CAUSAL
+    # unknown option bits
+    assert _plan_ex("deit_t", 4) == -m.MHLA_ERR_INVALID_ARG
+    # 7x7 tiles of a 14x14 grid are not runs of consecutive tokens
+    assert _plan_ex("deit_t", C) == -m.MHLA_ERR_SHAPE
+    assert "consecutive" in m.mhla_last_error()
+    # whole-row and whole-frame blocks are runs
+    assert _plan_ex("deit_t", C, grid=(1, 14, 14), block=(1, 2, 14)) == m.MHLA_PATH_BLOCKED
+    assert _plan_ex("video", C, grid=(8, 64, 64), block=(1, 64, 64)) == -m.MHLA_ERR_UNSUPPORTED
+    assert _plan_ex("video", C, grid=(8, 16, 16), block=(1, 16, 16), N=2048) == m.MHLA_PATH_BLOCKED
+    # fp32 has no causal kernel; chunks above 256 tokens neither
+    assert _plan_ex("tiny", C, grid=(1, 1, 64), block=(1, 1, 16)) == -m.MHLA_ERR_UNSUPPORTED
+    assert _plan_ex("lm_causal", C, block=(1, 1, 512)) == -m.MHLA_ERR_UNSUPPORTED
+
+
+def test_forward_ex_rejects_before_any_launch():
+    lib = m.load_library()
+    bs = m.BlockShape.make((1, 8, 8), (1, 4, 4))
+    buf = (ctypes.c_char * (64 * 16 * 2 * 8 + 64))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    sz = 64 * 16 * 2
+    args = (base, base + sz, base + 2 * sz, base + 3 * sz, base + 5 * sz, 1, 1, 64, 16,
+            ctypes.byref(bs), 0, 1)
+    assert lib.mhla_forward_ex(*args, 8, 0, None) == m.MHLA_ERR_INVALID_ARG
+    assert lib.mhla_forward_ex(*args, m.MHLA_FLAG_CAUSAL, 0, None) == m.MHLA_ERR_SHAPE
+    assert lib.mhla_forward_ex(*args, m.MHLA_FLAG_NO_NORM, 7, None) == m.MHLA_ERR_INVALID_ARG
+    bs1 = m.BlockShape.make((1, 1, 64), (1, 1, 16))
+    args1 = args[:9] + (ctypes.byref(bs1), 0, 1)
+    assert lib.mhla_forward_ex(*args1, m.MHLA_FLAG_CAUSAL, m.MHLA_PATH_FUSED,
+                               None) == m.MHLA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- LB-init
+
+@pytest.mark.parametrize("grid,block", [((1, 1, 3), (1, 1, 1)), ((1, 4, 4), (1, 2, 2)),
+                                        ((1, 14, 14), (1, 7, 7)), ((1, 16, 16), (1, 4, 4)),
+                                        ((8, 64, 64), (1, 8, 8)), ((1, 6, 10), (1, 3, 5)),
+                                        ((1, 8, 8), (1, 8, 8)), ((2, 3, 4), (1, 1, 1))])
+def test_lb_init_matches_oracle(grid, block):
+    """The library's host helper against the oracle's m0 (MHLA paper §4.2):
+    the same double-precision value rounded once to fp32."""
+    import numpy as np
+    import oracle
+    got = m.mhla_lb_init((grid, block)).astype(np.float64)
+    ref = oracle.np_lb_init(grid, block)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=2.0 ** -23, atol=1e-30)
+    assert np.all(got[ref == 0.0] == 0.0)
+
+
+def test_lb_init_rejects():
+    lib = m.load_library()
+    bs = m.BlockShape.make((1, 4, 4), (1, 2, 2))
+    buf = (ctypes.c_float * 16)()
+    assert lib.mhla_lb_init(ctypes.byref(bs), buf, 15) == m.MHLA_ERR_INVALID_ARG
+    assert lib.mhla_lb_init(ctypes.byref(bs), None, 16) == m.MHLA_ERR_INVALID_ARG
+    assert lib.mhla_lb_init(ctypes.byref(bs), buf, 16) == m.MHLA_OK
+    bad = m.BlockShape.make((1, 4, 4), (1, 3, 2))
+    assert lib.mhla_lb_init(ctypes.byref(bad), buf, 16) == m.MHLA_ERR_SHAPE

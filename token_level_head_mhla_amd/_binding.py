@@ -15,10 +15,12 @@ MHLA_DTYPE_F32, MHLA_DTYPE_BF16 = 0, 1
 (MHLA_OK, MHLA_ERR_INVALID_ARG, MHLA_ERR_SHAPE, MHLA_ERR_UNSUPPORTED, MHLA_ERR_HIP,
  MHLA_ERR_ALIAS) = range(6)
 MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_BLOCKED = range(5)
+MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL = 1, 2
 
 EXPORTED_SYMBOLS = (
-    "mhla_forward", "mhla_forward_path", "mhla_validate", "mhla_plan", "mhla_num_blocks",
-    "mhla_workspace_bytes", "mhla_error_string", "mhla_last_error", "mhla_release",
+    "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_validate", "mhla_plan",
+    "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
+    "mhla_error_string", "mhla_last_error", "mhla_release",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,12 @@ def load_library():
     lib.mhla_forward.restype = ip
     lib.mhla_forward_path.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, vp]
     lib.mhla_forward_path.restype = ip
+    lib.mhla_forward_ex.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, ip, vp]
+    lib.mhla_forward_ex.restype = ip
+    lib.mhla_plan_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
+    lib.mhla_plan_ex.restype = ip
+    lib.mhla_lb_init.argtypes = [bsp, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t]
+    lib.mhla_lb_init.restype = ip
     lib.mhla_validate.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
     lib.mhla_validate.restype = ip
     lib.mhla_plan.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
@@ -108,6 +116,27 @@ def mhla_validate(B, H, N, d, block_shape, phi_kind, dtype) -> int:
 def mhla_plan(B, H, N, d, block_shape, phi_kind, dtype) -> int:
     return int(load_library().mhla_plan(B, H, N, d, ctypes.byref(_shape(block_shape)), phi_kind,
                                         dtype))
+
+
+def mhla_plan_ex(B, H, N, d, block_shape, phi_kind, dtype, flags) -> int:
+    return int(load_library().mhla_plan_ex(B, H, N, d, ctypes.byref(_shape(block_shape)),
+                                           phi_kind, dtype, flags))
+
+
+def mhla_lb_init(block_shape):
+    """The locality-biased initial mixing matrix [M, M] as a float32 numpy array
+    (host-only call; replicate it per head for Wmix)."""
+    import numpy as np
+    bs = _shape(block_shape)
+    M = mhla_num_blocks(int(np.prod(list(bs.grid))), bs)
+    if M < 0:
+        raise MhlaError(-M, mhla_last_error())
+    out = np.empty((M, M), dtype=np.float32)
+    rc = load_library().mhla_lb_init(ctypes.byref(bs),
+                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), M * M)
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return out
 
 
 def mhla_num_blocks(N, block_shape) -> int:
@@ -164,6 +193,21 @@ def mhla_forward_path(Q, K, V, Wmix, out, block_shape, phi_kind, path, stream=No
     rc = load_library().mhla_forward_path(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
         ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(path), _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return out
+
+
+def mhla_forward_ex(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHLA_PATH_AUTO,
+                    stream=None):
+    """Enqueue the forward with option bits (MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL)."""
+    _check_tensors(Q, K, V, Wmix, out)
+    B, H, N, d = Q.shape
+    bs = _shape(block_shape)
+    rc = load_library().mhla_forward_ex(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
+        ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(flags), int(path),
+        _stream_ptr(stream))
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())
     return out

@@ -148,11 +148,14 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 // blocks are walked in steps of 32: the next step's S and W tiles are loaded
 // into registers while the current step's tiles (double-buffered in LDS) feed
 // the MFMAs, so there is one barrier per step.
+//
+// causal != 0 mixes only earlier chunks (W[i,b] is taken as 0 for b >= i):
+// the prefix mixture of the chunkwise causal form.
 template <int EP, int IB>
 __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
                                                           const float* __restrict__ W,
                                                           bf16_t* __restrict__ St, int M, int H,
-                                                          long nslices) {
+                                                          long nslices, int causal) {
   constexpr int EB = kMixEB, KB = kMixKB;
   constexpr int EW = IB == 64 ? 32 : 64, IW = 64;
   constexpr int AT = EW / 16, BT = IW / 16;        // MFMA tiles per wave along e and i
@@ -208,6 +211,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
         v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bc);                   \
       } else {                                                                            \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M) v[q] = Wh[(size_t)i * M + bc + q]; \
+      }                                                                                   \
+      if (causal) {                                                                       \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q >= i) v[q] = 0.0f;       \
       }                                                                                   \
     }                                                                                     \
     wr[u] = v;                                                                            \
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
       const float den = __shfl(oz[0], s);
-      const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+      const float rd = out_scale(g, den);
       if (tq[u] >= 0) {
         bf16_t* yrow = Y + off + (size_t)tq[u] * d;
 #pragma unroll
@@ -370,24 +376,34 @@ inline size_t blocked_workspace(long slices, int M, int d) {
   return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
 }
 
+// Summary and mixing launches shared by the plain and the causal readout; with
+// causal != 0 the mixing keeps only earlier chunks.  Returns S~ in the workspace.
 template <int DP, int PHI>
-int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
-                     const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
-                     hipStream_t st) {
+bf16_t* launch_summary_mix(long slices, int H, int N, int d, const Geo& g, const bf16_t* K,
+                           const bf16_t* V, const float* W, bf16_t* ws, int causal,
+                           hipStream_t st) {
   using D = BlockedDims<DP>;
   bf16_t* S = ws;
   bf16_t* St = ws + (size_t)slices * g.M * D::EP;
-  const unsigned nsl = (unsigned)slices;
-  const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
-  k_summary_mfma<DP, PHI><<<dim3((unsigned)g.M, nsl), 64 * D::NT, 0, st>>>(K, V, S, g, N, d);
+  k_summary_mfma<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), 64 * D::NT, 0, st>>>(
+      K, V, S, g, N, d);
   const long xslices = (slices + 7) / 8 * 8;
   const int ib = mix_ib(g.M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((g.M + ib - 1) / ib));
   if (ib == 64)
-    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices);
+    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices, causal);
   else
-    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices);
-  k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
+    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices, causal);
+  return St;
+}
+
+template <int DP, int PHI>
+int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                     const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
+                     hipStream_t st) {
+  const bf16_t* St = launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, ws, 0, st);
+  const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
+  k_readout_mfma<DP, PHI><<<dim3(nbw, (unsigned)slices), kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
   return 0;
 }
 

@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * fused_waves(MM)) void k_fused(
     for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
     // row 0 of the z~ tile (lane s of group 0, element 0) is phi(q).z~_i
     const float den = __shfl(oz[0], s);
-    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+    const float rd = out_scale(g, den);
     if (tok[u] >= 0) {
       bf16_t* yrow = Y + off + (size_t)tok[u] * d;
 #pragma unroll

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kValuThreads) void k_readout_valu(
           for (int k = 0; k < d; ++k) acc = fmaf(sq[j][k], ss[k][cc], acc);
           const float den = sden[j];
           const long t = g.token(i, j0 + j);
-          Elt<T>::store(Yb + t * d + c0 + cc, den == 0.0f ? 0.0f : acc / den);
+          Elt<T>::store(Yb + t * d + c0 + cc, !g.norm ? acc : den == 0.0f ? 0.0f : acc / den);
         }
       }
     }

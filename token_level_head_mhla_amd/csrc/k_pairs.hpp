@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
     for (int c = 0; c < CT; ++c)
       if (c == dct) dv = o[u][c][dr];
     const float den = __shfl(dv, 16 * dg + s);
-    const float rd = den == 0.0f ? 0.0f : 1.0f / den;
+    const float rd = out_scale(g, den);
     if (qtok[u] >= 0) {
       bf16_t* yrow = Y + off + (size_t)qtok[u] * d;
 #pragma unroll

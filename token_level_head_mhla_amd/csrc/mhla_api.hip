@@ -6,6 +6,7 @@
 // mixing, readout); the entry points are declared and documented in mhla.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -20,6 +21,7 @@
 #include "k_fused.hpp"
 #include "k_blocked.hpp"
 #include "k_pairs.hpp"
+#include "k_causal.hpp"
 
 namespace mhla {
 namespace {
@@ -38,6 +40,8 @@ int fail(int code, const char* fmt, ...) {
 
 struct Problem {
   int B, H, N, d, phi, dtype;
+  int flags = 0;
+  bool causal() const { return (flags & MHLA_FLAG_CAUSAL) != 0; }
   Geo g;
   long slices() const { return (long)B * H; }
   size_t elt() const { return dtype == MHLA_DTYPE_F32 ? 4 : 2; }
@@ -84,6 +88,7 @@ int check(int B, int H, int N, int d, const mhla_block_shape* s, int phi, int dt
     g.nb = g.bt * g.bh * g.bw;
     g.inv_bw = 1.0f / (float)g.bw;
     g.inv_bhw = 1.0f / (float)(g.bh * g.bw);
+    g.norm = 1;
     p->B = B; p->H = H; p->N = N; p->d = d; p->phi = phi; p->dtype = dtype;
     if (g.nb >= (1 << 22))
       return fail(MHLA_ERR_UNSUPPORTED, "blocks of %d tokens are too large (limit 2^22)", g.nb);
@@ -93,7 +98,24 @@ int check(int B, int H, int N, int d, const mhla_block_shape* s, int phi, int dt
   return MHLA_OK;
 }
 
+// Option bits: reject unknown ones and causal calls whose blocks are not runs
+// of consecutive tokens.
+int check_flags(int flags, Problem* p) {
+  if (flags & ~(MHLA_FLAG_NO_NORM | MHLA_FLAG_CAUSAL))
+    return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", flags);
+  p->flags = flags;
+  p->g.norm = (flags & MHLA_FLAG_NO_NORM) ? 0 : 1;
+  if (p->causal() && !blocks_contiguous(p->g))
+    return fail(MHLA_ERR_SHAPE,
+                "the causal form needs blocks that are runs of consecutive tokens (block "
+                "%dx%dx%d in grid %dx%dx%d is not)",
+                p->g.bt, p->g.bh, p->g.bw, p->g.T, p->g.Hg, p->g.Wg);
+  return MHLA_OK;
+}
+
 bool path_supports(int path, const Problem& p) {
+  if (p.causal())
+    return path == MHLA_PATH_BLOCKED && causal_supports(p.dtype, p.d, p.g, p.slices());
   switch (path) {
     case MHLA_PATH_GENERIC: return p.slices() <= 65535;  // slices run along grid y/z
     case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
@@ -104,6 +126,8 @@ bool path_supports(int path, const Problem& p) {
 }
 
 int choose_path(const Problem& p) {
+  if (p.causal())
+    return path_supports(MHLA_PATH_BLOCKED, p) ? MHLA_PATH_BLOCKED : -MHLA_ERR_UNSUPPORTED;
   if (path_supports(MHLA_PATH_FUSED, p)) return MHLA_PATH_FUSED;
   if (path_supports(MHLA_PATH_PAIRS, p)) return MHLA_PATH_PAIRS;
   if (path_supports(MHLA_PATH_BLOCKED, p)) return MHLA_PATH_BLOCKED;
@@ -180,10 +204,12 @@ int launch_generic(const Problem& p, const T* Q, const T* K, const T* V, const f
 }
 
 int run(const void* Q, const void* K, const void* V, const float* W, void* out, int B, int H,
-        int N, int d, const mhla_block_shape* shape, int phi, int dtype, int path,
+        int N, int d, const mhla_block_shape* shape, int phi, int dtype, int flags, int path,
         void* stream) {
   Problem p;
   int rc = check(B, H, N, d, shape, phi, dtype, &p);
+  if (rc != MHLA_OK) return rc;
+  rc = check_flags(flags, &p);
   if (rc != MHLA_OK) return rc;
   if (!Q || !K || !V || !W || !out)
     return fail(MHLA_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -198,7 +224,7 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
     return fail(MHLA_ERR_ALIAS, "out overlaps Wmix");
   if (path == MHLA_PATH_AUTO) path = choose_path(p);
   if (path < 0 || !path_supports(path, p))
-    return fail(MHLA_ERR_UNSUPPORTED, "path %d does not support this shape/dtype", path);
+    return fail(MHLA_ERR_UNSUPPORTED, "path %d does not support this shape/dtype/options", path);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
@@ -219,11 +245,14 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
   } else if (path == MHLA_PATH_PAIRS) {
     rc = launch_pairs(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
                       (const bf16_t*)V, W, (bf16_t*)out, st);
+  } else if (path == MHLA_PATH_BLOCKED && p.causal()) {
+    rc = launch_causal(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, W, (bf16_t*)out, (bf16_t*)ws, st);
   } else if (path == MHLA_PATH_BLOCKED) {
     rc = launch_blocked(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q,
                         (const bf16_t*)K, (const bf16_t*)V, W, (bf16_t*)out, (bf16_t*)ws, st);
   }
-  if (rc != MHLA_OK) return rc;
+  if (rc != MHLA_OK) return fail(MHLA_ERR_HIP, "kernel set-up failed (hipFuncSetAttribute)");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MHLA_OK;
@@ -239,7 +268,7 @@ extern "C" {
 int mhla_forward(const void* Q, const void* K, const void* V, const float* Wmix, void* out,
                  int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
                  int dtype, void* stream) {
-  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, MHLA_PATH_AUTO,
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, 0, MHLA_PATH_AUTO,
              stream);
 }
 
@@ -249,7 +278,81 @@ int mhla_forward_path(const void* Q, const void* K, const void* V, const float* 
                       void* stream) {
   if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
-  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, path, stream);
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, 0, path, stream);
+}
+
+int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wmix, void* out,
+                    int B, int H, int N, int d, const mhla_block_shape* block_shape,
+                    int phi_kind, int dtype, int flags, int path, void* stream) {
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, flags, path, stream);
+}
+
+int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
+                 int dtype, int flags) {
+  Problem p;
+  int rc = check(B, H, N, d, block_shape, phi_kind, dtype, &p);
+  if (rc != MHLA_OK) return -rc;
+  rc = check_flags(flags, &p);
+  if (rc != MHLA_OK) return -rc;
+  return choose_path(p);
+}
+
+int mhla_lb_init(const mhla_block_shape* block_shape, float* W, size_t capacity) {
+  Problem p;
+  if (block_shape == nullptr) return fail(MHLA_ERR_INVALID_ARG, "block_shape is NULL");
+  const long n = (long)block_shape->grid[0] * block_shape->grid[1] * block_shape->grid[2];
+  if (n <= 0 || n > 0x7fffffffL)
+    return fail(MHLA_ERR_SHAPE, "grid %dx%dx%d is empty or too large", block_shape->grid[0],
+                block_shape->grid[1], block_shape->grid[2]);
+  int rc = check(1, 1, (int)n, 8, block_shape, MHLA_PHI_RELU, MHLA_DTYPE_F32, &p);
+  if (rc != MHLA_OK) return rc;
+  const Geo& g = p.g;
+  const size_t M = (size_t)g.M;
+  if (W == nullptr || capacity < M * M)
+    return fail(MHLA_ERR_INVALID_ARG, "W needs room for %zu floats (M=%zu)", M * M, M);
+  if (M == 1) {
+    W[0] = 1.0f;
+    return MHLA_OK;
+  }
+  // block coordinates in raster order of the block grid (x fastest)
+  auto coord = [&](size_t b, double* c) {
+    const size_t nyx = (size_t)g.nby * g.nbx;
+    c[0] = (double)(b / nyx);
+    c[1] = (double)((b % nyx) / g.nbx);
+    c[2] = (double)(b % g.nbx);
+  };
+  for (size_t i = 0; i < M; ++i) {
+    double ci[3];
+    coord(i, ci);
+    // the farthest block from i is a corner of the block grid
+    double far = 0.0;
+    for (int corner = 0; corner < 8; ++corner) {
+      const double cz = (corner & 4) ? g.nbz - 1 : 0, cy = (corner & 2) ? g.nby - 1 : 0,
+                   cx = (corner & 1) ? g.nbx - 1 : 0;
+      far = std::fmax(far, std::sqrt((ci[0] - cz) * (ci[0] - cz) + (ci[1] - cy) * (ci[1] - cy) +
+                                     (ci[2] - cx) * (ci[2] - cx)));
+    }
+    double sum = 0.0;
+    for (size_t j = 0; j < M; ++j) {
+      double cj[3];
+      coord(j, cj);
+      const double dist = std::sqrt((ci[0] - cj[0]) * (ci[0] - cj[0]) +
+                                    (ci[1] - cj[1]) * (ci[1] - cj[1]) +
+                                    (ci[2] - cj[2]) * (ci[2] - cj[2]));
+      sum += 1.0 - dist / far;
+    }
+    for (size_t j = 0; j < M; ++j) {
+      double cj[3];
+      coord(j, cj);
+      const double dist = std::sqrt((ci[0] - cj[0]) * (ci[0] - cj[0]) +
+                                    (ci[1] - cj[1]) * (ci[1] - cj[1]) +
+                                    (ci[2] - cj[2]) * (ci[2] - cj[2]));
+      W[i * M + j] = (float)((1.0 - dist / far) / sum);
+    }
+  }
+  return MHLA_OK;
 }
 
 int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,

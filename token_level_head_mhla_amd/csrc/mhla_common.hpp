@@ -21,6 +21,9 @@ struct Geo {
   int M;                // number of blocks
   int nb;               // tokens per block
   float inv_bw, inv_bhw;  // 1/bw and 1/(bh*bw), for exact small-integer division
+  int norm;             // 1: divide by the denominator; 0: numerator only (the
+                        // normaliser switch of the MHLA paper, used for language
+                        // modelling and very long video)
 
   // Token index of member j (raster order inside the tile) of block b.
   __host__ __device__ __forceinline__ int token(int b, int j) const {
@@ -47,6 +50,12 @@ struct Geo {
 };
 
 enum { PHI_RELU = 0, PHI_ELU1 = 1 };
+
+// Factor applied to a numerator row: 1/den, 0 for a zero denominator (a
+// ReLU query whose features are all zero), or 1 with the normaliser off.
+__device__ __forceinline__ float out_scale(const Geo& g, float den) {
+  return g.norm ? (den == 0.0f ? 0.0f : 1.0f / den) : 1.0f;
+}
 
 // Feature maps named in the attention-variants tutorial (linear attention
 // section): ReLU, and elu(x)+1 with alpha = 1.
