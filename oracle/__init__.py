@@ -23,6 +23,11 @@ W[i,i]; in the explicit matrix that is the mask A[q,j] = 0 for j > q.
 
 ``np_lb_init`` is the locality-biased initial mixing matrix of §4.2
 (m0[i,j] proportional to 1 - dist(i,j) / max_k dist(i,k), rows summing to 1).
+
+``np_backward`` gives the gradients of the (non-causal) forward for an upstream
+gradient G = dL/dY.  The pages print no backward pass; it is the chain rule
+applied to the three forward steps of §4.1, written out step by step in
+reverse order (readout, mixing, summaries).
 """
 from __future__ import annotations
 
@@ -214,3 +219,74 @@ def np_lb_init(grid, block) -> np.ndarray:
         return np.ones((1, 1))
     m = 1.0 - dist / far
     return m / m.sum(axis=1, keepdims=True)
+
+
+def np_dphi(kind: int, x: np.ndarray) -> np.ndarray:
+    """Derivative of the feature map: ReLU' = 1 for x > 0 else 0; (elu+1)' =
+    1 for x > 0 else exp(x)."""
+    if kind == 0:
+        return (x > 0.0).astype(np.float64)
+    return np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True):
+    """Gradients (dQ, dK, dV, dW) of L = sum(G * Y) for the non-causal forward.
+
+    Forward, per (batch, head) slice, with phi applied to Q and K:
+      S_b = phi(K_b)^T V_b, z_b = phi(K_b)^T 1         (summaries)
+      S~_i = sum_b W[i,b] S_b, z~_i = sum_b W[i,b] z_b (mixing)
+      n_q = phi(q) S~_i, den_q = phi(q).z~_i, Y_q = n_q / den_q  (readout)
+    Reverse, step by step:
+      readout:   dn_q = G_q / den_q, dden_q = -(G_q . Y_q) / den_q
+                 (without the normaliser: dn_q = G_q, dden_q = 0; a zero
+                 denominator gives a zero row and zero gradients)
+                 dphi(q) = S~_i dn_q + z~_i dden_q
+                 dS~_i = sum_{q in i} phi(q) dn_q^T, dz~_i = sum_{q in i} phi(q) dden_q
+      mixing:    dS_b = sum_i W[i,b] dS~_i, dz_b = sum_i W[i,b] dz~_i
+                 dW[i,b] += <dS~_i, S_b> + dz~_i . z_b   (W is shared over the batch)
+      summaries: dphi(k_j) = dS_b v_j + dz_b, dV_j = dS_b^T phi(k_j)
+      feature map: dQ = dphi(Q) * phi'(Q), dK = dphi(K) * phi'(K).
+    """
+    Q, K, V, W, G = _f64(Q), _f64(K), _f64(V), _f64(W), _f64(G)
+    B, H, N, d = Q.shape
+    bm = np_block_map(grid, block)
+    M = int(bm.max()) + 1
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    dW = np.zeros_like(W)
+    for b in range(B):
+        for h in range(H):
+            pq, pk = np_phi(phi_kind, Q[b, h]), np_phi(phi_kind, K[b, h])
+            v, g, w = V[b, h], G[b, h], W[h]
+            S = np.zeros((M, d, d))
+            z = np.zeros((M, d))
+            for blk in range(M):
+                sel = bm == blk
+                S[blk] = pk[sel].T @ v[sel]
+                z[blk] = pk[sel].sum(axis=0)
+            St = np.einsum("ib,bfc->ifc", w, S)
+            zt = w @ z
+            n = np.einsum("qf,qfc->qc", pq, St[bm])
+            den = np.einsum("qf,qf->q", pq, zt[bm])
+            if norm:
+                rd = np.where(den == 0.0, 0.0, 1.0 / np.where(den == 0.0, 1.0, den))
+                y = n * rd[:, None]
+                dn = g * rd[:, None]
+                dden = -(g * y).sum(axis=1) * rd
+            else:
+                dn = g
+                dden = np.zeros(N)
+            dpq = np.einsum("qfc,qc->qf", St[bm], dn) + zt[bm] * dden[:, None]
+            dSt = np.zeros((M, d, d))
+            dzt = np.zeros((M, d))
+            for i in range(M):
+                sel = bm == i
+                dSt[i] = pq[sel].T @ dn[sel]
+                dzt[i] = pq[sel].T @ dden[sel]
+            dS = np.einsum("ib,ifc->bfc", w, dSt)
+            dz = w.T @ dzt
+            dW[h] += np.einsum("ifc,bfc->ib", dSt, S) + dzt @ z.T
+            dpk = np.einsum("jfc,jc->jf", dS[bm], v) + dz[bm]
+            dV[b, h] = np.einsum("jfc,jf->jc", dS[bm], pk)
+            dQ[b, h] = dpq * np_dphi(phi_kind, Q[b, h])
+            dK[b, h] = dpk * np_dphi(phi_kind, K[b, h])
+    return dQ, dK, dV, dW
