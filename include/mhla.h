@@ -132,6 +132,23 @@ int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape
  * (in floats) is below M*M. */
 int mhla_lb_init(const mhla_block_shape* block_shape, float* W, size_t capacity);
 
+/* Backward pass of the non-causal forward: given dY = dL/dY, writes dQ, dK,
+ * dV ([B, H, N, d], dtype) and dWmix ([H, M, M] fp32, summed over the batch,
+ * overwritten).  The pages print no backward; it is the chain rule through
+ * the three forward steps of the MHLA paper §4.1 (readout, mixing,
+ * summaries, in reverse order), with phi'(x) = [x > 0] for ReLU and 1 or
+ * exp(x) for elu+1.  A row whose denominator is exactly 0 is the constant 0
+ * and passes no gradient.  flags may hold MHLA_FLAG_NO_NORM; the causal form
+ * has no backward here (MHLA_ERR_UNSUPPORTED).  Supported: bf16, d a multiple
+ * of 8 up to 96.  All pointers are device pointers with the conventions
+ * above; the outputs must not overlap any input or each other
+ * (MHLA_ERR_ALIAS).  Uses the library's workspace (4 [B,H,M,d*d+d] bf16
+ * tables plus per-token and per-slice scratch). */
+int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix,
+                  const void* dY, void* dQ, void* dK, void* dV, float* dWmix,
+                  int B, int H, int N, int d, const mhla_block_shape* block_shape,
+                  int phi_kind, int dtype, int flags, void* stream);
+
 /* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
  * would return for these sizes. */
 int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape,

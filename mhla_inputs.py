@@ -190,6 +190,18 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, B: Optional[int] = Non
     return Inputs(dataclasses.replace(wl, B=B, H=H), q, k, v, w)
 
 
+def make_upstream_grad(wl: Workload, B: Optional[int] = None, H: Optional[int] = None,
+                       seed: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient G = dL/dY for the backward pass: standard normal of the
+    output's shape, drawn from its own stream (PCG64, seed = workload seed +
+    50000), rounded to bf16 bits for bf16 workloads (fp32 otherwise)."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 50000))
+    g = rng.standard_normal((B, H, wl.N, wl.d), dtype=np.float32)
+    return bf16_round_bits(g) if wl.dtype == DTYPE_BF16 else g
+
+
 def custom_workload(B: int, H: int, d: int, grid, block, phi: int, dtype: int,
                     name: str = "custom", index: int = 100, flags: int = 0) -> Workload:
     g = tuple(int(x) for x in grid)

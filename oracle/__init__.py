@@ -229,8 +229,11 @@ def np_dphi(kind: int, x: np.ndarray) -> np.ndarray:
     return np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True):
+def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True, dw_abs=False):
     """Gradients (dQ, dK, dV, dW) of L = sum(G * Y) for the non-causal forward.
+    With dw_abs=True a fifth array is returned: the sum of the absolute values
+    of the products that make up each dW entry (the scale of the error bound
+    of that dot product when it is evaluated in finite precision).
 
     Forward, per (batch, head) slice, with phi applied to Q and K:
       S_b = phi(K_b)^T V_b, z_b = phi(K_b)^T 1         (summaries)
@@ -253,6 +256,7 @@ def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True):
     M = int(bm.max()) + 1
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
     dW = np.zeros_like(W)
+    dWabs = np.zeros_like(W)
     for b in range(B):
         for h in range(H):
             pq, pk = np_phi(phi_kind, Q[b, h]), np_phi(phi_kind, K[b, h])
@@ -285,8 +289,11 @@ def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True):
             dS = np.einsum("ib,ifc->bfc", w, dSt)
             dz = w.T @ dzt
             dW[h] += np.einsum("ifc,bfc->ib", dSt, S) + dzt @ z.T
+            dWabs[h] += np.einsum("ifc,bfc->ib", np.abs(dSt), np.abs(S)) + np.abs(dzt) @ np.abs(z).T
             dpk = np.einsum("jfc,jc->jf", dS[bm], v) + dz[bm]
             dV[b, h] = np.einsum("jfc,jf->jc", dS[bm], pk)
             dQ[b, h] = dpq * np_dphi(phi_kind, Q[b, h])
             dK[b, h] = dpk * np_dphi(phi_kind, K[b, h])
+    if dw_abs:
+        return dQ, dK, dV, dW, dWabs
     return dQ, dK, dV, dW

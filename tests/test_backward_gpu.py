@@ -1,0 +1,102 @@
+"""GPU parity of the backward pass (mhla_backward through the C ABI) against
+the fp64 oracle's gradients (chain rule through the three forward steps of
+the MHLA paper §4.1; the oracle is pinned by finite differences and autograd).
+
+Gate: 1e-2 for bf16, per gradient: max over (batch, head) slices of
+max|g - g_oracle| / max|g_oracle| for dQ, dK, dV.  dW is a dot product over
+all d*d + d state entries (and the batch) of bf16-rounded factors, whose
+error is bounded relative to the sum of the absolute products, not to the
+result (with the normaliser a row of dW sums to zero against W, and for
+M = 1 it is exactly 0); its gate is max|dW - dW_oracle| per head over the
+largest such absolute sum of that head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_level_head_mhla_amd as m
+from mhla_inputs import (DTYPE_BF16, FLAG_CAUSAL, FLAG_NO_NORM, PHI_ELU1, PHI_RELU, WORKLOADS,
+                         bf16_bits_to_f32, custom_workload, make_inputs, make_upstream_grad)
+from gpu_util import TOL, slice_error, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _run_backward(inp, gbits, flags=0):
+    q, k, v, w = to_device(inp)
+    dy = _bf16_dev(gbits)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dw = torch.empty_like(w)
+    m.mhla_backward(q, k, v, w, dy, dq, dk, dv, dw, (inp.wl.grid, inp.wl.block), inp.wl.phi,
+                    flags)
+    torch.cuda.synchronize()
+    return to_f64(dq), to_f64(dk), to_f64(dv), dw.cpu().numpy().astype(np.float64)
+
+
+def _head_error(a, ref, scale):
+    num = np.abs(a - ref).reshape(a.shape[0], -1).max(axis=1)
+    den = np.abs(scale).reshape(scale.shape[0], -1).max(axis=1)
+    return float((num / np.where(den == 0, 1.0, den)).max())
+
+
+def _check(wl, flags=0, label=""):
+    inp = make_inputs(wl)
+    gbits = make_upstream_grad(wl)
+    got = _run_backward(inp, gbits, flags)
+    G = bf16_bits_to_f32(gbits).astype(np.float64)
+    ref = oracle.np_backward(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, G, wl.grid, wl.block,
+                             wl.phi, norm=not (flags & FLAG_NO_NORM), dw_abs=True)
+    errs = [slice_error(got[i], ref[i]) for i in range(3)] + [_head_error(got[3], ref[3], ref[4])]
+    print("PARITY backward %s %s %s d=%d phi=%d M=%d flags=%d errs dQ %.2e dK %.2e dV %.2e dW %.2e"
+          % (label, wl.grid, wl.block, wl.d, wl.phi, wl.M, flags, *errs))
+    for g in got:
+        assert np.all(np.isfinite(g))
+    for e in errs:
+        assert e <= TOL[DTYPE_BF16]
+
+
+BACKWARD_CASES = [
+    # (B, H, grid, block, d, phi)
+    (2, 3, (1, 14, 14), (1, 7, 7), 64, PHI_ELU1),    # DeiT-like, ragged 49-token blocks
+    (2, 2, (1, 16, 16), (1, 4, 4), 72, PHI_RELU),    # DiT-like, d = 72 padded to 96
+    (1, 2, (1, 32, 32), (1, 8, 8), 64, PHI_RELU),    # M = 16
+    (2, 2, (1, 40, 52), (1, 4, 4), 32, PHI_ELU1),    # M = 130: partial dW tiles
+    (2, 2, (1, 8, 8), (1, 8, 8), 16, PHI_ELU1),      # M = 1, d = 16 padded to 32
+    (2, 3, (4, 8, 8), (2, 4, 4), 48, PHI_RELU),      # 3-D blocks, d = 48
+    (1, 2, (1, 16, 16), (1, 16, 8), 96, PHI_ELU1),   # 128-token blocks, d = 96
+]
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("B,H,grid,block,d,phi", BACKWARD_CASES)
+def test_backward_shapes(B, H, grid, block, d, phi, norm):
+    wl = custom_workload(B, H, d, grid, block, phi, DTYPE_BF16, index=hash((grid, d)) % 953)
+    _check(wl, 0 if norm else FLAG_NO_NORM)
+
+
+@pytest.mark.parametrize("name,B,H", [("deit_t", 8, 3), ("dit_xl2", 4, 16), ("hires", 1, 4)])
+def test_backward_workload_shapes(name, B, H):
+    """The workloads' geometry and d with a reduced batch (the oracle's
+    gradient materialises per-token states)."""
+    wl = WORKLOADS[name]
+    import dataclasses
+    _check(dataclasses.replace(wl, B=B, H=H), 0, name)
+
+
+def test_backward_rejects():
+    wl = custom_workload(1, 1, 64, (1, 1, 128), (1, 1, 32), PHI_ELU1, DTYPE_BF16, index=2)
+    inp = make_inputs(wl)
+    with pytest.raises(m.MhlaError) as e:
+        _run_backward(inp, make_upstream_grad(wl), FLAG_CAUSAL)
+    assert e.value.code == m.MHLA_ERR_UNSUPPORTED
+    q, k, v, w = to_device(inp)
+    dy = _bf16_dev(make_upstream_grad(wl))
+    with pytest.raises(m.MhlaError) as e:   # dQ aliases K
+        m.mhla_backward(q, k, v, w, dy, k, torch.empty_like(k), torch.empty_like(v),
+                        torch.empty_like(w), (wl.grid, wl.block), wl.phi)
+    assert e.value.code == m.MHLA_ERR_ALIAS

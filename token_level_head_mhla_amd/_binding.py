@@ -18,7 +18,8 @@ MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_B
 MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL = 1, 2
 
 EXPORTED_SYMBOLS = (
-    "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_validate", "mhla_plan",
+    "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward", "mhla_validate",
+    "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
     "mhla_error_string", "mhla_last_error", "mhla_release",
 )
@@ -71,6 +72,9 @@ def load_library():
     lib.mhla_forward_path.restype = ip
     lib.mhla_forward_ex.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, ip, vp]
     lib.mhla_forward_ex.restype = ip
+    lib.mhla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip,
+                                  ip, vp]
+    lib.mhla_backward.restype = ip
     lib.mhla_plan_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
     lib.mhla_plan_ex.restype = ip
     lib.mhla_lb_init.argtypes = [bsp, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t]
@@ -211,6 +215,22 @@ def mhla_forward_ex(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHL
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())
     return out
+
+
+def mhla_backward(Q, K, V, Wmix, dY, dQ, dK, dV, dWmix, block_shape, phi_kind, flags=0,
+                  stream=None):
+    """Enqueue the backward pass: writes dQ, dK, dV (like Q) and dWmix (like Wmix)."""
+    _check_tensors(Q, K, V, Wmix, dY)
+    _check_tensors(dQ, dK, dV, dWmix, dY)
+    B, H, N, d = Q.shape
+    bs = _shape(block_shape)
+    rc = load_library().mhla_backward(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), dY.data_ptr(), dQ.data_ptr(),
+        dK.data_ptr(), dV.data_ptr(), dWmix.data_ptr(), B, H, N, d, ctypes.byref(bs),
+        int(phi_kind), _dtype_code(Q), int(flags), _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return dQ, dK, dV, dWmix
 
 
 def mhla_forward(Q, K, V, Wmix, out, block_shape, phi_kind, stream=None):

@@ -1,0 +1,376 @@
+// k_backward.hpp -- backward pass of the (non-causal) MHLA forward, bf16 in
+// and out, fp32 dW, gfx950 MFMA.  The pages print no backward; this is the
+// chain rule through the three forward steps of "MHLA: Restoring
+// Expressivity of Linear Attention via Token-Level Multi-Head" §4.1, taken in
+// reverse order.  With phi applied to Q and K and G = dL/dY:
+//
+//   readout   dn_q = G_q / den_q, dden_q = -(G_q . Y_q) / den_q
+//             (normaliser off: dn_q = G_q, dden_q = 0; den_q = 0: both 0)
+//             dphi(q) = S~_i dn_q + z~_i dden_q
+//             dS~_i = sum_{q in i} phi(q) dn_q^T,  dz~_i = sum_{q in i} dden_q phi(q)
+//   mixing    dS_b = sum_i W[i,b] dS~_i (and dz_b);
+//             dW[i,b] = sum over the batch of <dS~_i, S_b> + dz~_i . z_b
+//   summaries dphi(k_j) = dS_b v_j + dz_b,  dV_j = dS_b^T phi(k_j)
+//   phi       dQ = dphi(Q) * phi'(Q),  dK = dphi(K) * phi'(K)
+//
+// Treating z as one more value column ([S | z], [V | 1], [dn | dden]) makes
+// every step one of the forward's building blocks:
+//   1. S, S~          summary kernel and mixing GEMM, as in the forward
+//   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
+//   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
+//   4. dS, dz         mixing GEMM with W transposed
+//   5. dW             k_dw_partial (per slice, the rows of dS~ against the rows
+//                     of S over all d*d + d entries) and k_dw_reduce (sum
+//                     over the batch, fixed order: deterministic)
+//   6. dQ             k_bwd_dphi: S~ staged in LDS and read transposed,
+//                     times G (exact bf16) on MFMA, scaled by 1/den per token
+//                     in fp32, plus z~ dden in fp32, times phi'(Q)
+//   7. dK             k_bwd_dphi with dS and V, plus dz, times phi'(K)
+//   8. dV             the readout kernel with K for Q, dS for S~ and no
+//                     normaliser: dV^T = dS^T phi(K)^T.
+#pragma once
+
+#include "k_blocked.hpp"
+
+namespace mhla {
+
+template <int PHI>
+__device__ __forceinline__ float dphi_apply(float x) {
+  if constexpr (PHI == PHI_RELU) return x > 0.0f ? 1.0f : 0.0f;
+  return x > 0.0f ? 1.0f : __expf(x);
+}
+
+// ---------------------------------------------------------------------------
+// Step 2.  grid = (ceil(M / 4), slices), block = 256: wave w handles query
+// block 4*blockIdx.x + w, 16 queries per step, exactly like the readout
+// (Y^T tiles and the z~ row for the denominator), then forms dn and dden.
+// Writes dN [slices, N, d] bf16, and dden and the per-token factor rq (1/den,
+// or 1 with the normaliser off) as [slices, N] fp32.
+template <int DP, int PHI>
+__global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ St, const bf16_t* __restrict__ G,
+    bf16_t* __restrict__ dN, float* __restrict__ dden, float* __restrict__ rq, Geo g, int N,
+    int d) {
+  using D = BlockedDims<DP>;
+  constexpr int NT = D::NT, DS = D::DS, EP = D::EP;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.y;
+  const int i = blockIdx.x * kBlkWaves + wave;
+  if (i >= g.M) return;  // no barrier in this kernel
+  const size_t off = (size_t)slice * N * d;
+  const bf16_t* row = St + ((size_t)slice * g.M + i) * EP;
+  u16x8_t af[NT][DS], az[DS];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks)
+      af[ct][ks] = *reinterpret_cast<const u16x8_t*>(row + (16 * ct + s) * DP + 32 * ks + 8 * grp);
+#pragma unroll
+  for (int ks = 0; ks < DS; ++ks)
+    az[ks] = s == 0 ? *reinterpret_cast<const u16x8_t*>(row + DP * DP + 32 * ks + 8 * grp)
+                    : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  const int bb = g.blockbase(i);
+  for (int q0 = 0; q0 < g.nb; q0 += 16) {
+    const int j = q0 + s;
+    const int tq = j < g.nb ? bb + g.tokoff(j) : -1;
+    u16x8_t bq[DS];
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const int k0 = 32 * ks + 8 * grp;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (tq >= 0 && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)tq * d + k0);
+      bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
+    }
+    f32x4_t o[NT], oz = zero4();
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      o[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) o[ct] = mfma_bf16(af[ct][ks], bq[ks], o[ct]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[ks], oz);
+    const float rd = out_scale(g, __shfl(oz[0], s));
+    // G^T in the accumulator layout: lane (s, grp) holds G[q0+s][16ct+4grp .. +3]
+    float gv[NT][4];
+    float dot = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int c = 16 * ct + 4 * grp;
+      uint2 u = make_uint2(0u, 0u);
+      if (tq >= 0 && c < d) u = *reinterpret_cast<const uint2*>(G + off + (size_t)tq * d + c);
+      gv[ct][0] = lo_f32(u.x); gv[ct][1] = hi_f32(u.x);
+      gv[ct][2] = lo_f32(u.y); gv[ct][3] = hi_f32(u.y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dot += gv[ct][r] * (o[ct][r] * rd);
+    }
+    // sum over the four lanes of query s (groups 0..3)
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float scale = g.norm ? rd : 1.0f;
+    if (tq >= 0) {
+      bf16_t* nrow = dN + off + (size_t)tq * d;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int c = 16 * ct + 4 * grp;
+        if (c < d)
+          *reinterpret_cast<uint2*>(nrow + c) =
+              make_uint2(pack2(gv[ct][0] * scale, gv[ct][1] * scale),
+                         pack2(gv[ct][2] * scale, gv[ct][3] * scale));
+      }
+      if (grp == 0) {
+        dden[(size_t)slice * N + tq] = g.norm ? -dot * rd : 0.0f;
+        rq[(size_t)slice * N + tq] = scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 6 and 7.  dphi(x_t)[f] = us_t sum_c T_blk[f][c] u_t[c] + t_blk[f] e_t,
+// where
+//   T, t = S~, z~ (query blocks), u = G, us = 1/den, e = dden   for dQ, and
+//   T, t = dS, dz (key blocks),   u = V, us = 1,     e = 1      for dK,
+// then dX = dphi * phi'(X).  grid = (M, slices), block = 256: one workgroup
+// per block.  The block's workspace row (rows c = value column, entries f;
+// row DP = the z vector) is staged in LDS and read transposed as the A
+// operand (A[f][c]); wave w takes the block's 16-token tiles w, w + 4, ...;
+// the B operand u^T is read straight from global memory.  u stays exact
+// bf16; the per-token factor and the z term are applied in fp32.
+template <int DP, int PHI, typename TT>
+__global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
+    const bf16_t* __restrict__ X, const TT* __restrict__ T, const bf16_t* __restrict__ U,
+    const float* __restrict__ uscale, const float* __restrict__ uext, bf16_t* __restrict__ dX,
+    Geo g, int N, int d) {
+  using D = BlockedDims<DP>;
+  constexpr int NT = D::NT, DS = D::DS, EP = D::EP, RS = D::RS;
+  // fp32 state (the precise S~ of dQ) enters as two bf16 parts, hi + lo
+  constexpr bool SPLIT = sizeof(TT) == 4;
+  constexpr int NP = SPLIT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) bf16_t sT[NP][DP * RS];  // rows c, entries f
+  __shared__ __attribute__((aligned(16))) float sz[DP];             // the z row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.y;
+  const int blk = blockIdx.x;
+  const size_t off = (size_t)slice * N * d;
+  const TT* row = T + ((size_t)slice * g.M + blk) * EP;
+  constexpr int F8P = DP / 8;
+  for (int it = tid; it < DP * F8P; it += kBlkThreads) {
+    const int c = it / F8P, f = it - (it / F8P) * F8P;
+    if constexpr (SPLIT) {
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f + 4);
+      const u32x4_t hi = u32x4_t{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]),
+                                 pack2(x1[2], x1[3])};
+      const u32x4_t lo = u32x4_t{pack2(x0[0] - lo_f32(hi[0]), x0[1] - hi_f32(hi[0])),
+                                 pack2(x0[2] - lo_f32(hi[1]), x0[3] - hi_f32(hi[1])),
+                                 pack2(x1[0] - lo_f32(hi[2]), x1[1] - hi_f32(hi[2])),
+                                 pack2(x1[2] - lo_f32(hi[3]), x1[3] - hi_f32(hi[3]))};
+      *reinterpret_cast<u32x4_t*>(sT[0] + c * RS + 8 * f) = hi;
+      *reinterpret_cast<u32x4_t*>(sT[NP - 1] + c * RS + 8 * f) = lo;
+    } else {
+      *reinterpret_cast<u32x4_t*>(sT[0] + c * RS + 8 * f) =
+          *reinterpret_cast<const u32x4_t*>(row + c * DP + 8 * f);
+    }
+  }
+  for (int f = tid; f < DP; f += kBlkThreads) {
+    if constexpr (SPLIT) sz[f] = row[DP * DP + f];
+    else sz[f] = bf16_to_f32(row[DP * DP + f]);
+  }
+  lds_barrier();
+  const int bb = g.blockbase(blk);
+  for (int t0 = 16 * wave; t0 < g.nb; t0 += 16 * kBlkWaves) {
+    const int j = t0 + s;
+    const int tq = j < g.nb ? bb + g.tokoff(j) : -1;
+    // B operand u^T: lane (s, grp), step kc holds u[token][32kc + 8grp .. +7]
+    u16x8_t bu[DS];
+#pragma unroll
+    for (int kc = 0; kc < DS; ++kc) {
+      const int c0 = 32 * kc + 8 * grp;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (tq >= 0 && c0 < d) v = *reinterpret_cast<const u32x4_t*>(U + off + (size_t)tq * d + c0);
+      bu[kc] = __builtin_bit_cast(u16x8_t, v);
+    }
+    const float us = (tq >= 0 && uscale != nullptr) ? uscale[(size_t)slice * N + tq] : 1.0f;
+    const float ue = tq < 0 ? 0.0f : (uext != nullptr ? uext[(size_t)slice * N + tq] : 1.0f);
+#pragma unroll
+    for (int ft = 0; ft < NT; ++ft) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int kc = 0; kc < DS; ++kc)
+          acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), bu[kc], acc);
+      // acc lane (s, grp) element r = sum_c T[f][c] u[token t0 + s][c], f = 16ft + 4grp + r
+      const int f = 16 * ft + 4 * grp;
+      if (tq >= 0 && f < d) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(X + off + (size_t)tq * d + f);
+        const float x[4] = {lo_f32(xv.x), hi_f32(xv.x), lo_f32(xv.y), hi_f32(xv.y)};
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (acc[r] * us + sz[f + r] * ue) * dphi_apply<PHI>(x[r]);
+        *reinterpret_cast<uint2*>(dX + off + (size_t)tq * d + f) =
+            make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step 5.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
+// over the workspace rows (A = dS~, B = S).  grid = (ceil(M/16)^2, slices),
+// block = 256: a 16 x 16 output tile per workgroup, the contraction split over
+// the four waves (steps of 32 entries, wave w takes steps w, w + 4, ...) and
+// summed in LDS.  Rows past M are clamped on load and never stored.
+template <int DP>
+__global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __restrict__ A,
+                                                            const bf16_t* __restrict__ Bm,
+                                                            float* __restrict__ P, int M) {
+  using D = BlockedDims<DP>;
+  constexpr int EP = D::EP, E = DP * DP + DP, NSTEP = E / 32;
+  static_assert(E % 32 == 0, "contraction steps");
+  __shared__ float red[kBlkWaves][256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const long slice = blockIdx.y;
+  const int nt = (M + 15) / 16;
+  const int i0 = 16 * (blockIdx.x / nt), b0 = 16 * (blockIdx.x % nt);
+  const bf16_t* arow = A + ((size_t)slice * M + min(i0 + s, M - 1)) * EP + 8 * grp;
+  const bf16_t* brow = Bm + ((size_t)slice * M + min(b0 + s, M - 1)) * EP + 8 * grp;
+  f32x4_t acc = zero4();
+  for (int k = wave; k < NSTEP; k += kBlkWaves)
+    acc = mfma_bf16(*reinterpret_cast<const u16x8_t*>(arow + 32 * k),
+                    *reinterpret_cast<const u16x8_t*>(brow + 32 * k), acc);
+  // acc lane (s, grp) element r = P[i0 + 4grp + r][b0 + s]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][(4 * grp + r) * 16 + s] = acc[r];
+  __syncthreads();
+  if (tid < 256) {
+    const int ii = tid / 16, bl = tid % 16;
+    const float v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    if (i0 + ii < M && b0 + bl < M) P[((size_t)slice * M + i0 + ii) * M + b0 + bl] = v;
+  }
+}
+
+// dW[h][i][b] = sum over the batch of P[batch * H + h][i][b], in batch order.
+__global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
+                                                   float* __restrict__ dW, int B, int H, int M) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long MM = (long)M * M;
+  if (e >= (long)H * MM) return;
+  const long h = e / MM, ib = e - h * MM;
+  float acc = 0.0f;
+  for (int b = 0; b < B; ++b) acc += P[((long)b * H + h) * MM + ib];
+  dW[e] = acc;
+}
+
+// ---------------------------------------------------------------------------
+inline bool backward_supports(int dtype, int d, int M, long slices) {
+  if (!blocked_supports(dtype, d, M, slices)) return false;
+  // the precise mixing GEMM runs 64 query blocks per workgroup on a 1-D grid,
+  // and the dW tile grid is ceil(M/16)^2 workgroups along x
+  const long n = (slices + 7) / 8 * 8 * (long)(blocked_ws_elems(d) / kMixEB) * ((M + 63) / 64);
+  return n * kBlkThreads < (1L << 31) && (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
+}
+
+// Workspace: S, S~, dS~, dS ([slices][M][EP] bf16 each), the precise S~
+// ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden and rq ([slices][N]
+// fp32 each), P ([slices][M][M] fp32).
+inline size_t backward_workspace(long slices, int M, int N, int d) {
+  const size_t rows = (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
+  const size_t al = 256;
+  auto up = [&](size_t x) { return (x + al - 1) / al * al; };
+  return 4 * up(rows) + 2 * up(rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
+         2 * up((size_t)slices * N * sizeof(float)) + up((size_t)slices * M * M * sizeof(float));
+}
+
+template <int DP, int PHI>
+int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                      const bf16_t* K, const bf16_t* V, const float* W, const bf16_t* dY,
+                      bf16_t* dQ, bf16_t* dK, bf16_t* dV, float* dW, void* ws, hipStream_t st) {
+  using D = BlockedDims<DP>;
+  const int M = g.M;
+  const size_t al = 256;
+  auto up = [&](size_t x) { return (x + al - 1) / al * al; };
+  const size_t rows = (size_t)slices * M * D::EP;
+  char* p = static_cast<char*>(ws);
+  bf16_t* S = reinterpret_cast<bf16_t*>(p);
+  bf16_t* St = S + rows;  // launch_summary_mix places S~ right after S
+  p += 2 * up(rows * sizeof(bf16_t));
+  bf16_t* dSt = reinterpret_cast<bf16_t*>(p);
+  p += up(rows * sizeof(bf16_t));
+  bf16_t* dS = reinterpret_cast<bf16_t*>(p);
+  p += up(rows * sizeof(bf16_t));
+  float* St32 = reinterpret_cast<float*>(p);
+  p += up(rows * sizeof(float));
+  bf16_t* dN = reinterpret_cast<bf16_t*>(p);
+  p += up((size_t)slices * N * d * sizeof(bf16_t));
+  float* dden = reinterpret_cast<float*>(p);
+  p += up((size_t)slices * N * sizeof(float));
+  float* rq = reinterpret_cast<float*>(p);
+  p += up((size_t)slices * N * sizeof(float));
+  float* P = reinterpret_cast<float*>(p);
+  static_assert(sizeof(bf16_t) == 2, "bf16");
+  if (2 * up(rows * sizeof(bf16_t)) != 2 * rows * sizeof(bf16_t)) {
+    // S~ must directly follow S (launch_summary_mix's layout): rows*2 bytes is
+    // a multiple of 256 because EP is a multiple of 128
+    return -1;
+  }
+  const unsigned nsl = (unsigned)slices;
+  // 1. forward state
+  launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, S, 0, st);
+  // 2. dn, dden
+  const unsigned nbw = (unsigned)((M + kBlkWaves - 1) / kBlkWaves);
+  k_bwd_dn<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, dY, dN, dden, rq, g, N, d);
+  // 3. dS~ = phi(Q)^T dN per query block, dz~ weighted by dden
+  k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(Q, dN, dSt, g, N, d,
+                                                                           dden);
+  // 4. dS = W^T-mixing of dS~
+  launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, st);
+  // 5. dW
+  const unsigned nt = (unsigned)((M + 15) / 16);
+  k_dw_partial<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+  const long nw = (long)H * M * M;
+  k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
+  // 6. dQ, against the precise S~
+  launch_mix_f32<DP>(slices, H, M, S, W, St32, kMixPlain, st);
+  k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
+      Q, St32, dY, rq, dden, dQ, g, N, d);
+  // 7. dK
+  k_bwd_dphi<DP, PHI, bf16_t><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
+      K, dS, V, nullptr, nullptr, dK, g, N, d);
+  // 8. dV = readout of phi(K) against dS without the normaliser
+  Geo g0 = g;
+  g0.norm = 0;
+  k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, dS, dV, g0, N, d);
+  return 0;
+}
+
+template <int PHI>
+int launch_backward_p(long slices, int B, int H, int N, int d, const Geo& g, const bf16_t* Q,
+                      const bf16_t* K, const bf16_t* V, const float* W, const bf16_t* dY,
+                      bf16_t* dQ, bf16_t* dK, bf16_t* dV, float* dW, void* ws, hipStream_t st) {
+  switch (blocked_dp(d)) {
+    case 32: return launch_backward_t<32, PHI>(slices, B, H, N, d, g, Q, K, V, W, dY, dQ, dK, dV, dW, ws, st);
+    case 64: return launch_backward_t<64, PHI>(slices, B, H, N, d, g, Q, K, V, W, dY, dQ, dK, dV, dW, ws, st);
+    default: return launch_backward_t<96, PHI>(slices, B, H, N, d, g, Q, K, V, W, dY, dQ, dK, dV, dW, ws, st);
+  }
+}
+
+inline int launch_backward(long slices, int B, int H, int N, int d, const Geo& g, int phi,
+                           const bf16_t* Q, const bf16_t* K, const bf16_t* V, const float* W,
+                           const bf16_t* dY, bf16_t* dQ, bf16_t* dK, bf16_t* dV, float* dW,
+                           void* ws, hipStream_t st) {
+  if (phi == PHI_RELU)
+    return launch_backward_p<PHI_RELU>(slices, B, H, N, d, g, Q, K, V, W, dY, dQ, dK, dV, dW, ws, st);
+  return launch_backward_p<PHI_ELU1>(slices, B, H, N, d, g, Q, K, V, W, dY, dQ, dK, dV, dW, ws, st);
+}
+
+}  // namespace mhla

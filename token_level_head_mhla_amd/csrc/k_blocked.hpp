@@ -45,10 +45,14 @@ inline int blocked_dp(int d) { return (d + 31) / 32 * 32; }
 // S[:, 16ct .. 16ct+15] from transpose-read operands, and wave 0 also forms
 // z_b (a ones B operand).  Small LDS and register footprints keep ~24 waves
 // per CU, which hides the load latency of this bandwidth-bound kernel.
+//
+// zw == nullptr gives z_b = sum_j phi(K_j); otherwise z_b = sum_j zw[j] phi(K_j)
+// with zw a per-token fp32 weight ([slices, N]); the backward pass uses this
+// for dz~_i = sum_q dden_q phi(Q_q).
 template <int DP, int PHI>
 __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
     const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, bf16_t* __restrict__ S, Geo g,
-    int N, int d) {
+    int N, int d, const float* __restrict__ zw) {
   using D = BlockedDims<DP>;
   constexpr int NT = D::NT, RS = D::RS, EP = D::EP;
   constexpr int NTHR = 64 * NT;
@@ -56,6 +60,7 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
   constexpr int UCH = 64 * F8P / NTHR;  // 16-byte chunks per thread and tensor (= 2)
   __shared__ __attribute__((aligned(16))) bf16_t sk[64 * RS];
   __shared__ __attribute__((aligned(16))) bf16_t sv[64 * RS];
+  __shared__ __attribute__((aligned(16))) bf16_t szw[64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int ct = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,8 +100,12 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
         vr[u] = *reinterpret_cast<const u32x4_t*>(V + src);
       }
     }
+    float wz = 0.0f;
+    if (zw != nullptr && tid < 64 && c0 + tid < g.nb)
+      wz = zw[(size_t)slice * N + bb + g.tokoff(c0 + tid)];
     // the previous chunk's reads (or, for d < DP, the zero fill) are done
     if (c0 > 0 || d < DP) lds_barrier();
+    if (zw != nullptr && tid < 64) szw[tid] = f32_to_bf16(wz);
 #pragma unroll
     for (int u = 0; u < UCH; ++u) {
       if (dst[u] >= 0) {
@@ -109,11 +118,15 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const u16x8_t bv = lds_tr8(sv, RS, 32 * st, 16 * ct, lane);
+      // B operand of the z column: ones, or the chunk's token weights
+      const u16x8_t bz = zw == nullptr
+          ? ones
+          : *reinterpret_cast<const u16x8_t*>(szw + 32 * st + 8 * (lane >> 4));
 #pragma unroll
       for (int kt = 0; kt < NT; ++kt) {
         const u16x8_t a = lds_tr8(sk, RS, 32 * st, 16 * kt, lane);
         acc[kt] = mfma_bf16(a, bv, acc[kt]);
-        if (ct == 0) zacc[kt] = mfma_bf16(a, ones, zacc[kt]);
+        if (ct == 0) zacc[kt] = mfma_bf16(a, bz, zacc[kt]);
       }
     }
   }
@@ -149,13 +162,23 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 // into registers while the current step's tiles (double-buffered in LDS) feed
 // the MFMAs, so there is one barrier per step.
 //
-// causal != 0 mixes only earlier chunks (W[i,b] is taken as 0 for b >= i):
-// the prefix mixture of the chunkwise causal form.
-template <int EP, int IB>
+// mode selects the coefficient of S[b] in output row i: kMixPlain W[i,b];
+// kMixCausal W[i,b] for b < i and 0 otherwise (the prefix mixture of the
+// chunkwise causal form); kMixTransposed W[b,i] (the backward pass's
+// dS_b = sum_i W[i,b] dS~_i).
+//
+// OutT = float is the precise variant used by the backward pass: the
+// coefficients enter as two bf16 parts (w = hi + lo, two MFMAs per step) and
+// S~ is stored in fp32, so that the only rounding left is that of S.
+enum { kMixPlain = 0, kMixCausal = 1, kMixTransposed = 2 };
+
+template <int EP, int IB, typename OutT = bf16_t>
 __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
                                                           const float* __restrict__ W,
-                                                          bf16_t* __restrict__ St, int M, int H,
-                                                          long nslices, int causal) {
+                                                          OutT* __restrict__ St, int M, int H,
+                                                          long nslices, int mode) {
+  constexpr bool PREC = sizeof(OutT) == 4;
+  constexpr int WSPLIT = PREC ? 2 : 1;
   constexpr int EB = kMixEB, KB = kMixKB;
   constexpr int EW = IB == 64 ? 32 : 64, IW = 64;
   constexpr int AT = EW / 16, BT = IW / 16;        // MFMA tiles per wave along e and i
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   constexpr int WCH = IB * KB / 4 / kBlkThreads;   // 4-float W chunks per thread per step
   static_assert(SCH * 8 * kBlkThreads == KB * EB && WCH * 4 * kBlkThreads == IB * KB, "tiles");
   __shared__ __attribute__((aligned(16))) bf16_t sS[2][KB * SRS];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[2][IB * WRS];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][WSPLIT][IB * WRS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,7 +206,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   const int h = (int)(slice % H);
   const bf16_t* Ss = S + (size_t)slice * M * EP;
   const float* Wh = W + (size_t)h * M * M;
-  const bool wvec = (M & 3) == 0;
+  const bool wvec = (M & 3) == 0 && mode != kMixTransposed;
 
   f32x4_t acc[AT][BT];
 #pragma unroll
@@ -210,9 +233,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
       if (wvec && bc + 3 < M) {                                                           \
         v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bc);                   \
       } else {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M) v[q] = Wh[(size_t)i * M + bc + q]; \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M)                     \
+          v[q] = mode == kMixTransposed ? Wh[(size_t)(bc + q) * M + i] : Wh[(size_t)i * M + bc + q]; \
       }                                                                                   \
-      if (causal) {                                                                       \
+      if (mode == kMixCausal) {                                                           \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q >= i) v[q] = 0.0f;       \
       }                                                                                   \
     }                                                                                     \
@@ -227,8 +251,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
     const int c = tid + kBlkThreads * u;                                                  \
     const int r = c / (KB / 4), f = c % (KB / 4);                                         \
-    *reinterpret_cast<uint2*>(sW[buf] + r * WRS + 4 * f) =                                \
-        make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));                 \
+    const uint2 hi_ = make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));  \
+    *reinterpret_cast<uint2*>(sW[buf][0] + r * WRS + 4 * f) = hi_;                        \
+    if constexpr (PREC) {                                                                 \
+      *reinterpret_cast<uint2*>(sW[buf][WSPLIT - 1] + r * WRS + 4 * f) =                  \
+          make_uint2(pack2(wr[u][0] - lo_f32(hi_.x), wr[u][1] - hi_f32(hi_.x)),           \
+                     pack2(wr[u][2] - lo_f32(hi_.y), wr[u][3] - hi_f32(hi_.y)));          \
+    }                                                                                     \
   }
 
   const int nk = (M + KB - 1) / KB;
@@ -245,11 +274,21 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
     for (int a = 0; a < AT; ++a) af[a] = lds_tr8(sS[buf], SRS, 0, EW * we + 16 * a, lane);
 #pragma unroll
     for (int c = 0; c < BT; ++c)
-      bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf] + (IW * wi + 16 * c + s) * WRS + 8 * grp);
+      bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf][0] + (IW * wi + 16 * c + s) * WRS + 8 * grp);
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
       for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+    if constexpr (PREC) {
+#pragma unroll
+      for (int c = 0; c < BT; ++c)
+        bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf][WSPLIT - 1] +
+                                                  (IW * wi + 16 * c + s) * WRS + 8 * grp);
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+    }
     if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1) }
     lds_barrier();
   }
@@ -260,11 +299,15 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   for (int c = 0; c < BT; ++c) {
     const int i = i0 + IW * wi + 16 * c + s;
     if (i < M) {
-      bf16_t* row = St + ((size_t)slice * M + i) * EP + e0 + EW * we;
+      OutT* row = St + ((size_t)slice * M + i) * EP + e0 + EW * we;
 #pragma unroll
-      for (int a = 0; a < AT; ++a)
-        *reinterpret_cast<uint2*>(row + 16 * a + 4 * grp) =
-            make_uint2(pack2(acc[a][c][0], acc[a][c][1]), pack2(acc[a][c][2], acc[a][c][3]));
+      for (int a = 0; a < AT; ++a) {
+        if constexpr (PREC)
+          *reinterpret_cast<f32x4_t*>(row + 16 * a + 4 * grp) = acc[a][c];
+        else
+          *reinterpret_cast<uint2*>(row + 16 * a + 4 * grp) =
+              make_uint2(pack2(acc[a][c][0], acc[a][c][1]), pack2(acc[a][c][2], acc[a][c][3]));
+      }
     }
   }
 }
@@ -376,6 +419,32 @@ inline size_t blocked_workspace(long slices, int M, int d) {
   return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
 }
 
+// One mixing GEMM over all slices: St[slice][i] = sum_b coef(i, b) S[slice][b]
+// with the coefficient chosen by mode (kMixPlain, kMixCausal, kMixTransposed).
+template <int DP>
+void launch_mix(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St, int mode,
+                hipStream_t st) {
+  using D = BlockedDims<DP>;
+  const long xslices = (slices + 7) / 8 * 8;
+  const int ib = mix_ib(M);
+  const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + ib - 1) / ib));
+  if (ib == 64)
+    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+  else
+    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+}
+
+// The precise variant (fp32 S~, coefficients split in two bf16 parts), with
+// 64 query blocks per workgroup so that both coefficient tiles fit in LDS.
+template <int DP>
+void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, float* St,
+                    int mode, hipStream_t st) {
+  using D = BlockedDims<DP>;
+  const long xslices = (slices + 7) / 8 * 8;
+  const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + 63) / 64));
+  k_mix_mfma<D::EP, 64, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+}
+
 // Summary and mixing launches shared by the plain and the causal readout; with
 // causal != 0 the mixing keeps only earlier chunks.  Returns S~ in the workspace.
 template <int DP, int PHI>
@@ -386,14 +455,8 @@ bf16_t* launch_summary_mix(long slices, int H, int N, int d, const Geo& g, const
   bf16_t* S = ws;
   bf16_t* St = ws + (size_t)slices * g.M * D::EP;
   k_summary_mfma<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), 64 * D::NT, 0, st>>>(
-      K, V, S, g, N, d);
-  const long xslices = (slices + 7) / 8 * 8;
-  const int ib = mix_ib(g.M);
-  const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((g.M + ib - 1) / ib));
-  if (ib == 64)
-    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices, causal);
-  else
-    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, g.M, H, slices, causal);
+      K, V, S, g, N, d, nullptr);
+  launch_mix<DP>(slices, H, g.M, S, W, St, causal ? kMixCausal : kMixPlain, st);
   return St;
 }
 

@@ -22,6 +22,7 @@
 #include "k_blocked.hpp"
 #include "k_pairs.hpp"
 #include "k_causal.hpp"
+#include "k_backward.hpp"
 
 namespace mhla {
 namespace {
@@ -258,6 +259,55 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
   return MHLA_OK;
 }
 
+int run_backward(const void* Q, const void* K, const void* V, const float* W, const void* dY,
+                 void* dQ, void* dK, void* dV, float* dW, int B, int H, int N, int d,
+                 const mhla_block_shape* shape, int phi, int dtype, int flags, void* stream) {
+  Problem p;
+  int rc = check(B, H, N, d, shape, phi, dtype, &p);
+  if (rc != MHLA_OK) return rc;
+  rc = check_flags(flags, &p);
+  if (rc != MHLA_OK) return rc;
+  if (p.causal()) return fail(MHLA_ERR_UNSUPPORTED, "the causal form has no backward pass here");
+  if (!backward_supports(dtype, d, p.g.M, p.slices()))
+    return fail(MHLA_ERR_UNSUPPORTED, "the backward pass needs bf16 and d <= 96 (d=%d dtype=%d)",
+                d, dtype);
+  const void* in[5] = {Q, K, V, W, dY};
+  void* outp[4] = {dQ, dK, dV, dW};
+  for (const void* q : in)
+    if (!q) return fail(MHLA_ERR_INVALID_ARG, "an input pointer is NULL");
+  for (const void* q : outp)
+    if (!q) return fail(MHLA_ERR_INVALID_ARG, "an output pointer is NULL");
+  for (const void* q : in)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return fail(MHLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  for (const void* q : outp)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return fail(MHLA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t tb = p.tensor_bytes(), wb = (size_t)H * p.g.M * p.g.M * sizeof(float);
+  const size_t in_b[5] = {tb, tb, tb, wb, tb};
+  const size_t out_b[4] = {tb, tb, tb, wb};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 5; ++b)
+      if (overlaps(outp[a], out_b[a], in[b], in_b[b]))
+        return fail(MHLA_ERR_ALIAS, "gradient %d overlaps input %d", a, b);
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outp[a], out_b[a], outp[b], out_b[b]))
+        return fail(MHLA_ERR_ALIAS, "gradients %d and %d overlap", a, b);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  void* ws = nullptr;
+  rc = get_workspace(backward_workspace(p.slices(), p.g.M, N, d), st, &ws);
+  if (rc != MHLA_OK) return rc;
+  rc = launch_backward(p.slices(), B, H, N, d, p.g, phi, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, W, (const bf16_t*)dY, (bf16_t*)dQ, (bf16_t*)dK,
+                       (bf16_t*)dV, dW, ws, st);
+  if (rc != MHLA_OK) return fail(MHLA_ERR_HIP, "backward set-up failed");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MHLA_OK;
+}
+
 }  // namespace
 }  // namespace mhla
 
@@ -287,6 +337,14 @@ int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wm
   if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
   return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, flags, path, stream);
+}
+
+int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix, const void* dY,
+                  void* dQ, void* dK, void* dV, float* dWmix, int B, int H, int N, int d,
+                  const mhla_block_shape* block_shape, int phi_kind, int dtype, int flags,
+                  void* stream) {
+  return run_backward(Q, K, V, Wmix, dY, dQ, dK, dV, dWmix, B, H, N, d, block_shape, phi_kind,
+                      dtype, flags, stream);
 }
 
 int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
