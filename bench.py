@@ -44,6 +44,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="time a plain device copy of this many MB instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (mhla_backward) instead of the forward")
     return ap.parse_args()
 
 
@@ -78,6 +80,8 @@ def main():
         return 2
     if args.copy_mb:
         return copy_bench(args)
+    if args.backward:
+        return backward_bench(args)
 
     import torch
     import token_level_head_mhla_amd as m
@@ -179,6 +183,58 @@ def main():
         result["cpu_baseline"], result["parity"] = cpu_baseline(inp, out, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def backward_bench(args):
+    """One step = one mhla_backward call (recompute of the forward state, then
+    dQ, dK, dV, dW) on the workload's inputs and a seeded upstream gradient."""
+    import torch
+    import token_level_head_mhla_amd as m
+    from mhla_inputs import WORKLOADS, make_inputs, make_upstream_grad
+
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, dy = dev(inp.q), dev(inp.k), dev(inp.v), dev(make_upstream_grad(wl))
+    w = torch.from_numpy(inp.w).cuda()
+    dq, dk, dv, dw = (torch.empty_like(x) for x in (q, k, v, w))
+    shape = (wl.grid, wl.block)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m.mhla_backward(q, k, v, w, dy, dq, dk, dv, dw, shape, wl.phi, wl.flags, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    t = wl.B * wl.H * wl.N * wl.d * 2
+    alg_bytes = 7 * t + 2 * wl.H * wl.M * wl.M * 4   # read Q,K,V,dY,W; write dQ,dK,dV,dW
+    d2 = wl.d * wl.d
+    alg_flops = wl.B * wl.H * (12 * wl.N * d2 + 6 * wl.M * wl.M * d2)
+    gbs = alg_bytes / (ms / 1e3) / 1e9
+    tfs = alg_flops / (ms / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "MHLA bwd tokens/s per GPU", "value": round(wl.B * wl.N / (ms / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "dtype": "bf16",
+        "config": {"workload": wl.name, "pass": "backward"},
+        "roofline": {"bound": "hbm" if gbs / HBM_PEAK_GBS >= tfs / BF16_PEAK_TFLOPS else "mfma",
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "algorithmic_flops_per_launch": alg_flops}}), flush=True)
     return 0
 
 

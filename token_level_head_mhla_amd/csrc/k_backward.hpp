@@ -340,7 +340,7 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   const long nw = (long)H * M * M;
   k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
   // 6. dQ, against the precise S~
-  launch_mix_f32<DP>(slices, H, M, S, W, St32, kMixPlain, st);
+  launch_mix_f32<DP>(slices, H, M, S, W, St32, st);
   k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
       Q, St32, dY, rq, dden, dQ, g, N, d);
   // 7. dK

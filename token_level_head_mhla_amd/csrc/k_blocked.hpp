@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 // into registers while the current step's tiles (double-buffered in LDS) feed
 // the MFMAs, so there is one barrier per step.
 //
-// mode selects the coefficient of S[b] in output row i: kMixPlain W[i,b];
+// MODE selects the coefficient of S[b] in output row i: kMixPlain W[i,b];
 // kMixCausal W[i,b] for b < i and 0 otherwise (the prefix mixture of the
 // chunkwise causal form); kMixTransposed W[b,i] (the backward pass's
 // dS_b = sum_i W[i,b] dS~_i).
@@ -172,11 +172,11 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 // S~ is stored in fp32, so that the only rounding left is that of S.
 enum { kMixPlain = 0, kMixCausal = 1, kMixTransposed = 2 };
 
-template <int EP, int IB, typename OutT = bf16_t>
+template <int EP, int IB, int MODE, typename OutT = bf16_t>
 __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
                                                           const float* __restrict__ W,
                                                           OutT* __restrict__ St, int M, int H,
-                                                          long nslices, int mode) {
+                                                          long nslices) {
   constexpr bool PREC = sizeof(OutT) == 4;
   constexpr int WSPLIT = PREC ? 2 : 1;
   constexpr int EB = kMixEB, KB = kMixKB;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   const int h = (int)(slice % H);
   const bf16_t* Ss = S + (size_t)slice * M * EP;
   const float* Wh = W + (size_t)h * M * M;
-  const bool wvec = (M & 3) == 0 && mode != kMixTransposed;
+  const bool wvec = (M & 3) == 0 && MODE != kMixTransposed;
 
   f32x4_t acc[AT][BT];
 #pragma unroll
@@ -232,11 +232,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
     if (i < M) {                                                                          \
       if (wvec && bc + 3 < M) {                                                           \
         v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bc);                   \
+      } else if constexpr (MODE == kMixTransposed) {                                      \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M)                     \
+          v[q] = Wh[(size_t)(bc + q) * M + i];                                            \
       } else {                                                                            \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M)                     \
-          v[q] = mode == kMixTransposed ? Wh[(size_t)(bc + q) * M + i] : Wh[(size_t)i * M + bc + q]; \
+          v[q] = Wh[(size_t)i * M + bc + q];                                              \
       }                                                                                   \
-      if (mode == kMixCausal) {                                                           \
+      if constexpr (MODE == kMixCausal) {                                                 \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q >= i) v[q] = 0.0f;       \
       }                                                                                   \
     }                                                                                     \
@@ -421,28 +424,37 @@ inline size_t blocked_workspace(long slices, int M, int d) {
 
 // One mixing GEMM over all slices: St[slice][i] = sum_b coef(i, b) S[slice][b]
 // with the coefficient chosen by mode (kMixPlain, kMixCausal, kMixTransposed).
-template <int DP>
-void launch_mix(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St, int mode,
-                hipStream_t st) {
+template <int DP, int MODE>
+void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St,
+                  hipStream_t st) {
   using D = BlockedDims<DP>;
   const long xslices = (slices + 7) / 8 * 8;
   const int ib = mix_ib(M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + ib - 1) / ib));
   if (ib == 64)
-    k_mix_mfma<D::EP, 64><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+    k_mix_mfma<D::EP, 64, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
   else
-    k_mix_mfma<D::EP, 128><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+    k_mix_mfma<D::EP, 128, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
+}
+
+template <int DP>
+void launch_mix(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St, int mode,
+                hipStream_t st) {
+  if (mode == kMixCausal) launch_mix_m<DP, kMixCausal>(slices, H, M, S, W, St, st);
+  else if (mode == kMixTransposed) launch_mix_m<DP, kMixTransposed>(slices, H, M, S, W, St, st);
+  else launch_mix_m<DP, kMixPlain>(slices, H, M, S, W, St, st);
 }
 
 // The precise variant (fp32 S~, coefficients split in two bf16 parts), with
 // 64 query blocks per workgroup so that both coefficient tiles fit in LDS.
 template <int DP>
 void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, float* St,
-                    int mode, hipStream_t st) {
+                    hipStream_t st) {
   using D = BlockedDims<DP>;
   const long xslices = (slices + 7) / 8 * 8;
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + 63) / 64));
-  k_mix_mfma<D::EP, 64, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices, mode);
+  k_mix_mfma<D::EP, 64, kMixPlain, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
+                                                                           slices);
 }
 
 // Summary and mixing launches shared by the plain and the causal readout; with
