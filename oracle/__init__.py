@@ -24,6 +24,12 @@ W[i,i]; in the explicit matrix that is the mask A[q,j] = 0 for j > q.
 ``np_lb_init`` is the locality-biased initial mixing matrix of §4.2
 (m0[i,j] proportional to 1 - dist(i,j) / max_k dist(i,k), rows summing to 1).
 
+``np_decode`` is incremental (streaming) inference of the causal form, one
+token at a time, in the order the MHLA paper's App. C ("Causal inference")
+describes: past chunk summaries are kept, the current chunk's summary is
+updated with each new token, and the current chunk's mixed state is the mix of
+the past summaries plus m_ii times that running summary.
+
 ``np_backward`` gives the gradients of the (non-causal) forward for an upstream
 gradient G = dL/dY.  The pages print no backward pass; it is the chain rule
 applied to the three forward steps of §4.1, written out step by step in
@@ -297,3 +303,42 @@ def np_backward(Q, K, V, W, G, grid, block, phi_kind, norm=True, dw_abs=False):
     if dw_abs:
         return dQ, dK, dV, dW, dWabs
     return dQ, dK, dV, dW
+
+
+def np_decode(Q, K, V, W, nb, phi_kind, norm=True):
+    """Token-by-token causal inference over a 1-D sequence cut into chunks of nb
+    tokens (chunk i = tokens [i*nb, (i+1)*nb)).  Q, K, V: [B, H, N, d]; W:
+    [H, M, M].  For each token t in chunk i:
+      1. when t starts chunk i, the finished chunks' summaries are mixed once:
+         P_i = sum_{b<i} W[i,b] S_b, p_i = sum_{b<i} W[i,b] z_b, and the
+         running summary of chunk i starts at zero;
+      2. S_i += phi(k_t) v_t^T, z_i += phi(k_t);
+      3. y_t = phi(q_t)(P_i + W[i,i] S_i) / phi(q_t).(p_i + W[i,i] z_i)
+         (the numerator alone without the normaliser; 0 for a zero denominator).
+    Returns Y [B, H, N, d]."""
+    Q, K, V, W = _f64(Q), _f64(K), _f64(V), _f64(W)
+    B, H, N, d = Q.shape
+    M = (N + nb - 1) // nb
+    Y = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((M, d, d))
+            z = np.zeros((M, d))
+            P = np.zeros((d, d))
+            p = np.zeros(d)
+            for t in range(N):
+                i = t // nb
+                if t % nb == 0:
+                    P = np.einsum("b,bfc->fc", W[h, i, :i], S[:i])
+                    p = W[h, i, :i] @ z[:i]
+                pk = np_phi(phi_kind, K[b, h, t])
+                S[i] += np.outer(pk, V[b, h, t])
+                z[i] += pk
+                pq = np_phi(phi_kind, Q[b, h, t])
+                num = pq @ (P + W[h, i, i] * S[i])
+                if not norm:
+                    Y[b, h, t] = num
+                    continue
+                den = pq @ (p + W[h, i, i] * z[i])
+                Y[b, h, t] = 0.0 if den == 0.0 else num / den
+    return Y

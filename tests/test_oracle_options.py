@@ -250,3 +250,61 @@ def test_lb_init_properties(grid, block):
     assert np.all(np.argmax(m, axis=1) == np.arange(M))
     assert np.all(m.min(axis=1) == 0.0)
     np.testing.assert_allclose(m, m[::-1, ::-1], rtol=0, atol=1e-15)   # point symmetry
+
+
+# ---------------------------------------------------------------- incremental inference
+
+@pytest.mark.parametrize("norm", [True, False])
+def test_decode_worked_example(norm):
+    """The hand-derived chunkwise example, produced token by token (MHLA paper
+    App. C, causal inference)."""
+    g = _load("worked_causal_relu_1x4.json")
+    num = np.array(g["numerator"], dtype=np.float64)
+    den = np.array(g["denominator"], dtype=np.float64)
+    exp = num / den[:, None] if norm else num
+    Y = oracle.np_decode(_arr(g, "Q"), _arr(g, "K"), _arr(g, "V"), np.array(g["W"])[None], 2,
+                         g["phi"], norm=norm)[0, 0]
+    np.testing.assert_allclose(Y, exp, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("nb", [1, 6, 8, 24])
+@pytest.mark.parametrize("phi", [PHI_RELU, PHI_ELU1])
+@pytest.mark.parametrize("norm", [True, False])
+def test_decode_equals_causal_forward(nb, phi, norm):
+    """Streaming inference reproduces the chunkwise causal forward (C blockwise
+    oracle) and the masked token form (NumPy brute force) at every position."""
+    rng = np.random.default_rng(26 + nb + 3 * phi)
+    N = 24
+    M = N // nb
+    Q, K, V, W = _rand(rng, 2, 2, N, 5, M, "raw")
+    Yd = oracle.np_decode(Q, K, V, W, nb, phi, norm=norm)
+    Yc = oracle.blockwise(Q, K, V, W, (1, 1, N), (1, 1, nb), phi, norm=norm, causal=True)
+    np.testing.assert_allclose(Yd, Yc, rtol=1e-11, atol=1e-11)
+    Yn = oracle.numpy_bruteforce(Q, K, V, W, (1, 1, N), (1, 1, nb), phi, norm=norm, causal=True)
+    np.testing.assert_allclose(Yd, Yn, rtol=1e-11, atol=1e-11)
+
+
+DECODE_MUTANTS = {
+    "prefix_includes_own": ('P = np.einsum("b,bfc->fc", W[h, i, :i], S[:i])',
+                            'P = np.einsum("b,bfc->fc", W[h, i, :i + 1], S[:i + 1])'),
+    "own_unweighted": ("num = pq @ (P + W[h, i, i] * S[i])", "num = pq @ (P + S[i])"),
+    "den_prefix_dropped": ("den = pq @ (p + W[h, i, i] * z[i])", "den = pq @ (W[h, i, i] * z[i])"),
+    "chunk_never_reset": ("if t % nb == 0:", "if t == 0:"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_MUTANTS))
+def test_pins_catch_decode_mutant(name):
+    """Planted mistakes in a copy of np_decode fail the comparison with the
+    causal blockwise oracle."""
+    import inspect
+    import textwrap
+    old, new = DECODE_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.np_decode))
+    assert src.count(old) == 1, old
+    ns = dict(vars(oracle))
+    exec(src.replace(old, new), ns)
+    rng = np.random.default_rng(27)
+    Q, K, V, W = _rand(rng, 1, 2, 24, 4, 4, "raw")
+    ref = oracle.blockwise(Q, K, V, W, (1, 1, 24), (1, 1, 6), PHI_ELU1, causal=True)
+    assert not np.allclose(ns["np_decode"](Q, K, V, W, 6, PHI_ELU1), ref, rtol=1e-8, atol=1e-8)
