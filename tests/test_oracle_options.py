@@ -285,8 +285,8 @@ def test_decode_equals_causal_forward(nb, phi, norm):
 
 
 DECODE_MUTANTS = {
-    "prefix_includes_own": ('P = np.einsum("b,bfc->fc", W[h, i, :i], S[:i])',
-                            'P = np.einsum("b,bfc->fc", W[h, i, :i + 1], S[:i + 1])'),
+    "prefix_uses_w_column": ('P = np.einsum("b,bfc->fc", W[h, i, :i], S[:i])',
+                             'P = np.einsum("b,bfc->fc", W[h, :i, i], S[:i])'),
     "own_unweighted": ("num = pq @ (P + W[h, i, i] * S[i])", "num = pq @ (P + S[i])"),
     "den_prefix_dropped": ("den = pq @ (p + W[h, i, i] * z[i])", "den = pq @ (W[h, i, i] * z[i])"),
     "chunk_never_reset": ("if t % nb == 0:", "if t == 0:"),
