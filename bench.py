@@ -46,6 +46,9 @@ def parse():
                     help="time a plain device copy of this many MB instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (mhla_backward) instead of the forward")
+    ap.add_argument("--decode", action="store_true",
+                    help="time token-by-token causal inference (mhla_decode_step) over the "
+                         "workload's sequence instead (1-D chunked workloads, e.g. lm_causal)")
     return ap.parse_args()
 
 
@@ -82,6 +85,8 @@ def main():
         return copy_bench(args)
     if args.backward:
         return backward_bench(args)
+    if args.decode:
+        return decode_bench(args)
 
     import torch
     import token_level_head_mhla_amd as m
@@ -235,6 +240,62 @@ def backward_bench(args):
                      "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "algorithmic_flops_per_launch": alg_flops}}), flush=True)
+    return 0
+
+
+def decode_bench(args):
+    """One step = one mhla_decode_step call: one new token for each of the B*H
+    slices.  The timed region streams the whole sequence (N steps) after a
+    warm-up pass; tokens/s counts B tokens per step."""
+    import torch
+    import token_level_head_mhla_amd as m
+    from mhla_inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    if wl.grid[0] != 1 or wl.grid[1] != 1:
+        print("bench.py: --decode needs a 1-D chunked workload", file=sys.stderr)
+        return 2
+    inp = make_inputs(wl)
+
+    def dev(x):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return t.permute(2, 0, 1, 3).contiguous()   # [N, B, H, d]: token t is one slice
+
+    qt, kt, vt = dev(inp.q), dev(inp.k), dev(inp.v)
+    w = torch.from_numpy(inp.w).cuda()
+    y = torch.empty_like(qt)
+    nb, M = wl.block[2], wl.M
+    state = torch.empty(m.mhla_decode_state_bytes(wl.B, wl.H, wl.d, M) // 4, dtype=torch.float32,
+                        device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run_sequence():
+        for t in range(wl.N):
+            m.mhla_decode_step(qt[t], kt[t], vt[t], w, y[t], state, M, nb, t, wl.phi, wl.flags,
+                               stream=stream)
+
+    run_sequence()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    run_sequence()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / wl.N
+    E = wl.d * (wl.d + 1) * 4
+    # per step and slice: prefix read, running summary read and written, q/k/v/y
+    step_bytes = wl.B * wl.H * (3 * E + 4 * wl.d * 2)
+    print(json.dumps({
+        "metric": "MHLA incremental decode tokens/s per GPU",
+        "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": wl.N, "warmup": wl.N, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "dtype": "bf16 in, fp32 state",
+        "config": {"workload": wl.name, "pass": "decode", "sequences": wl.B, "heads": wl.H},
+        "roofline": {"bound": "hbm", "state_bytes_per_step": step_bytes,
+                     "achieved_GBs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}),
+          flush=True)
     return 0
 
 

@@ -149,6 +149,34 @@ int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix
                   int B, int H, int N, int d, const mhla_block_shape* block_shape,
                   int phi_kind, int dtype, int flags, void* stream);
 
+/* Incremental (streaming) inference of the causal form (MHLA paper App. C,
+ * "Causal inference"): one new token per (batch, head) slice per call.  The
+ * sequence is cut into chunks of nb tokens (at most M chunks); token t lies
+ * in chunk i = t / nb.  The caller owns a device state buffer of
+ * mhla_decode_state_bytes(B, H, d, M) bytes, holding per slice, in fp32, the
+ * M chunk summaries [S_b | z_b] and the current chunk's prefix mixture
+ * sum_{b<i} W[h][i][b] [S_b | z_b].  A call:
+ *   - when t starts chunk i, forms that prefix mixture once and restarts the
+ *     running summary of chunk i;
+ *   - adds phi(k_t) [v_t | 1]^T to the running summary;
+ *   - writes y_t = phi(q_t)(P_i + W[h][i][i] S_i) / phi(q_t).(p_i + W[h][i][i] z_i)
+ *     (the numerator alone with MHLA_FLAG_NO_NORM; 0 for a zero denominator),
+ *     which equals mhla_forward_ex(..., MHLA_FLAG_CAUSAL, ...) at position t
+ *     of a 1-D sequence with chunks of nb tokens.
+ * q, k, v, y: [B, H, d] device tensors of `dtype` (the token at position t of
+ * every slice); Wmix: [H, M, M] fp32.  Calls must come for t = 0, 1, 2, ...
+ * in order on one stream (t = 0 starts a new sequence; no separate
+ * initialisation is needed).  Cost per call: O(B H d^2), plus O(B H i d^2)
+ * when a chunk starts.  flags: 0 or MHLA_FLAG_NO_NORM (MHLA_FLAG_CAUSAL is
+ * implied and accepted).  Errors: MHLA_ERR_INVALID_ARG (bad sizes, t outside
+ * [0, M*nb), NULL pointers, unknown flags), MHLA_ERR_UNSUPPORTED (d > 128, or
+ * bf16 with d not a multiple of 8), MHLA_ERR_ALIAS (y overlaps q, k, v or the
+ * state). */
+size_t mhla_decode_state_bytes(int B, int H, int d, int M);
+int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix,
+                     void* y, void* state, int B, int H, int d, int M, int nb, int t,
+                     int phi_kind, int dtype, int flags, void* stream);
+
 /* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
  * would return for these sizes. */
 int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape,

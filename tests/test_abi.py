@@ -213,3 +213,25 @@ def test_lb_init_rejects():
     assert lib.mhla_lb_init(ctypes.byref(bs), buf, 16) == m.MHLA_OK
     bad = m.BlockShape.make((1, 4, 4), (1, 3, 2))
     assert lib.mhla_lb_init(ctypes.byref(bad), buf, 16) == m.MHLA_ERR_SHAPE
+
+
+def test_decode_state_bytes_and_rejects():
+    assert m.mhla_decode_state_bytes(2, 3, 64, 32) == 2 * 3 * 33 * 64 * 65 * 4
+    assert m.mhla_decode_state_bytes(0, 3, 64, 32) == 0
+    assert m.mhla_decode_state_bytes(1, 1, 129, 4) == 0
+    lib = m.load_library()
+    buf = (ctypes.c_char * (1 << 16))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    q, k, v, w, y, st = (base + 1024 * i for i in range(6))
+    call = lambda *a: lib.mhla_decode_step(q, k, v, w, y, st, *a)
+    # (B, H, d, M, nb, t, phi, dtype, flags, stream)
+    assert call(1, 1, 16, 4, 8, 32, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG   # t = M*nb
+    assert call(1, 1, 16, 4, 8, -1, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG
+    assert call(1, 1, 16, 4, 0, 0, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG
+    assert call(1, 1, 16, 4, 8, 0, 0, 1, 4, None) == m.MHLA_ERR_INVALID_ARG   # unknown flag
+    assert call(1, 1, 12, 4, 8, 0, 0, 1, 0, None) == m.MHLA_ERR_UNSUPPORTED   # bf16, d % 8
+    assert call(1, 1, 136, 4, 8, 0, 0, 0, 0, None) == m.MHLA_ERR_UNSUPPORTED
+    assert lib.mhla_decode_step(q, k, v, w, q, st, 1, 1, 16, 4, 8, 0, 0, 1, 0,
+                                None) == m.MHLA_ERR_ALIAS
+    assert lib.mhla_decode_step(q, k, v, w, y, None, 1, 1, 16, 4, 8, 0, 0, 1, 0,
+                                None) == m.MHLA_ERR_INVALID_ARG

@@ -1,0 +1,79 @@
+"""GPU parity of incremental (streaming) inference: mhla_decode_step called
+token by token through the C ABI against the oracle's token-by-token causal
+inference (MHLA paper App. C), which is pinned to the chunkwise causal forward.
+
+Gate: max over (batch, head) slices of max|y - y_oracle| / max|y_oracle| over
+the whole sequence, 1e-5 for fp32 and 1e-2 for bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_level_head_mhla_amd as m
+from mhla_inputs import (DTYPE_BF16, DTYPE_F32, FLAG_CAUSAL, FLAG_NO_NORM, PHI_ELU1, PHI_RELU,
+                         custom_workload, make_inputs)
+from gpu_util import TOL, slice_error, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _stream(inp, nb, flags=0):
+    """Feed the sequence one token at a time; returns Y [B, H, N, d] on the host."""
+    wl = inp.wl
+    q, k, v, w = to_device(inp)
+    B, H, N, d = q.shape
+    M = N // nb
+    qt, kt, vt = (x.permute(2, 0, 1, 3).contiguous() for x in (q, k, v))   # [N, B, H, d]
+    state = torch.empty(m.mhla_decode_state_bytes(B, H, d, M) // 4, dtype=torch.float32,
+                        device="cuda")
+    state.fill_(float("nan"))   # the first token of every chunk must not read stale state
+    y = torch.empty_like(qt)
+    for t in range(N):
+        m.mhla_decode_step(qt[t], kt[t], vt[t], w, y[t], state, M, nb, t, wl.phi, flags)
+    torch.cuda.synchronize()
+    return to_f64(y.permute(1, 2, 0, 3).contiguous())
+
+
+DECODE_CASES = [
+    # (B, H, N, nb, d, phi, dtype)
+    (2, 3, 256, 64, 64, PHI_ELU1, DTYPE_BF16),    # the LM chunk size, 4 chunks
+    (1, 2, 96, 16, 72, PHI_RELU, DTYPE_BF16),
+    (2, 2, 40, 1, 32, PHI_ELU1, DTYPE_BF16),      # a chunk per token
+    (1, 2, 48, 48, 16, PHI_ELU1, DTYPE_BF16),     # a single chunk
+    (1, 1, 64, 16, 16, PHI_RELU, DTYPE_F32),
+    (1, 2, 32, 8, 128, PHI_ELU1, DTYPE_F32),      # d = 128: LDS above 64 KB
+    (1, 2, 30, 6, 13, PHI_ELU1, DTYPE_F32),       # odd d in fp32
+]
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("B,H,N,nb,d,phi,dtype", DECODE_CASES)
+def test_decode_stream(B, H, N, nb, d, phi, dtype, norm):
+    flags = FLAG_CAUSAL | (0 if norm else FLAG_NO_NORM)
+    wl = custom_workload(B, H, d, (1, 1, N), (1, 1, nb), phi, dtype,
+                         index=hash((N, nb, d)) % 937, flags=flags)
+    inp = make_inputs(wl)
+    y = _stream(inp, nb, flags)
+    ref = oracle.np_decode(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, nb, phi, norm=norm)
+    err = slice_error(y, ref)
+    print("PARITY decode N=%d nb=%d d=%d phi=%d dtype=%d norm=%d err=%.3e"
+          % (N, nb, d, phi, dtype, norm, err))
+    assert np.all(np.isfinite(y))
+    assert err <= TOL[dtype]
+
+
+def test_decode_matches_chunkwise_forward_on_gpu():
+    """The streamed outputs and the chunkwise causal forward (blocked path) of
+    the same inputs agree to the bf16 gate."""
+    wl = custom_workload(2, 2, 64, (1, 1, 256), (1, 1, 64), PHI_ELU1, DTYPE_BF16, index=41,
+                         flags=FLAG_CAUSAL | FLAG_NO_NORM)
+    inp = make_inputs(wl)
+    y_dec = _stream(inp, 64, wl.flags)
+    q, k, v, w = to_device(inp)
+    out = torch.empty_like(q)
+    m.mhla_forward_ex(q, k, v, w, out, (wl.grid, wl.block), wl.phi, wl.flags)
+    torch.cuda.synchronize()
+    err = slice_error(y_dec, to_f64(out))
+    print("PARITY decode vs chunkwise forward err=%.3e" % err)
+    assert err <= TOL[DTYPE_BF16]

@@ -18,8 +18,8 @@ MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_B
 MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL = 1, 2
 
 EXPORTED_SYMBOLS = (
-    "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward", "mhla_validate",
-    "mhla_plan",
+    "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward",
+    "mhla_decode_state_bytes", "mhla_decode_step", "mhla_validate", "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
     "mhla_error_string", "mhla_last_error", "mhla_release",
 )
@@ -75,6 +75,11 @@ def load_library():
     lib.mhla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip,
                                   ip, vp]
     lib.mhla_backward.restype = ip
+    lib.mhla_decode_state_bytes.argtypes = [ip, ip, ip, ip]
+    lib.mhla_decode_state_bytes.restype = ctypes.c_size_t
+    lib.mhla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip,
+                                     vp]
+    lib.mhla_decode_step.restype = ip
     lib.mhla_plan_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
     lib.mhla_plan_ex.restype = ip
     lib.mhla_lb_init.argtypes = [bsp, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t]
@@ -231,6 +236,38 @@ def mhla_backward(Q, K, V, Wmix, dY, dQ, dK, dV, dWmix, block_shape, phi_kind, f
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())
     return dQ, dK, dV, dWmix
+
+
+def mhla_decode_state_bytes(B, H, d, M) -> int:
+    return int(load_library().mhla_decode_state_bytes(B, H, d, M))
+
+
+def mhla_decode_step(q, k, v, Wmix, y, state, M, nb, t, phi_kind, flags=0, stream=None):
+    """One streaming step: q, k, v, y are [B, H, d] GPU tensors (the token at
+    position t of every slice); state is a GPU buffer of
+    mhla_decode_state_bytes(B, H, d, M) bytes."""
+    import torch
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("Wmix", Wmix), ("y", y)):
+        if not (isinstance(t_, torch.Tensor) and t_.is_cuda and t_.is_contiguous()):
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or y.shape != q.shape:
+        raise ValueError("q, k, v, y must share one [B, H, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or y.dtype != q.dtype:
+        raise ValueError("q, k, v, y must share one dtype")
+    if Wmix.dtype != torch.float32:
+        raise ValueError("Wmix must be float32")
+    if not (isinstance(state, torch.Tensor) and state.is_cuda and state.is_contiguous()):
+        raise ValueError("state must be a contiguous GPU tensor")
+    B, H, d = q.shape
+    if state.numel() * state.element_size() < mhla_decode_state_bytes(B, H, d, M):
+        raise ValueError("state is smaller than mhla_decode_state_bytes")
+    rc = load_library().mhla_decode_step(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), Wmix.data_ptr(), y.data_ptr(), state.data_ptr(),
+        B, H, d, int(M), int(nb), int(t), int(phi_kind), _dtype_code(q), int(flags),
+        _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return y
 
 
 def mhla_forward(Q, K, V, Wmix, out, block_shape, phi_kind, stream=None):

@@ -1,0 +1,126 @@
+// k_decode.hpp -- incremental (streaming) inference of the causal form, one
+// token per (batch, head) slice per call: "MHLA: Restoring Expressivity of
+// Linear Attention via Token-Level Multi-Head", App. C ("Causal inference").
+//
+// The sequence is cut into chunks of nb tokens; token t sits in chunk
+// i = t / nb.  Per slice the state keeps, in fp32,
+//   slots 0 .. M-1 : the chunk summaries [S_b | z_b] (rows f = key feature,
+//                    columns c = value column, column d = z), finished for
+//                    b < i and running for b = i;
+//   slot M         : the prefix mixture [P_i | p_i] = sum_{b<i} W[i,b] [S_b | z_b],
+//                    formed once when chunk i starts.
+// One call:
+//   t starts chunk i : P_i = sum_{b<i} W[i,b] S_b (the finished summaries are
+//                      fixed from then on) and the running summary restarts;
+//   every token      : S_i += phi(k_t) [v_t | 1]^T;
+//   readout          : [n | den] = phi(q_t) (P_i + W[i,i] S_i),
+//                      y_t = n / den (0 for den = 0), or n without the normaliser.
+// This equals the chunkwise causal forward at position t.  The cost per token
+// is O(d^2) (plus O(i d^2) once per chunk), independent of t.
+#pragma once
+
+#include "mhla_common.hpp"
+
+namespace mhla {
+
+constexpr int kDecThreads = 256;
+
+inline size_t decode_state_elems(int d, int M) {
+  return (size_t)(M + 1) * (size_t)d * (size_t)(d + 1);
+}
+
+inline size_t decode_lds_bytes(int d) {
+  const size_t E = (size_t)d * (d + 1);
+  return (E + 3 * (size_t)d + 2 * (size_t)(d + 1)) * sizeof(float);
+}
+
+// grid = B*H, block = 256.  q, k, v, y: [B*H, d]; W: [H, M, M]; state:
+// [B*H][M+1][d][d+1] fp32.  Calls for t = 0, 1, 2, ... in order on one stream.
+template <typename T, int PHI>
+__global__ __launch_bounds__(kDecThreads) void k_decode_step(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ W, T* __restrict__ y, float* __restrict__ state, int H, int d, int M,
+    int nb, int t, int norm) {
+  extern __shared__ float smd[];
+  const int C = d + 1;
+  const int E = d * C;
+  float* comb = smd;        // [d][C]: P_i + W[i,i] S_i after this token's update
+  float* pq = comb + E;     // phi(q_t)
+  float* pk = pq + d;       // phi(k_t)
+  float* vv = pk + d;       // [v_t | 1]
+  float* red = vv + C;      // [n | den]
+  const int tid = threadIdx.x;
+  const long slice = blockIdx.x;
+  const int h = (int)(slice % H);
+  const int i = t / nb, j = t - (t / nb) * nb;
+  float* sums = state + (size_t)slice * (M + 1) * E;
+  float* prefix = sums + (size_t)M * E;
+  float* Si = sums + (size_t)i * E;
+  const float* Wi = W + ((size_t)h * M + i) * M;
+  const float wii = Wi[i];
+
+  for (int f = tid; f < d; f += kDecThreads) {
+    pq[f] = phi_apply(PHI, Elt<T>::load(q + slice * d + f));
+    pk[f] = phi_apply(PHI, Elt<T>::load(k + slice * d + f));
+    vv[f] = Elt<T>::load(v + slice * d + f);
+  }
+  if (tid == 0) vv[d] = 1.0f;
+  __syncthreads();
+
+  for (int e = tid; e < E; e += kDecThreads) {
+    const int f = e / C, c = e - (e / C) * C;
+    float P, s_old;
+    if (j == 0) {  // chunk i starts: mix the finished chunks once, restart S_i
+      P = 0.0f;
+      for (int b = 0; b < i; ++b) P = fmaf(Wi[b], sums[(size_t)b * E + e], P);
+      prefix[e] = P;
+      s_old = 0.0f;
+    } else {
+      P = prefix[e];
+      s_old = Si[e];
+    }
+    const float s_new = fmaf(pk[f], vv[c], s_old);
+    Si[e] = s_new;
+    comb[e] = fmaf(wii, s_new, P);
+  }
+  __syncthreads();
+
+  for (int c = tid; c < C; c += kDecThreads) {
+    float acc = 0.0f;
+    for (int f = 0; f < d; ++f) acc = fmaf(pq[f], comb[f * C + c], acc);
+    red[c] = acc;
+  }
+  __syncthreads();
+  for (int c = tid; c < d; c += kDecThreads) {
+    const float den = red[d];
+    const float val = !norm ? red[c] : den == 0.0f ? 0.0f : red[c] / den;
+    Elt<T>::store(y + slice * d + c, val);
+  }
+}
+
+template <typename T>
+int launch_decode_t(long slices, int H, int d, int M, int nb, int t, int phi, int norm,
+                    const T* q, const T* k, const T* v, const float* W, T* y, float* state,
+                    hipStream_t st) {
+  const size_t lds = decode_lds_bytes(d);
+  static bool attr_set[2][64] = {{false}};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const void* fn = phi == PHI_RELU ? reinterpret_cast<const void*>(&k_decode_step<T, PHI_RELU>)
+                                   : reinterpret_cast<const void*>(&k_decode_step<T, PHI_ELU1>);
+  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_set[phi][dev])) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+        hipSuccess)
+      return -1;
+    if (dev >= 0 && dev < 64) attr_set[phi][dev] = true;
+  }
+  if (phi == PHI_RELU)
+    k_decode_step<T, PHI_RELU><<<dim3((unsigned)slices), kDecThreads, lds, st>>>(
+        q, k, v, W, y, state, H, d, M, nb, t, norm);
+  else
+    k_decode_step<T, PHI_ELU1><<<dim3((unsigned)slices), kDecThreads, lds, st>>>(
+        q, k, v, W, y, state, H, d, M, nb, t, norm);
+  return 0;
+}
+
+}  // namespace mhla

@@ -23,6 +23,7 @@
 #include "k_pairs.hpp"
 #include "k_causal.hpp"
 #include "k_backward.hpp"
+#include "k_decode.hpp"
 
 namespace mhla {
 namespace {
@@ -345,6 +346,62 @@ int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix
                   void* stream) {
   return run_backward(Q, K, V, Wmix, dY, dQ, dK, dV, dWmix, B, H, N, d, block_shape, phi_kind,
                       dtype, flags, stream);
+}
+
+size_t mhla_decode_state_bytes(int B, int H, int d, int M) {
+  if (B <= 0 || H <= 0 || d <= 0 || M <= 0 || d > 128) return 0;
+  return (size_t)B * H * decode_state_elems(d, M) * sizeof(float);
+}
+
+int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix, void* y,
+                     void* state, int B, int H, int d, int M, int nb, int t, int phi_kind,
+                     int dtype, int flags, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || H <= 0 || d <= 0 || M <= 0 || nb <= 0)
+    return fail(MHLA_ERR_INVALID_ARG, "B=%d H=%d d=%d M=%d nb=%d: all must be positive", B, H, d,
+                M, nb);
+  if ((long)M * nb > 0x7fffffffL || t < 0 || (long)t >= (long)M * nb)
+    return fail(MHLA_ERR_INVALID_ARG, "t=%d is outside [0, M*nb) with M=%d nb=%d", t, M, nb);
+  if (phi_kind != MHLA_PHI_RELU && phi_kind != MHLA_PHI_ELU1)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown phi_kind %d", phi_kind);
+  if (dtype != MHLA_DTYPE_F32 && dtype != MHLA_DTYPE_BF16)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~(MHLA_FLAG_NO_NORM | MHLA_FLAG_CAUSAL))
+    return fail(MHLA_ERR_INVALID_ARG, "unknown option bits 0x%x", flags);
+  if (d > 128) return fail(MHLA_ERR_UNSUPPORTED, "d=%d > 128 is not supported", d);
+  if (dtype == MHLA_DTYPE_BF16 && d % 8 != 0)
+    return fail(MHLA_ERR_UNSUPPORTED, "bf16 needs d to be a multiple of 8 (d=%d)", d);
+  if ((long)B * H > 0x7fffffffL || (long)M * M * H > 0x7fffffffL)
+    return fail(MHLA_ERR_UNSUPPORTED, "too many slices or blocks");
+  if (!q || !k || !v || !Wmix || !y || !state)
+    return fail(MHLA_ERR_INVALID_ARG, "a pointer is NULL");
+  const void* ptrs[6] = {q, k, v, Wmix, y, state};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+      return fail(MHLA_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  const size_t eb = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+  const size_t tb = (size_t)B * H * d * eb;
+  const size_t sb = mhla_decode_state_bytes(B, H, d, M);
+  if (overlaps(y, tb, q, tb) || overlaps(y, tb, k, tb) || overlaps(y, tb, v, tb) ||
+      overlaps(y, tb, state, sb))
+    return fail(MHLA_ERR_ALIAS, "y overlaps q, k, v or the state");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int norm = (flags & MHLA_FLAG_NO_NORM) ? 0 : 1;
+  const long slices = (long)B * H;
+  int rc;
+  if (dtype == MHLA_DTYPE_F32)
+    rc = launch_decode_t<float>(slices, H, d, M, nb, t, phi_kind, norm, (const float*)q,
+                                (const float*)k, (const float*)v, Wmix, (float*)y, (float*)state,
+                                st);
+  else
+    rc = launch_decode_t<bf16_t>(slices, H, d, M, nb, t, phi_kind, norm, (const bf16_t*)q,
+                                 (const bf16_t*)k, (const bf16_t*)v, Wmix, (bf16_t*)y,
+                                 (float*)state, st);
+  if (rc != 0) return fail(MHLA_ERR_HIP, "decode set-up failed (hipFuncSetAttribute)");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MHLA_OK;
 }
 
 int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
