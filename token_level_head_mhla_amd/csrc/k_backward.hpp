@@ -244,10 +244,23 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
   const int i0 = 16 * (blockIdx.x / nt), b0 = 16 * (blockIdx.x % nt);
   const bf16_t* arow = A + ((size_t)slice * M + min(i0 + s, M - 1)) * EP + 8 * grp;
   const bf16_t* brow = Bm + ((size_t)slice * M + min(b0 + s, M - 1)) * EP + 8 * grp;
-  f32x4_t acc = zero4();
-  for (int k = wave; k < NSTEP; k += kBlkWaves)
-    acc = mfma_bf16(*reinterpret_cast<const u16x8_t*>(arow + 32 * k),
-                    *reinterpret_cast<const u16x8_t*>(brow + 32 * k), acc);
+  // four independent accumulators, four steps' loads issued together
+  f32x4_t acc4[4] = {zero4(), zero4(), zero4(), zero4()};
+  int k = wave;
+  for (; k + 3 * kBlkWaves < NSTEP; k += 4 * kBlkWaves) {
+    u16x8_t av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = *reinterpret_cast<const u16x8_t*>(arow + 32 * (k + u * kBlkWaves));
+      bv[u] = *reinterpret_cast<const u16x8_t*>(brow + 32 * (k + u * kBlkWaves));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc4[u] = mfma_bf16(av[u], bv[u], acc4[u]);
+  }
+  for (; k < NSTEP; k += kBlkWaves)
+    acc4[0] = mfma_bf16(*reinterpret_cast<const u16x8_t*>(arow + 32 * k),
+                        *reinterpret_cast<const u16x8_t*>(brow + 32 * k), acc4[0]);
+  const f32x4_t acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   // acc lane (s, grp) element r = P[i0 + 4grp + r][b0 + s]
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][(4 * grp + r) * 16 + s] = acc[r];
@@ -266,9 +279,16 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
   const long MM = (long)M * M;
   if (e >= (long)H * MM) return;
   const long h = e / MM, ib = e - h * MM;
-  float acc = 0.0f;
-  for (int b = 0; b < B; ++b) acc += P[((long)b * H + h) * MM + ib];
-  dW[e] = acc;
+  // eight partial sums in a fixed order (batch items b, b+8, ...), so that
+  // eight loads are in flight at a time
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int b = 0;
+  for (; b + 8 <= B; b += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += P[((long)(b + u) * H + h) * MM + ib];
+  }
+  for (int u = 0; b + u < B; ++u) acc[u] += P[((long)(b + u) * H + h) * MM + ib];
+  dW[e] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 // ---------------------------------------------------------------------------

@@ -424,10 +424,88 @@ inline size_t blocked_workspace(long slices, int M, int d) {
 
 // One mixing GEMM over all slices: St[slice][i] = sum_b coef(i, b) S[slice][b]
 // with the coefficient chosen by mode (kMixPlain, kMixCausal, kMixTransposed).
+// ---------------------------------------------------------------------------
+// Mixing for small M on the vector ALUs.  With M <= 16 the MFMA tiles of
+// k_mix_mfma (64 query blocks, 32 key blocks per step) are at most a quarter
+// used, and the mixing is bound by reading S and writing S~ once, not by its
+// 2*M^2 flops per entry (measured: 4.4 TB/s at M = 16; at M = 32 the flops
+// already make it slower than the MFMA GEMM).  grid = (EP / 512, slices), block = 256: each thread
+// owns two adjacent entries of every row, reads them for all M key blocks and
+// writes them for all M query blocks; the M x M coefficients (mode applied,
+// fp32) sit in LDS and are read as broadcasts.
+constexpr int kMixSmallM = 16;
+
+template <int EP, int MODE, int MMAX, typename OutT>
+__global__ __launch_bounds__(256) void k_mix_small(const bf16_t* __restrict__ S,
+                                                   const float* __restrict__ W,
+                                                   OutT* __restrict__ St, int M, int H) {
+  __shared__ __attribute__((aligned(16))) float sw[MMAX * MMAX];
+  const int tid = threadIdx.x;
+  const long slice = blockIdx.y;
+  const int h = (int)(slice % H);
+  const float* Wh = W + (size_t)h * M * M;
+  for (int e = tid; e < M * M; e += 256) {
+    const int i = e / M, b = e - (e / M) * M;
+    float c = MODE == kMixTransposed ? Wh[(size_t)b * M + i] : Wh[e];
+    if (MODE == kMixCausal && b >= i) c = 0.0f;
+    sw[i * MMAX + b] = c;
+  }
+  __syncthreads();
+  const int e0 = (blockIdx.x * 256 + tid) * 2;
+  if (e0 >= EP) return;  // after the only barrier
+  const bf16_t* src = S + (size_t)slice * M * EP + e0;
+  float x0[MMAX], x1[MMAX];
+#pragma unroll
+  for (int b = 0; b < MMAX; ++b) {
+    uint32_t u = 0u;
+    if (b < M) u = *reinterpret_cast<const uint32_t*>(src + (size_t)b * EP);
+    x0[b] = __uint_as_float(u << 16);
+    x1[b] = __uint_as_float(u & 0xffff0000u);
+  }
+  OutT* dst = St + (size_t)slice * M * EP + e0;
+#pragma unroll
+  for (int i = 0; i < MMAX; ++i) {
+    if (i >= M) break;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int b = 0; b < MMAX; b += 4) {
+      // four coefficients per LDS read (a broadcast); entries with b >= M are
+      // never set and never used
+      const f32x4_t c = *reinterpret_cast<const f32x4_t*>(sw + i * MMAX + b);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (b + u < M) {
+          a0 = fmaf(c[u], x0[b + u], a0);
+          a1 = fmaf(c[u], x1[b + u], a1);
+        }
+      }
+    }
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<float2*>(dst + (size_t)i * EP) = make_float2(a0, a1);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst + (size_t)i * EP) = pack2(a0, a1);
+    }
+  }
+}
+
+template <int EP, int MODE, typename OutT>
+void launch_mix_small(long slices, int H, int M, const bf16_t* S, const float* W, OutT* St,
+                      hipStream_t st) {
+  const dim3 grid((unsigned)((EP + 511) / 512), (unsigned)slices);
+  if (M <= 8)
+    k_mix_small<EP, MODE, 8, OutT><<<grid, 256, 0, st>>>(S, W, St, M, H);
+  else
+    k_mix_small<EP, MODE, kMixSmallM, OutT><<<grid, 256, 0, st>>>(S, W, St, M, H);
+}
+
 template <int DP, int MODE>
 void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St,
                   hipStream_t st) {
   using D = BlockedDims<DP>;
+  if (M <= kMixSmallM) {
+    launch_mix_small<D::EP, MODE, bf16_t>(slices, H, M, S, W, St, st);
+    return;
+  }
   const long xslices = (slices + 7) / 8 * 8;
   const int ib = mix_ib(M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + ib - 1) / ib));
@@ -451,6 +529,10 @@ template <int DP>
 void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, float* St,
                     hipStream_t st) {
   using D = BlockedDims<DP>;
+  if (M <= kMixSmallM) {
+    launch_mix_small<D::EP, kMixPlain, float>(slices, H, M, S, W, St, st);
+    return;
+  }
   const long xslices = (slices + 7) / 8 * 8;
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + 63) / 64));
   k_mix_mfma<D::EP, 64, kMixPlain, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
