@@ -110,16 +110,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
     const float scale = g.norm ? rd : 1.0f;
-    if (tq >= 0) {
-      bf16_t* nrow = dN + off + (size_t)tq * d;
+    {
+      f32x4_t gt[NT];
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
-        const int c = 16 * ct + 4 * grp;
-        if (c < d)
-          *reinterpret_cast<uint2*>(nrow + c) =
-              make_uint2(pack2(gv[ct][0] * scale, gv[ct][1] * scale),
-                         pack2(gv[ct][2] * scale, gv[ct][3] * scale));
-      }
+      for (int ct = 0; ct < NT; ++ct) gt[ct] = f32x4_t{gv[ct][0], gv[ct][1], gv[ct][2], gv[ct][3]};
+      store_row_tiles<NT>(tq >= 0 ? dN + off + (size_t)tq * d : nullptr, d, gt, scale, grp);
+    }
+    if (tq >= 0) {
       if (grp == 0) {
         dden[(size_t)slice * N + tq] = g.norm ? -dot * rd : 0.0f;
         rq[(size_t)slice * N + tq] = scale;

@@ -134,10 +134,7 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
   // consecutive features of value column 16ct + s.
   const int s = lane & 15, grp = lane >> 4;
   bf16_t* row = S + ((size_t)slice * g.M + b) * EP;
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt)
-    *reinterpret_cast<uint2*>(row + (16 * ct + s) * DP + 16 * kt + 4 * grp) =
-        make_uint2(pack2(acc[kt][0], acc[kt][1]), pack2(acc[kt][2], acc[kt][3]));
+  store_row_tiles<NT>(row + (16 * ct + s) * DP, DP, acc, 1.0f, grp);
   if (ct == 0 && s == 0) {
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt)
@@ -303,14 +300,18 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
     const int i = i0 + IW * wi + 16 * c + s;
     if (i < M) {
       OutT* row = St + ((size_t)slice * M + i) * EP + e0 + EW * we;
+      if constexpr (PREC) {
 #pragma unroll
-      for (int a = 0; a < AT; ++a) {
-        if constexpr (PREC)
-          *reinterpret_cast<f32x4_t*>(row + 16 * a + 4 * grp) = acc[a][c];
-        else
-          *reinterpret_cast<uint2*>(row + 16 * a + 4 * grp) =
-              make_uint2(pack2(acc[a][c][0], acc[a][c][1]), pack2(acc[a][c][2], acc[a][c][3]));
+        for (int a = 0; a < AT; ++a) *reinterpret_cast<f32x4_t*>(row + 16 * a + 4 * grp) = acc[a][c];
       }
+    }
+    if constexpr (!PREC) {
+      // every lane joins the exchange of the 16-byte stores
+      f32x4_t t[AT];
+#pragma unroll
+      for (int a = 0; a < AT; ++a) t[a] = acc[a][c];
+      store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 + EW * we : nullptr, EW, t,
+                          1.0f, grp);
     }
   }
 }
@@ -381,16 +382,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
       for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
       const float den = __shfl(oz[0], s);
       const float rd = out_scale(g, den);
-      if (tq[u] >= 0) {
-        bf16_t* yrow = Y + off + (size_t)tq[u] * d;
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const int c = 16 * ct + 4 * grp;
-          if (c < d)
-            *reinterpret_cast<uint2*>(yrow + c) = make_uint2(pack2(o[ct][0] * rd, o[ct][1] * rd),
-                                                             pack2(o[ct][2] * rd, o[ct][3] * rd));
-        }
-      }
+      store_row_tiles<NT>(tq[u] >= 0 ? Y + off + (size_t)tq[u] * d : nullptr, d, o, rd, grp);
     }
   }
 }

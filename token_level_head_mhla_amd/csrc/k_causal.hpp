@@ -137,16 +137,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
     }
 
     const float rd = out_scale(g, __shfl(oz[0], s));
-    if (qj < nb) {
-      bf16_t* yrow = Y + off + (size_t)(base + qj) * d;
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
-        const int c = 16 * ct + 4 * grp;
-        if (c < d)
-          *reinterpret_cast<uint2*>(yrow + c) = make_uint2(pack2(o[ct][0] * rd, o[ct][1] * rd),
-                                                           pack2(o[ct][2] * rd, o[ct][3] * rd));
-      }
-    }
+    store_row_tiles<NT>(qj < nb ? Y + off + (size_t)(base + qj) * d : nullptr, d, o, rd, grp);
   }
 }
 

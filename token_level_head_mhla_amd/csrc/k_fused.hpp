@@ -329,16 +329,7 @@ __global__ __launch_bounds__(64 * fused_waves(MM)) void k_fused(
     // row 0 of the z~ tile (lane s of group 0, element 0) is phi(q).z~_i
     const float den = __shfl(oz[0], s);
     const float rd = out_scale(g, den);
-    if (tok[u] >= 0) {
-      bf16_t* yrow = Y + off + (size_t)tok[u] * d;
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const int cl = 16 * c + 4 * grp;
-        if (cl < d)
-          *reinterpret_cast<uint2*>(yrow + cl) =
-              make_uint2(pack2(o[c][0] * rd, o[c][1] * rd), pack2(o[c][2] * rd, o[c][3] * rd));
-      }
-    }
+    store_row_tiles<NT>(tok[u] >= 0 ? Y + off + (size_t)tok[u] * d : nullptr, d, o, rd, grp);
   }
 }
 

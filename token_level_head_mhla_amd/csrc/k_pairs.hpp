@@ -205,16 +205,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
       if (c == dct) dv = o[u][c][dr];
     const float den = __shfl(dv, 16 * dg + s);
     const float rd = out_scale(g, den);
-    if (qtok[u] >= 0) {
-      bf16_t* yrow = Y + off + (size_t)qtok[u] * d;
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int cl = 16 * c + 4 * grp;
-        if (cl < d)
-          *reinterpret_cast<uint2*>(yrow + cl) = make_uint2(pack2(o[u][c][0] * rd, o[u][c][1] * rd),
-                                                            pack2(o[u][c][2] * rd, o[u][c][3] * rd));
-      }
-    }
+    store_row_tiles<CT>(qtok[u] >= 0 ? Y + off + (size_t)qtok[u] * d : nullptr, d, o[u], rd, grp);
   }
 }
 

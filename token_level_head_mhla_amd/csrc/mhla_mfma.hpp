@@ -119,4 +119,37 @@ __device__ __forceinline__ u16x8_t from_u2x2(uint2 a, uint2 b) {
   return __builtin_bit_cast(u16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
 }
 
+// Stores the accumulator tiles t[0..NT) of one output row -- tile j, lane
+// group g, element r holds entry 16j + 4g + r -- scaled by `scale`, as bf16 at
+// row[entry], with 16-byte stores: for each pair of tiles (j, j+1) the lane
+// groups g and g^1 swap halves, so that even groups hold 8 consecutive
+// entries of tile j and odd groups 8 of tile j+1 (a last odd tile is stored
+// with 8-byte stores).  Every lane takes part in the exchange; only the
+// stores are masked: nothing for row == nullptr, and no entry >= limit
+// (limit a multiple of 8; row 16-byte aligned).
+template <int NT>
+__device__ __forceinline__ void store_row_tiles(bf16_t* row, int limit, const f32x4_t (&t)[NT],
+                                                float scale, int grp) {
+  const bool odd = (grp & 1) != 0;
+#pragma unroll
+  for (int j = 0; j + 1 < NT; j += 2) {
+    const uint32_t a0 = pack2(t[j][0] * scale, t[j][1] * scale);
+    const uint32_t a1 = pack2(t[j][2] * scale, t[j][3] * scale);
+    const uint32_t b0 = pack2(t[j + 1][0] * scale, t[j + 1][1] * scale);
+    const uint32_t b1 = pack2(t[j + 1][2] * scale, t[j + 1][3] * scale);
+    // send what the partner group needs: even groups send tile j+1, odd tile j
+    const uint32_t r0 = __shfl_xor(odd ? a0 : b0, 16), r1 = __shfl_xor(odd ? a1 : b1, 16);
+    const u32x4_t v = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+    const int c = odd ? 16 * (j + 1) + 4 * (grp - 1) : 16 * j + 4 * grp;
+    if (row != nullptr && c < limit) *reinterpret_cast<u32x4_t*>(row + c) = v;
+  }
+  if constexpr (NT % 2 != 0) {
+    const int c = 16 * (NT - 1) + 4 * grp;
+    if (row != nullptr && c < limit)
+      *reinterpret_cast<uint2*>(row + c) =
+          make_uint2(pack2(t[NT - 1][0] * scale, t[NT - 1][1] * scale),
+                     pack2(t[NT - 1][2] * scale, t[NT - 1][3] * scale));
+  }
+}
+
 }  // namespace mhla
