@@ -69,6 +69,7 @@ BACKWARD_CASES = [
     (2, 2, (1, 8, 8), (1, 8, 8), 16, PHI_ELU1),      # M = 1, d = 16 padded to 32
     (2, 3, (4, 8, 8), (2, 4, 4), 48, PHI_RELU),      # 3-D blocks, d = 48
     (1, 2, (1, 16, 16), (1, 16, 8), 96, PHI_ELU1),   # 128-token blocks, d = 96
+    (1, 2, (1, 32, 32), (1, 2, 2), 32, PHI_ELU1),    # M = 256: large-M mixing, both directions
 ]
 
 

@@ -64,6 +64,8 @@ CAUSAL_CASES = [
     ((1, 1, 256), (1, 1, 256), 64, PHI_ELU1),   # one chunk of the maximum 256 tokens
     ((1, 1, 40), (1, 1, 1), 16, PHI_ELU1),      # one token per chunk, M = 40
     ((1, 1, 1200), (1, 1, 24), 96, PHI_RELU),   # M = 50, d = 96
+    ((1, 1, 8192), (1, 1, 32), 32, PHI_ELU1),   # M = 256: the large-M prefix mixing
+    ((1, 1, 4608), (1, 1, 16), 16, PHI_RELU),   # M = 288: a partial query-block tile
 ]
 
 
@@ -82,10 +84,11 @@ def test_causal_shapes(grid, block, d, phi, norm):
     assert err <= TOL[DTYPE_BF16]
 
 
-def test_causal_ignores_upper_triangle():
+@pytest.mark.parametrize("n,chunk", [(512, 64), (8192, 32)])
+def test_causal_ignores_upper_triangle(n, chunk):
     """W[i,b] for b > i never enters the causal form: the output is bit-identical
-    when those entries change."""
-    wl = custom_workload(2, 2, 64, (1, 1, 512), (1, 1, 64), PHI_ELU1, DTYPE_BF16, index=31,
+    when those entries change (M = 8, and M = 256 for the large-M mixing)."""
+    wl = custom_workload(2, 2, 64, (1, 1, n), (1, 1, chunk), PHI_ELU1, DTYPE_BF16, index=31,
                          flags=FLAG_CAUSAL)
     inp = make_inputs(wl)
     q, k, v, w = to_device(inp)

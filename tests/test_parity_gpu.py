@@ -107,6 +107,11 @@ BLOCKED_CASES = [
     ((4, 16, 16), (2, 4, 4), 64, PHI_ELU1),    # 3-D blocks, M = 32
     ((1, 1, 300), (1, 1, 5), 16, PHI_RELU),    # 1-D, M = 60, d = 16 padded to 32
     ((3, 8, 8), (1, 8, 8), 48, PHI_ELU1),      # whole-frame blocks, M = 3
+    # M >= 256: bf16 coefficients and the large-tile mixing GEMM
+    ((1, 32, 32), (1, 2, 2), 32, PHI_ELU1),    # M = 256, one query-block tile
+    ((1, 48, 48), (1, 2, 4), 16, PHI_RELU),    # M = 288: a partial query-block tile
+    ((4, 32, 32), (1, 4, 4), 64, PHI_ELU1),    # M = 256, d = 64 (the video entry width)
+    ((1, 32, 64), (1, 2, 4), 96, PHI_RELU),    # M = 256, d = 96
 ]
 
 

@@ -299,13 +299,14 @@ inline bool backward_supports(int dtype, int d, int M, long slices) {
 
 // Workspace: S, S~, dS~, dS ([slices][M][EP] bf16 each), the precise S~
 // ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden and rq ([slices][N]
-// fp32 each), P ([slices][M][M] fp32).
-inline size_t backward_workspace(long slices, int M, int N, int d) {
+// fp32 each), P ([slices][M][M] fp32), the mixing's coefficient scratch.
+inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   const size_t rows = (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
   const size_t al = 256;
   auto up = [&](size_t x) { return (x + al - 1) / al * al; };
   return 4 * up(rows) + 2 * up(rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
-         2 * up((size_t)slices * N * sizeof(float)) + up((size_t)slices * M * M * sizeof(float));
+         2 * up((size_t)slices * N * sizeof(float)) + up((size_t)slices * M * M * sizeof(float)) +
+         mix_coef_bytes(H, M);
 }
 
 template <int DP, int PHI>
@@ -334,6 +335,8 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   float* rq = reinterpret_cast<float*>(p);
   p += up((size_t)slices * N * sizeof(float));
   float* P = reinterpret_cast<float*>(p);
+  p += up((size_t)slices * M * M * sizeof(float));
+  bf16_t* wc = reinterpret_cast<bf16_t*>(p);
   static_assert(sizeof(bf16_t) == 2, "bf16");
   if (2 * up(rows * sizeof(bf16_t)) != 2 * rows * sizeof(bf16_t)) {
     // S~ must directly follow S (launch_summary_mix's layout): rows*2 bytes is
@@ -342,7 +345,7 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   }
   const unsigned nsl = (unsigned)slices;
   // 1. forward state
-  launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, S, 0, st);
+  launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, S, wc, 0, st);
   // 2. dn, dden
   const unsigned nbw = (unsigned)((M + kBlkWaves - 1) / kBlkWaves);
   k_bwd_dn<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, dY, dN, dden, rq, g, N, d);
@@ -350,7 +353,7 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(Q, dN, dSt, g, N, d,
                                                                            dden);
   // 4. dS = W^T-mixing of dS~
-  launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, st);
+  launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, wc, st);
   // 5. dW
   const unsigned nt = (unsigned)((M + 15) / 16);
   k_dw_partial<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);

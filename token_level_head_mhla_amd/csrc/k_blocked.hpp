@@ -7,6 +7,8 @@
 //                    transpose reads, fp32 accumulation, bf16 result)
 //   k_mix_mfma     : S~_i = sum_b W[i,b] S_b, z~_i = sum_b W[i,b] z_b, one
 //                    GEMM per (batch, head) slice over all d*d + d entries
+//                    (k_mix_small for M <= 16; k_mix_coef + k_mix_big, a
+//                    larger-tile GEMM on bf16 coefficients, for M >= 256)
 //   k_readout_mfma : Y_q = phi(Q_q) S~_i / (phi(Q_q) . z~_i), one wave per
 //                    query block, operands straight from global memory
 //
@@ -317,6 +319,195 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Mixing for many blocks (M >= kMixBigM, M % 32 == 0; plain, prefix and
+// transposed modes).  k_mix_coef first writes the coefficient matrix of the
+// mode in bf16 (Wc[h][i][b] = coef(i, b)), so that the GEMM streams two bf16
+// operands with unconditional 16-byte loads.  k_mix_big: one workgroup (4
+// waves) computes 256 query blocks x 128 entries of one slice; wave (we, wi)
+// owns 64 entries x 128 query blocks (32 accumulator tiles), which keeps it
+// within 256 registers, so two workgroups share a CU and one's barrier waits
+// overlap the other's MFMAs.  Key blocks advance 32 per step: the tiles of
+// step k + 2 are fetched into one of two register sets while step k runs, and
+// the tiles of step k + 1 are written to the other LDS buffer between the
+// MFMAs of step k (scheduling groups), with one barrier per step.  In the
+// prefix mode a tile stops at the last key block its rows can use.
+constexpr int kMixBigM = 256;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_mix_coef(const float* __restrict__ W,
+                                                  bf16_t* __restrict__ Wc, int M, long total) {
+  // grid = ceil(total / 1024), four consecutive entries per thread (M % 4 == 0)
+  const long e = 4 * ((long)blockIdx.x * 256 + threadIdx.x);
+  if (e >= total) return;
+  f32x4_t v;
+  if constexpr (MODE == kMixTransposed) {
+    const long mm = (long)M * M, h = e / mm, r = e - h * mm;
+    const int i = (int)(r / M), b = (int)(r - (r / M) * M);
+    const float* Wh = W + h * mm;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = Wh[(size_t)(b + q) * M + i];
+  } else {
+    v = *reinterpret_cast<const f32x4_t*>(W + e);
+    if constexpr (MODE == kMixCausal) {
+      const long r = e % ((long)M * M);
+      const int i = (int)(r / M), b = (int)(r - (r / M) * M);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (b + q >= i) v[q] = 0.0f;
+    }
+  }
+  *reinterpret_cast<uint2*>(Wc + e) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+}
+
+template <int A, int AT, int NWR>
+__device__ __forceinline__ void mix_big_groups() {
+  // NWR rounds of (4 MFMAs, 1 LDS write), then the remaining MFMAs
+  if constexpr (A < NWR) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+    mix_big_groups<A + 1, AT, NWR>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8 * AT - 4 * NWR, 0);
+  }
+}
+
+template <int EP, int MODE>
+__global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S,
+                                                    const bf16_t* __restrict__ Wc,
+                                                    bf16_t* __restrict__ St, int M, int H,
+                                                    long nslices) {
+  constexpr int TI = 256, TE = 128, KB = 32;
+  constexpr int EW = TE / 2, AT = EW / 16;  // entries and A tiles per wave
+  constexpr int SRS = TE + 8;               // S tile row stride (elements), rows = key blocks
+  constexpr int WRS = KB + 16;              // W tile row stride, rows = query blocks (measured
+                                            // fastest for the 16-byte fragment reads)
+  constexpr int nE = EP / TE;
+  constexpr int SCH = KB * TE / 8 / 256;  // 16-byte S chunks per thread per step (2)
+  constexpr int WCH = TI * KB / 8 / 256;  // 16-byte W chunks per thread per step (4)
+  static_assert(EP % TE == 0 && SCH * 8 * 256 == KB * TE && WCH * 8 * 256 == TI * KB, "tiles");
+  __shared__ __attribute__((aligned(16))) bf16_t sS[2][KB * SRS];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][TI * WRS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int we = wave & 1, wi = wave >> 1;
+  const int nI = (M + TI - 1) / TI;
+  const int per = nE * nI;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const long slice = (long)(j / per) * 8 + xcd;
+  if (slice >= nslices) return;  // before any barrier
+  const int rem = j - (j / per) * per;
+  const int e0 = (rem / nI) * TE, i0 = (rem - (rem / nI) * nI) * TI;
+  const int h = (int)(slice % H);
+  const bf16_t* Ss = S + (size_t)slice * M * EP;
+  const bf16_t* Wh = Wc + (size_t)h * M * M;
+  int nk = M / KB;
+  if constexpr (MODE == kMixCausal) {
+    // coefficients vanish for b >= i: stop below the tile's last row
+    const int last = i0 + TI - 1 < M - 1 ? i0 + TI - 1 : M - 1;
+    const int need = (last + KB - 1) / KB;
+    nk = need < nk ? need : nk;
+    nk = nk > 0 ? nk : 1;  // one all-zero step keeps the pipeline shape
+  }
+
+  f32x4_t acc[AT][8];
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = zero4();
+
+  // Two register sets, indexed by compile-time constants only (the step loop
+  // is unrolled by two), so that they stay in registers.
+  u32x4_t sr0[SCH], wr0[WCH], sr1[SCH], wr1[WCH];
+  auto gload = [&](u32x4_t (&sr)[SCH], u32x4_t (&wr)[WCH], int k) {
+    const int b0 = k * KB;
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (TE / 8), f = c % (TE / 8);
+      sr[u] = *reinterpret_cast<const u32x4_t*>(Ss + (size_t)(b0 + r) * EP + e0 + 8 * f);
+    }
+#pragma unroll
+    for (int u = 0; u < WCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (KB / 8), f = c % (KB / 8);
+      // rows past M are clamped in bounds; they feed outputs that are never
+      // stored (unconditional loads keep the wait counts exact)
+      const int i = i0 + r < M ? i0 + r : M - 1;
+      wr[u] = *reinterpret_cast<const u32x4_t*>(Wh + (size_t)i * M + b0 + 8 * f);
+    }
+  };
+  auto lstore = [&](const u32x4_t (&sr)[SCH], const u32x4_t (&wr)[WCH], int buf) {
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (TE / 8), f = c % (TE / 8);
+      *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) = sr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < WCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (KB / 8), f = c % (KB / 8);
+      *reinterpret_cast<u32x4_t*>(sW[buf] + r * WRS + 8 * f) = wr[u];
+    }
+  };
+  // A = S^T (rows e, contraction b via transpose reads), B = W^T (column i,
+  // the same b: W[i][8grp .. 8grp+7] is contiguous)
+  auto compute = [&](int buf) {
+    u16x8_t bw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf] + (128 * wi + 16 * c + s) * WRS + 8 * grp);
+#pragma unroll
+    for (int a = 0; a < AT; ++a) {
+      const u16x8_t af = lds_tr8(sS[buf], SRS, 0, EW * we + 16 * a, lane);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[a][c] = mfma_bf16(af, bw[c], acc[a][c]);
+    }
+  };
+  auto schedule = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x020, SCH + WCH, 0);  // global loads first
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * AT, 0);  // then the fragment reads
+    mix_big_groups<0, AT, SCH + WCH>();                          // LDS writes among MFMAs
+  };
+
+  // Step k reads LDS buffer k & 1; register set (k + 1) & 1 holds step k + 1
+  // and set k & 1 is refilled with step k + 2.  Loads and stores are
+  // unconditional (steps past the end repeat the last one, which is
+  // harmless), and no path leaves the loop from its middle, so every path
+  // into the loop head has the same loads in flight.
+  gload(sr0, wr0, 0);
+  gload(sr1, wr1, nk > 1 ? 1 : 0);
+  lstore(sr0, wr0, 0);
+  lds_barrier();
+  int k = 0;
+  for (; k + 1 < nk; k += 2) {
+    gload(sr0, wr0, k + 2 < nk ? k + 2 : nk - 1);
+    compute(0);
+    lstore(sr1, wr1, 1);
+    schedule();
+    lds_barrier();
+    gload(sr1, wr1, k + 3 < nk ? k + 3 : nk - 1);
+    compute(1);
+    lstore(sr0, wr0, 0);
+    schedule();
+    lds_barrier();
+  }
+  if (k < nk) compute(0);  // an odd last step, already in buffer 0
+  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int i = i0 + 128 * wi + 16 * c + s;
+    f32x4_t t[AT];
+#pragma unroll
+    for (int a = 0; a < AT; ++a) t[a] = acc[a][c];
+    store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 + EW * we : nullptr, EW, t,
+                        1.0f, grp);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Readout.  grid = (ceil(M / 4), slices), block = 256; wave w reads out query
 // block 4*blockIdx.x + w, 16 queries per step.  Y^T = S~_i^T phi(Q)^T with the
 // contraction split as features 32ks + 8grp .. +7 on both operands; the z~
@@ -409,9 +600,17 @@ inline size_t blocked_ws_elems(int d) {
   }
 }
 
-// Workspace: S and S~, [slices][M][EP] bf16 each.
-inline size_t blocked_workspace(long slices, int M, int d) {
-  return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
+// Bytes of the bf16 coefficient matrix of the large-M mixing (0 where that
+// kernel is not used), 256-byte aligned.
+inline size_t mix_coef_bytes(int H, int M) {
+  if (M < kMixBigM || M % 32 != 0) return 0;
+  return ((size_t)H * M * M * sizeof(bf16_t) + 255) / 256 * 256;
+}
+
+// Workspace: S and S~, [slices][M][EP] bf16 each, then the mixing's bf16
+// coefficients ([H][M][M], large M only).
+inline size_t blocked_workspace(long slices, int H, int M, int d) {
+  return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t) + mix_coef_bytes(H, M);
 }
 
 // One mixing GEMM over all slices: St[slice][i] = sum_b coef(i, b) S[slice][b]
@@ -490,15 +689,24 @@ void launch_mix_small(long slices, int H, int M, const bf16_t* S, const float* W
     k_mix_small<EP, MODE, kMixSmallM, OutT><<<grid, 256, 0, st>>>(S, W, St, M, H);
 }
 
+// wc: mix_coef_bytes(H, M) bytes of scratch for the large-M kernel (which is
+// used whenever those bytes are nonzero).
 template <int DP, int MODE>
 void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St,
-                  hipStream_t st) {
+                  bf16_t* wc, hipStream_t st) {
   using D = BlockedDims<DP>;
   if (M <= kMixSmallM) {
     launch_mix_small<D::EP, MODE, bf16_t>(slices, H, M, S, W, St, st);
     return;
   }
   const long xslices = (slices + 7) / 8 * 8;
+  if (mix_coef_bytes(H, M) != 0) {
+    const long tot = (long)H * M * M;
+    k_mix_coef<MODE><<<dim3((unsigned)((tot / 4 + 255) / 256)), 256, 0, st>>>(W, wc, M, tot);
+    const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 255) / 256));
+    k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+    return;
+  }
   const int ib = mix_ib(M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + ib - 1) / ib));
   if (ib == 64)
@@ -509,10 +717,10 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
 
 template <int DP>
 void launch_mix(long slices, int H, int M, const bf16_t* S, const float* W, bf16_t* St, int mode,
-                hipStream_t st) {
-  if (mode == kMixCausal) launch_mix_m<DP, kMixCausal>(slices, H, M, S, W, St, st);
-  else if (mode == kMixTransposed) launch_mix_m<DP, kMixTransposed>(slices, H, M, S, W, St, st);
-  else launch_mix_m<DP, kMixPlain>(slices, H, M, S, W, St, st);
+                bf16_t* wc, hipStream_t st) {
+  if (mode == kMixCausal) launch_mix_m<DP, kMixCausal>(slices, H, M, S, W, St, wc, st);
+  else if (mode == kMixTransposed) launch_mix_m<DP, kMixTransposed>(slices, H, M, S, W, St, wc, st);
+  else launch_mix_m<DP, kMixPlain>(slices, H, M, S, W, St, wc, st);
 }
 
 // The precise variant (fp32 S~, coefficients split in two bf16 parts), with
@@ -532,25 +740,33 @@ void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, 
 }
 
 // Summary and mixing launches shared by the plain and the causal readout; with
-// causal != 0 the mixing keeps only earlier chunks.  Returns S~ in the workspace.
+// causal != 0 the mixing keeps only earlier chunks.  S and S~ sit at the start
+// of ws; wc is the mixing's coefficient scratch.  Returns S~.
 template <int DP, int PHI>
 bf16_t* launch_summary_mix(long slices, int H, int N, int d, const Geo& g, const bf16_t* K,
-                           const bf16_t* V, const float* W, bf16_t* ws, int causal,
+                           const bf16_t* V, const float* W, bf16_t* ws, bf16_t* wc, int causal,
                            hipStream_t st) {
   using D = BlockedDims<DP>;
   bf16_t* S = ws;
   bf16_t* St = ws + (size_t)slices * g.M * D::EP;
   k_summary_mfma<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), 64 * D::NT, 0, st>>>(
       K, V, S, g, N, d, nullptr);
-  launch_mix<DP>(slices, H, g.M, S, W, St, causal ? kMixCausal : kMixPlain, st);
+  launch_mix<DP>(slices, H, g.M, S, W, St, causal ? kMixCausal : kMixPlain, wc, st);
   return St;
+}
+
+// The coefficient scratch of the blocked and causal paths: right after S~.
+template <int DP>
+bf16_t* blocked_coef_scratch(bf16_t* ws, long slices, int M) {
+  return ws + 2 * (size_t)slices * M * BlockedDims<DP>::EP;
 }
 
 template <int DP, int PHI>
 int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
                      const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
                      hipStream_t st) {
-  const bf16_t* St = launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, ws, 0, st);
+  const bf16_t* St = launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, ws,
+                                                 blocked_coef_scratch<DP>(ws, slices, g.M), 0, st);
   const unsigned nbw = (unsigned)((g.M + kBlkWaves - 1) / kBlkWaves);
   k_readout_mfma<DP, PHI><<<dim3(nbw, (unsigned)slices), kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
   return 0;

@@ -177,7 +177,8 @@ template <int DP, int PHI>
 int launch_causal_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
                     const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, bf16_t* ws,
                     hipStream_t st) {
-  const bf16_t* St = launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, ws, 1, st);
+  const bf16_t* St = launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, ws,
+                                                 blocked_coef_scratch<DP>(ws, slices, g.M), 1, st);
   return launch_readout_causal<DP, PHI>(slices, H, N, d, g, Q, K, V, W, St, Y, st);
 }
 
@@ -193,7 +194,7 @@ int launch_causal_p(long slices, int H, int N, int d, const Geo& g, const bf16_t
 }
 
 // Chunkwise causal forward: summaries, prefix mixing, causal readout.  The
-// workspace is the blocked path's (S and S~).
+// workspace is the blocked path's (S, S~ and the mixing coefficients).
 inline int launch_causal(long slices, int H, int N, int d, const Geo& g, int phi,
                          const bf16_t* Q, const bf16_t* K, const bf16_t* V, const float* W,
                          bf16_t* Y, bf16_t* ws, hipStream_t st) {

@@ -142,7 +142,7 @@ size_t workspace_for(const Problem& p, int path) {
     const size_t L = (size_t)p.d * p.d + p.d;
     return 2 * (size_t)p.slices() * p.g.M * L * sizeof(float);
   }
-  if (path == MHLA_PATH_BLOCKED) return blocked_workspace(p.slices(), p.g.M, p.d);
+  if (path == MHLA_PATH_BLOCKED) return blocked_workspace(p.slices(), p.H, p.g.M, p.d);
   return 0;
 }
 
@@ -298,7 +298,7 @@ int run_backward(const void* Q, const void* K, const void* V, const float* W, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   void* ws = nullptr;
-  rc = get_workspace(backward_workspace(p.slices(), p.g.M, N, d), st, &ws);
+  rc = get_workspace(backward_workspace(p.slices(), H, p.g.M, N, d), st, &ws);
   if (rc != MHLA_OK) return rc;
   rc = launch_backward(p.slices(), B, H, N, d, p.g, phi, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, W, (const bf16_t*)dY, (bf16_t*)dQ, (bf16_t*)dK,
