@@ -158,16 +158,11 @@ int launch_readout_causal(long slices, int H, int N, int d, const Geo& g, const 
                           const bf16_t* K, const bf16_t* V, const float* W, const bf16_t* St,
                           bf16_t* Y, hipStream_t st) {
   const size_t lds = causal_lds<DP>(g.nb);
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_set[dev])) {
-    const void* fn = reinterpret_cast<const void*>(&k_readout_causal<DP, PHI>);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
-      return -1;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
+  static std::atomic<bool> attr_set[64];
+  if (lds > 64 * 1024 &&
+      lds_limit_once(reinterpret_cast<const void*>(&k_readout_causal<DP, PHI>), attr_set,
+                     160 * 1024) != 0)
+    return -1;
   k_readout_causal<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), kBlkThreads, lds, st>>>(
       Q, K, V, W, St, Y, g, H, N, d);
   return 0;

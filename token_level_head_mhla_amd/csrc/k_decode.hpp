@@ -103,17 +103,11 @@ int launch_decode_t(long slices, int H, int d, int M, int nb, int t, int phi, in
                     const T* q, const T* k, const T* v, const float* W, T* y, float* state,
                     hipStream_t st) {
   const size_t lds = decode_lds_bytes(d);
-  static bool attr_set[2][64] = {{false}};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
+  static std::atomic<bool> attr_set[2][64];
   const void* fn = phi == PHI_RELU ? reinterpret_cast<const void*>(&k_decode_step<T, PHI_RELU>)
                                    : reinterpret_cast<const void*>(&k_decode_step<T, PHI_ELU1>);
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_set[phi][dev])) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
-      return -1;
-    if (dev >= 0 && dev < 64) attr_set[phi][dev] = true;
-  }
+  if (lds > 64 * 1024 && lds_limit_once(fn, attr_set[phi == PHI_RELU ? 0 : 1], 160 * 1024) != 0)
+    return -1;
   if (phi == PHI_RELU)
     k_decode_step<T, PHI_RELU><<<dim3((unsigned)slices), kDecThreads, lds, st>>>(
         q, k, v, W, y, state, H, d, M, nb, t, norm);

@@ -351,16 +351,10 @@ template <int DP, int NBP, int MM, int PHI>
 int launch_fused_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
                    const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
   const size_t lds = FusedLayout<DP>::total(N, g.M);
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const void* fn = reinterpret_cast<const void*>(&k_fused<DP, NBP, MM, PHI>);
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) !=
-        hipSuccess)
-      return -1;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
+  static std::atomic<bool> attr_set[64];
+  if (lds_limit_once(reinterpret_cast<const void*>(&k_fused<DP, NBP, MM, PHI>), attr_set,
+                     (int)kLdsLimit) != 0)
+    return -1;
   FusedBases fb;
   for (int b = 0; b < kFusedMaxM; ++b) fb.b[b] = b < g.M ? g.blockbase(b) : 0;
   k_fused<DP, NBP, MM, PHI><<<dim3((unsigned)slices), dim3(64 * fused_waves(MM)), lds, st>>>(

@@ -249,16 +249,10 @@ template <int DK, int DO, int QB, int PHI>
 int launch_pairs_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* Q,
                    const bf16_t* K, const bf16_t* V, const float* W, bf16_t* Y, hipStream_t st) {
   const size_t lds = PairsLayout<DK, DO>::total(N, g.M);
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const void* fn = reinterpret_cast<const void*>(&k_pairs<DK, DO, QB, PHI>);
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
-      return -1;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
+  static std::atomic<bool> attr_set[64];
+  if (lds_limit_once(reinterpret_cast<const void*>(&k_pairs<DK, DO, QB, PHI>), attr_set,
+                     160 * 1024) != 0)
+    return -1;
   k_pairs<DK, DO, QB, PHI><<<dim3((unsigned)slices), dim3(kPairsThreads), lds, st>>>(
       Q, K, V, W, Y, g, H, N, d);
   return 0;

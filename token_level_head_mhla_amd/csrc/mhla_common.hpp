@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mhla {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
@@ -85,5 +87,20 @@ template <> struct Elt<bf16_t> {
   static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per device (the
+// attribute belongs to the function on each device).  `done` is the caller's
+// per-kernel flag array; threads that race here only repeat the call.
+// Returns 0, or -1 when the runtime refuses.
+inline int lds_limit_once(const void* fn, std::atomic<bool> (&done)[64], int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool tracked = dev >= 0 && dev < 64;
+  if (tracked && done[dev].load(std::memory_order_acquire)) return 0;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return -1;
+  if (tracked) done[dev].store(true, std::memory_order_release);
+  return 0;
+}
 
 }  // namespace mhla
