@@ -80,6 +80,48 @@ def test_backward_shapes(B, H, grid, block, d, phi, norm):
     _check(wl, 0 if norm else FLAG_NO_NORM)
 
 
+PAIRS_BACKWARD_CASES = [
+    # (B, H, grid, block, d, phi): blocks of at most 16 tokens take the
+    # token-pair backward (two kernels, no d x d state)
+    (2, 2, (1, 16, 16), (1, 4, 4), 72, PHI_ELU1),    # DiT-like: M = 16, d = 72 (16-wide tail)
+    (2, 3, (1, 12, 16), (1, 3, 4), 64, PHI_RELU),    # 12-token blocks, M = 16
+    (2, 2, (1, 6, 9), (1, 3, 3), 96, PHI_ELU1),      # 9-token blocks, M = 6, d = 96
+    (3, 2, (4, 8, 8), (1, 2, 4), 32, PHI_RELU),      # M = 32: four query blocks per wave, B = 3
+    (2, 2, (1, 4, 4), (1, 1, 1), 16, PHI_ELU1),      # one token per block, M = 16
+    (2, 2, (1, 8, 8), (1, 4, 4), 48, PHI_RELU),      # M = 4: waves without a block
+    (2, 2, (1, 10, 16), (1, 2, 8), 80, PHI_ELU1),    # d = 80, M = 10
+    (2, 2, (1, 9, 15), (1, 3, 5), 48, PHI_ELU1),     # odd M = 9, 15-token blocks
+]
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("B,H,grid,block,d,phi", PAIRS_BACKWARD_CASES)
+def test_pairs_backward_shapes(B, H, grid, block, d, phi, norm):
+    wl = custom_workload(B, H, d, grid, block, phi, DTYPE_BF16, index=hash((grid, d, 7)) % 951)
+    _check(wl, 0 if norm else FLAG_NO_NORM, "pairs")
+
+
+def test_pairs_backward_zero_denominator_rows():
+    """ReLU queries with no positive feature have a 0/0 row (returned as 0):
+    they must pass no gradient on the token-pair path either."""
+    wl = custom_workload(2, 2, 48, (1, 8, 8), (1, 4, 4), PHI_RELU, DTYPE_BF16, index=17)
+    inp = make_inputs(wl)
+    bits = inp.q.copy()
+    # make tokens 3 and 40 of every slice all-negative
+    bits[:, :, [3, 40], :] = bits[:, :, [3, 40], :] | np.uint16(0x8000)
+    inp.q = bits
+    gbits = make_upstream_grad(wl)
+    got = _run_backward(inp, gbits, 0)
+    G = bf16_bits_to_f32(gbits).astype(np.float64)
+    ref = oracle.np_backward(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, G, wl.grid, wl.block,
+                             wl.phi, norm=True, dw_abs=True)
+    errs = [slice_error(got[i], ref[i]) for i in range(3)] + [_head_error(got[3], ref[3], ref[4])]
+    print("PARITY pairs backward zero-den errs", errs)
+    assert np.all(got[0][:, :, [3, 40], :] == 0.0)
+    for e in errs:
+        assert e <= TOL[DTYPE_BF16]
+
+
 @pytest.mark.parametrize("name,B,H", [("deit_t", 8, 3), ("dit_xl2", 4, 16), ("hires", 1, 4)])
 def test_backward_workload_shapes(name, B, H):
     """The workloads' geometry and d with a reduced batch (the oracle's

@@ -23,6 +23,7 @@
 #include "k_pairs.hpp"
 #include "k_causal.hpp"
 #include "k_backward.hpp"
+#include "k_pairs_bwd.hpp"
 #include "k_decode.hpp"
 
 namespace mhla {
@@ -269,7 +270,9 @@ int run_backward(const void* Q, const void* K, const void* V, const float* W, co
   rc = check_flags(flags, &p);
   if (rc != MHLA_OK) return rc;
   if (p.causal()) return fail(MHLA_ERR_UNSUPPORTED, "the causal form has no backward pass here");
-  if (!backward_supports(dtype, d, p.g.M, p.slices()))
+  // blocks of at most 16 tokens: the token-pair order; otherwise the blocked one
+  const bool pairs = pairs_bwd_supports(dtype, d, p.g.M, p.g.nb, N);
+  if (!pairs && !backward_supports(dtype, d, p.g.M, p.slices()))
     return fail(MHLA_ERR_UNSUPPORTED, "the backward pass needs bf16 and d <= 96 (d=%d dtype=%d)",
                 d, dtype);
   const void* in[5] = {Q, K, V, W, dY};
@@ -298,9 +301,16 @@ int run_backward(const void* Q, const void* K, const void* V, const float* W, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   void* ws = nullptr;
-  rc = get_workspace(backward_workspace(p.slices(), H, p.g.M, N, d), st, &ws);
+  rc = get_workspace(pairs ? pairs_bwd_workspace(p.slices(), p.g.M, N, d)
+                           : backward_workspace(p.slices(), H, p.g.M, N, d),
+                     st, &ws);
   if (rc != MHLA_OK) return rc;
-  rc = launch_backward(p.slices(), B, H, N, d, p.g, phi, (const bf16_t*)Q, (const bf16_t*)K,
+  if (pairs)
+    rc = launch_pairs_backward(p.slices(), B, H, N, d, p.g, phi, (const bf16_t*)Q,
+                               (const bf16_t*)K, (const bf16_t*)V, W, (const bf16_t*)dY,
+                               (bf16_t*)dQ, (bf16_t*)dK, (bf16_t*)dV, dW, ws, st);
+  else
+    rc = launch_backward(p.slices(), B, H, N, d, p.g, phi, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, W, (const bf16_t*)dY, (bf16_t*)dQ, (bf16_t*)dK,
                        (bf16_t*)dV, dW, ws, st);
   if (rc != MHLA_OK) return fail(MHLA_ERR_HIP, "backward set-up failed");
