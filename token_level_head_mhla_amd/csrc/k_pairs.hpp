@@ -31,13 +31,28 @@ constexpr int kPairsThreads = 512;
 constexpr int kPairsWaves = kPairsThreads / 64;
 constexpr int kPairsMaxQB = 4;  // query blocks per wave (M <= 32)
 
-typedef short i16x4v_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// Feature operands of phi(K) phi(Q)^T in steps of 32 (lane group g holds
+// features 32 ks + 8g .. +7).  When DK is not a multiple of 32 the last step
+// (ks == ks_full) covers 16 features and groups 2 and 3 hold zeros, so that
+// every product is a 16x16x32 MFMA.  (A 16x16x16 MFMA for that tail, fed
+// from a 16x16x32 accumulation, gave wrong results in the backward kernels.)
+//   feat_operand: from global row `tok` (phi applied; features past d and
+//                 tok < 0 give 0)
+//   feat_row:     from an LDS row of phi values (pad columns already 0)
+template <int PHI>
+__device__ __forceinline__ u16x8_t feat_operand(const bf16_t* base, int tok, int d, int ks,
+                                                int ks_full, int grp) {
+  const int k0 = 32 * ks + 8 * grp;
+  const bool ok = tok >= 0 && k0 < d && (ks < ks_full || grp < 2);
+  u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+  if (ok) v = phi8<PHI>(*reinterpret_cast<const u32x4_t*>(base + (size_t)tok * d + k0));
+  return __builtin_bit_cast(u16x8_t, v);
+}
 
-__device__ __forceinline__ f32x4_t mfma_bf16_k16(const i16x4v_t& a, const i16x4v_t& b,
-                                                 const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4v_t, a),
-                                                   __builtin_bit_cast(i16x4v_t, b), c, 0, 0, 0);
+__device__ __forceinline__ u16x8_t feat_row(const bf16_t* lds, int row, int rs, int ks,
+                                            int ks_full, int grp) {
+  if (ks == ks_full && grp >= 2) return u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  return *reinterpret_cast<const u16x8_t*>(lds + (size_t)row * rs + 32 * ks + 8 * grp);
 }
 
 // DK: contraction width over features (multiple of 16: 32-steps plus an
@@ -47,8 +62,9 @@ template <int DK, int DO>
 struct PairsLayout {
   static constexpr int RSK = DK + 8;   // LDS row stride of phi(K)
   static constexpr int RSV = DO;       // LDS row stride of V (+ ones column)
-  static constexpr int KS = DK / 32;   // 32-feature steps
+  static constexpr int KS = DK / 32;   // full 32-feature steps
   static constexpr bool TAIL = (DK % 32) != 0;
+  static constexpr int KSF = KS + (TAIL ? 1 : 0);  // steps, the last one maybe half empty
   static constexpr int CT = DO / 16;   // O^T row tiles
   __host__ __device__ static size_t k_bytes(int N) { return (size_t)(N + 1) * RSK * 2; }
   __host__ __device__ static size_t v_bytes(int N) { return (size_t)(N + 1) * RSV * 2; }
@@ -63,8 +79,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const float* __restrict__ W, bf16_t* __restrict__ Y, Geo g, int H, int N, int d) {
   using L = PairsLayout<DK, DO>;
-  constexpr int RSK = L::RSK, RSV = L::RSV, KS = L::KS, CT = L::CT;
-  constexpr bool TAIL = L::TAIL;
+  constexpr int RSK = L::RSK, RSV = L::RSV, KS = L::KS, KSF = L::KSF, CT = L::CT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int M = g.M, nb = g.nb;
   const int tid = threadIdx.x;
@@ -105,29 +120,14 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
   // block, features 32ks + 8grp .. +7 (and 32KS + 4grp .. +3 for the tail).
   const int myq = (M - wave + kPairsWaves - 1) / kPairsWaves;  // query blocks of this wave
   int qtok[QB];
-  u16x8_t qf[QB][KS > 0 ? KS : 1];
-  i16x4v_t qt[QB];
+  u16x8_t qf[QB][KSF];
 #pragma unroll
   for (int u = 0; u < QB; ++u) {
     const int i = wave + u * kPairsWaves;
     const bool real = u < myq && s < nb;
     qtok[u] = real ? sB[i] + g.tokoff(s) : -1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int k0 = 32 * ks + 8 * grp;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (real && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)qtok[u] * d + k0);
-      qf[u][ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
-    }
-    if constexpr (TAIL) {
-      const int k0 = 32 * KS + 4 * grp;
-      uint2 v = make_uint2(0u, 0u);
-      if (real && k0 < d) v = *reinterpret_cast<const uint2*>(Q + off + (size_t)qtok[u] * d + k0);
-      const uint2 p = phi4<PHI>(v);
-      // features past d must be 0 in at least one operand: phi(0) = 1 for
-      // elu+1, so mask them here (phi(K) has zero pad columns anyway)
-      qt[u] = __builtin_bit_cast(i16x4v_t, k0 < d ? p : make_uint2(0u, 0u));
-    }
+    for (int ks = 0; ks < KSF; ++ks) qf[u][ks] = feat_operand<PHI>(Q + off, qtok[u], d, ks, KS, grp);
   }
 
   f32x4_t o[QB][CT];
@@ -160,16 +160,11 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
     }
     (void)b1;
     // phi(K) A operands of the two key blocks (row = key member s)
-    u16x8_t ka[2][KS > 0 ? KS : 1];
-    i16x4v_t kt[2];
+    u16x8_t ka[2][KSF];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[hb][ks] = *reinterpret_cast<const u16x8_t*>(sK + kr[hb] * RSK + 32 * ks + 8 * grp);
-      if constexpr (TAIL)
-        kt[hb] = *reinterpret_cast<const i16x4v_t*>(sK + kr[hb] * RSK + 32 * KS + 4 * grp);
-    }
+      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, kr[hb], RSK, ks, KS, grp);
     // V^T A operands: rows c = 16ct + s, keys {4grp..4grp+3} of b0 then of b1
     u16x8_t va[CT];
 #pragma unroll
@@ -183,8 +178,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
       for (int hb = 0; hb < 2; ++hb) {
         p[hb] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) p[hb] = mfma_bf16(ka[hb][ks], qf[u][ks], p[hb]);
-        if constexpr (TAIL) p[hb] = mfma_bf16_k16(kt[hb], qt[u], p[hb]);
+        for (int ks = 0; ks < KSF; ++ks) p[hb] = mfma_bf16(ka[hb][ks], qf[u][ks], p[hb]);
         p[hb] *= wb[hb][u];
       }
       // p[hb] lane (s, grp) element r = P'^T[key 4grp + r of block b0+hb][query s]

@@ -47,29 +47,6 @@ __device__ __forceinline__ u16x8_t acc8_row(const bf16_t* base, int row, int rs,
   return from_u2x2(lo, hi);
 }
 
-// Feature operands of P = phi(Q) phi(K)^T in steps of 32 (lane group g holds
-// features 32 ks + 8g .. +7).  When DK is not a multiple of 32 the last step
-// (ks == ks_full) covers 16 features: groups 2 and 3 hold zeros.  (All
-// products here are 16x16x32 MFMAs.)
-//   feat_operand: from global row `tok` (phi applied; features past d and
-//                 tok < 0 give 0)
-//   feat_row:     from an LDS row of phi values (pad columns already 0)
-template <int PHI>
-__device__ __forceinline__ u16x8_t feat_operand(const bf16_t* base, int tok, int d, int ks,
-                                                int ks_full, int grp) {
-  const int k0 = 32 * ks + 8 * grp;
-  const bool ok = tok >= 0 && k0 < d && (ks < ks_full || grp < 2);
-  u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-  if (ok) v = phi8<PHI>(*reinterpret_cast<const u32x4_t*>(base + (size_t)tok * d + k0));
-  return __builtin_bit_cast(u16x8_t, v);
-}
-
-__device__ __forceinline__ u16x8_t feat_row(const bf16_t* lds, int row, int rs, int ks,
-                                            int ks_full, int grp) {
-  if (ks == ks_full && grp >= 2) return u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  return *reinterpret_cast<const u16x8_t*>(lds + (size_t)row * rs + 32 * ks + 8 * grp);
-}
-
 // LDS of the key side: phi(Q), dnum as two bf16 parts (hi, lo), dden, W,
 // block bases.
 template <int DK, int DO>
