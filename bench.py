@@ -191,6 +191,21 @@ def main():
     return 0
 
 
+def roofline_of_call(gbs, tfs, alg_bytes, alg_flops):
+    """Roofline object of a whole call timed by events (several kernels): the
+    binding roofline is the larger of the HBM and bf16 MFMA fractions."""
+    hbm, mfma = gbs / HBM_PEAK_GBS, tfs / BF16_PEAK_TFLOPS
+    if hbm >= mfma:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s"}
+    r.update({"frac": round(max(hbm, mfma), 4), "traffic": None, "hbm_frac": round(hbm, 4),
+              "mfma_frac": round(mfma, 4), "algorithmic_bytes_per_launch": alg_bytes,
+              "algorithmic_flops_per_launch": alg_flops})
+    return r
+
+
 def backward_bench(args):
     """One step = one mhla_backward call (recompute of the forward state, then
     dQ, dK, dV, dW) on the workload's inputs and a seeded upstream gradient."""
@@ -235,11 +250,7 @@ def backward_bench(args):
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "dtype": "bf16",
         "config": {"workload": wl.name, "pass": "backward"},
-        "roofline": {"bound": "hbm" if gbs / HBM_PEAK_GBS >= tfs / BF16_PEAK_TFLOPS else "mfma",
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "algorithmic_flops_per_launch": alg_flops}}), flush=True)
+        "roofline": roofline_of_call(gbs, tfs, alg_bytes, alg_flops)}), flush=True)
     return 0
 
 
@@ -292,9 +303,10 @@ def decode_bench(args):
         "steps": wl.N, "warmup": wl.N, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "dtype": "bf16 in, fp32 state",
         "config": {"workload": wl.name, "pass": "decode", "sequences": wl.B, "heads": wl.H},
-        "roofline": {"bound": "hbm", "state_bytes_per_step": step_bytes,
-                     "achieved_GBs": round(step_bytes / (ms / 1e3) / 1e9, 1),
-                     "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}),
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "state_bytes_per_step": step_bytes}}),
           flush=True)
     return 0
 

@@ -58,16 +58,29 @@ __device__ __forceinline__ u16x8_t feat_row(const bf16_t* lds, int row, int rs, 
 // DK: contraction width over features (multiple of 16: 32-steps plus an
 // optional 16-step tail).  DO: rows of O^T (multiple of 16, > d: the row d
 // holds the denominator).
+// LDS rows are in member order: row b * nb + m holds the token of member m of
+// block b, so that the members of a block occupy consecutive rows (row N is
+// all zero).  Row strides of 16 (mod 32) elements keep the 16-row transpose
+// reads and the 16-byte row reads of one block free of bank conflicts.
+__host__ __device__ constexpr int pairs_rs(int w) { return (w + 15) / 32 * 32 + 16; }
+
+// Element offset of LDS row r at row stride rs: 8 more elements after every 8
+// rows, so that rows r and r + 8 of a block do not share banks in the 8- and
+// 16-byte row reads.
+__host__ __device__ constexpr int prow(int r, int rs) { return r * rs + (r >> 3) * 8; }
+// Elements of rows 0 .. N at stride rs.
+__host__ __device__ constexpr size_t prow_elems(int N, int rs) { return (size_t)prow(N + 1, rs) + 8; }
+
 template <int DK, int DO>
 struct PairsLayout {
-  static constexpr int RSK = DK + 8;   // LDS row stride of phi(K)
-  static constexpr int RSV = DO;       // LDS row stride of V (+ ones column)
+  static constexpr int RSK = pairs_rs(DK);  // LDS row stride of phi(K)
+  static constexpr int RSV = pairs_rs(DO);  // LDS row stride of V (+ ones column)
   static constexpr int KS = DK / 32;   // full 32-feature steps
   static constexpr bool TAIL = (DK % 32) != 0;
   static constexpr int KSF = KS + (TAIL ? 1 : 0);  // steps, the last one maybe half empty
   static constexpr int CT = DO / 16;   // O^T row tiles
-  __host__ __device__ static size_t k_bytes(int N) { return (size_t)(N + 1) * RSK * 2; }
-  __host__ __device__ static size_t v_bytes(int N) { return (size_t)(N + 1) * RSV * 2; }
+  __host__ __device__ static size_t k_bytes(int N) { return prow_elems(N, RSK) * 2; }
+  __host__ __device__ static size_t v_bytes(int N) { return prow_elems(N, RSV) * 2; }
   __host__ __device__ static size_t total(int N, int M) {
     return k_bytes(N) + v_bytes(N) + (size_t)M * M * 4 + (size_t)kPairsMaxM * 4;
   }
@@ -102,16 +115,18 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
   lds_barrier();
   {
     const int F8 = d >> 3;
-    const float inv8 = 1.0f / (float)F8;
+    const float inv8 = 1.0f / (float)F8, invnb = 1.0f / (float)nb;
     for (int it = tid; it < N * F8; it += kPairsThreads) {
-      const int t = (int)(((float)it + 0.5f) * inv8);
-      const int f = it - t * F8;
-      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + off + (size_t)it * 8);
-      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + off + (size_t)it * 8);
-      *reinterpret_cast<u32x4_t*>(sK + t * RSK + 8 * f) = phi8<PHI>(kr);
-      *reinterpret_cast<u32x4_t*>(sV + t * RSV + 8 * f) = vr;
+      const int row = (int)(((float)it + 0.5f) * inv8);
+      const int f = it - row * F8;
+      const int b = (int)(((float)row + 0.5f) * invnb);
+      const size_t src = off + (size_t)(sB[b] + g.tokoff(row - b * nb)) * d + 8 * f;
+      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + src);
+      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + src);
+      *reinterpret_cast<u32x4_t*>(sK + prow(row, RSK) + 8 * f) = phi8<PHI>(kr);
+      *reinterpret_cast<u32x4_t*>(sV + prow(row, RSV) + 8 * f) = vr;
     }
-    for (int t = tid; t < N; t += kPairsThreads) sV[t * RSV + d] = 0x3f80;  // bf16 1.0
+    for (int t = tid; t < N; t += kPairsThreads) sV[prow(t, RSV) + d] = 0x3f80;  // bf16 1.0
   }
   lds_barrier();
 
@@ -138,9 +153,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
 
   // key member s of a block: row of this lane for the phi(K) A operand;
   // key member 4grp + s/4: row supplied to the V^T transpose reads
-  const int koff = s < nb ? g.tokoff(s) : -1;
   const int vj = 4 * grp + (s >> 2);
-  const int voff = vj < nb ? g.tokoff(vj) : -1;
   for (int b0 = 0; b0 < M; b0 += 2) {
     const int b1 = b0 + 1;
     int kr[2], vr[2];
@@ -149,9 +162,8 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
     for (int hb = 0; hb < 2; ++hb) {
       const int b = b0 + hb;
       const bool real = b < M;
-      const int bb = real ? sB[b] : 0;
-      kr[hb] = (real && koff >= 0) ? bb + koff : N;
-      vr[hb] = (real && voff >= 0) ? bb + voff : N;
+      kr[hb] = (real && s < nb) ? b * nb + s : N;
+      vr[hb] = (real && vj < nb) ? b * nb + vj : N;
 #pragma unroll
       for (int u = 0; u < QB; ++u) {
         const int i = wave + u * kPairsWaves;
@@ -164,12 +176,12 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, kr[hb], RSK, ks, KS, grp);
+      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, prow(kr[hb], RSK), 1, ks, KS, grp);
     // V^T A operands: rows c = 16ct + s, keys {4grp..4grp+3} of b0 then of b1
     u16x8_t va[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c)
-      va[c] = lds_tr8_rows(sV + 16 * c + 4 * (s & 3), RSV, vr[0], vr[1]);
+      va[c] = lds_tr8_rows(sV + 16 * c + 4 * (s & 3), 1, prow(vr[0], RSV), prow(vr[1], RSV));
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       if (u >= myq) break;

@@ -51,10 +51,10 @@ __device__ __forceinline__ u16x8_t acc8_row(const bf16_t* base, int row, int rs,
 // block bases.
 template <int DK, int DO>
 struct PairsBwdLayout {
-  static constexpr int RSQ = DK + 8;  // phi(Q) rows
-  static constexpr int RSD = DO;      // dnum rows (columns d .. DO-1 zero)
-  __host__ __device__ static size_t q_bytes(int N) { return (size_t)(N + 1) * RSQ * 2; }
-  __host__ __device__ static size_t d_bytes(int N) { return (size_t)(N + 1) * RSD * 2; }
+  static constexpr int RSQ = pairs_rs(DK);  // phi(Q) rows (member order, as the forward's)
+  static constexpr int RSD = pairs_rs(DO);  // dnum rows (columns d .. DO-1 zero)
+  __host__ __device__ static size_t q_bytes(int N) { return prow_elems(N, RSQ) * 2; }
+  __host__ __device__ static size_t d_bytes(int N) { return prow_elems(N, RSD) * 2; }
   __host__ __device__ static size_t total(int N, int M) {
     return q_bytes(N) + 2 * d_bytes(N) + (size_t)(N + 1) * 4 + (size_t)M * M * 4 +
            (size_t)32 * 4;
@@ -107,18 +107,20 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
   for (int e = tid; e < M * M; e += kPairsThreads) sW[e] = W[(size_t)h * M * M + e];
   for (int b = tid; b < M; b += kPairsThreads) sB[b] = g.blockbase(b);
   lds_barrier();
-  {
+  {  // rows in member order (see PairsLayout)
     const int F8 = d >> 3;
-    const float inv8 = 1.0f / (float)F8;
+    const float inv8 = 1.0f / (float)F8, invnb = 1.0f / (float)nb;
     for (int it = tid; it < N * F8; it += kPairsThreads) {
-      const int t = (int)(((float)it + 0.5f) * inv8);
-      const int f = it - t * F8;
-      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + off + (size_t)it * 8);
-      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + off + (size_t)it * 8);
-      *reinterpret_cast<u32x4_t*>(sK + t * RSK + 8 * f) = phi8<PHI>(kr);
-      *reinterpret_cast<u32x4_t*>(sV + t * RSV + 8 * f) = vr;
+      const int row = (int)(((float)it + 0.5f) * inv8);
+      const int f = it - row * F8;
+      const int b = (int)(((float)row + 0.5f) * invnb);
+      const size_t src = off + (size_t)(sB[b] + g.tokoff(row - b * nb)) * d + 8 * f;
+      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + src);
+      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + src);
+      *reinterpret_cast<u32x4_t*>(sK + prow(row, RSK) + 8 * f) = phi8<PHI>(kr);
+      *reinterpret_cast<u32x4_t*>(sV + prow(row, RSV) + 8 * f) = vr;
     }
-    for (int t = tid; t < N; t += kPairsThreads) sV[t * RSV + d] = 0x3f80;  // bf16 1.0
+    for (int t = tid; t < N; t += kPairsThreads) sV[prow(t, RSV) + d] = 0x3f80;  // bf16 1.0
   }
   lds_barrier();
 
@@ -137,17 +139,14 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
 
   // key member s of a block: row of this lane for the row-operand reads; key
   // member 4grp + s/4: row supplied to the transpose reads
-  const int koff = s < nb ? g.tokoff(s) : -1;
   const int vj = 4 * grp + (s >> 2);
-  const int voff = vj < nb ? g.tokoff(vj) : -1;
   auto pair_rows = [&](int b0, int (&kr)[2], int (&vr)[2]) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int b = b0 + hb;
       const bool real = b < M;
-      const int bb = real ? sB[b] : 0;
-      kr[hb] = (real && koff >= 0) ? bb + koff : N;
-      vr[hb] = (real && voff >= 0) ? bb + voff : N;
+      kr[hb] = (real && s < nb) ? b * nb + s : N;
+      vr[hb] = (real && vj < nb) ? b * nb + vj : N;
     }
   };
 
@@ -164,11 +163,11 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, kr[hb], RSK, ks, KS, grp);
+      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, prow(kr[hb], RSK), 1, ks, KS, grp);
     u16x8_t va[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c)
-      va[c] = lds_tr8_rows(sV + 16 * c + 4 * (s & 3), RSV, vr[0], vr[1]);
+      va[c] = lds_tr8_rows(sV + 16 * c + 4 * (s & 3), 1, prow(vr[0], RSV), prow(vr[1], RSV));
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       if (u >= myq) break;
@@ -257,15 +256,15 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, kr[hb], RSK, ks, KS, grp);
+      for (int ks = 0; ks < KSF; ++ks) ka[hb][ks] = feat_row(sK, prow(kr[hb], RSK), 1, ks, KS, grp);
 #pragma unroll
-      for (int m = 0; m < CS; ++m) vb[hb][m] = acc8_row<CT>(sV, kr[hb], RSV, m, grp);
+      for (int m = 0; m < CS; ++m) vb[hb][m] = acc8_row<CT>(sV, prow(kr[hb], RSV), 1, m, grp);
     }
     // phi(K)^T A operands: rows f = 16ft + s, keys {4grp..4grp+3} of b0 then b1
     u16x8_t kT[FT];
 #pragma unroll
     for (int f = 0; f < FT; ++f)
-      kT[f] = lds_tr8_rows(sK + 16 * f + 4 * (s & 3), RSK, vr[0], vr[1]);
+      kT[f] = lds_tr8_rows(sK + 16 * f + 4 * (s & 3), 1, prow(vr[0], RSK), prow(vr[1], RSK));
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       if (u >= myq) break;
@@ -353,20 +352,30 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
     reinterpret_cast<u32x4_t*>(smem)[e] = u32x4_t{0u, 0u, 0u, 0u};
   for (int e = tid; e < M * M; e += kPairsThreads) sW[e] = W[(size_t)h * M * M + e];
   for (int b = tid; b < M; b += kPairsThreads) sB[b] = g.blockbase(b);
-  for (int t = tid; t <= N; t += kPairsThreads) sdd[t] = t < N ? dden[(size_t)slice * N + t] : 0.0f;
   lds_barrier();
-  {
+  {  // rows in member order (see PairsLayout)
+    const float invnb = 1.0f / (float)nb;
+    for (int row = tid; row <= N; row += kPairsThreads) {
+      float v = 0.0f;
+      if (row < N) {
+        const int b = (int)(((float)row + 0.5f) * invnb);
+        v = dden[(size_t)slice * N + sB[b] + g.tokoff(row - b * nb)];
+      }
+      sdd[row] = v;
+    }
     const int F8 = d >> 3;
     const float inv8 = 1.0f / (float)F8;
     for (int it = tid; it < N * F8; it += kPairsThreads) {
-      const int t = (int)(((float)it + 0.5f) * inv8);
-      const int f = it - t * F8;
-      const u32x4_t qr = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)it * 8);
-      const u32x4_t nr = *reinterpret_cast<const u32x4_t*>(dN + off + (size_t)it * 8);
-      const u32x4_t lr = *reinterpret_cast<const u32x4_t*>(dNlo + off + (size_t)it * 8);
-      *reinterpret_cast<u32x4_t*>(sQ + t * RSQ + 8 * f) = phi8<PHI>(qr);
-      *reinterpret_cast<u32x4_t*>(sD + t * RSD + 8 * f) = nr;
-      *reinterpret_cast<u32x4_t*>(sDl + t * RSD + 8 * f) = lr;
+      const int row = (int)(((float)it + 0.5f) * inv8);
+      const int f = it - row * F8;
+      const int b = (int)(((float)row + 0.5f) * invnb);
+      const size_t src = off + (size_t)(sB[b] + g.tokoff(row - b * nb)) * d + 8 * f;
+      const u32x4_t qr = *reinterpret_cast<const u32x4_t*>(Q + src);
+      const u32x4_t nr = *reinterpret_cast<const u32x4_t*>(dN + src);
+      const u32x4_t lr = *reinterpret_cast<const u32x4_t*>(dNlo + src);
+      *reinterpret_cast<u32x4_t*>(sQ + prow(row, RSQ) + 8 * f) = phi8<PHI>(qr);
+      *reinterpret_cast<u32x4_t*>(sD + prow(row, RSD) + 8 * f) = nr;
+      *reinterpret_cast<u32x4_t*>(sDl + prow(row, RSD) + 8 * f) = lr;
     }
   }
   lds_barrier();
@@ -393,13 +402,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
     }
   }
 
-  const int qoff = s < nb ? g.tokoff(s) : -1;
   const int vj = 4 * grp + (s >> 2);
-  const int voff = vj < nb ? g.tokoff(vj) : -1;
-  // this lane's output rows of P and dA: query members 4grp + r
-  int roff[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) roff[r] = 4 * grp + r < nb ? g.tokoff(4 * grp + r) : -1;
 
   f32x4_t dv[QB][FT], dk[QB][FT];
 #pragma unroll
@@ -413,22 +416,23 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
     for (int hb = 0; hb < 2; ++hb) {
       const int i = i0 + hb;
       const bool real = i < M;
-      const int bb = real ? sB[i] : 0;
-      qr[hb] = (real && qoff >= 0) ? bb + qoff : N;
-      qv[hb] = (real && voff >= 0) ? bb + voff : N;
+      qr[hb] = (real && s < nb) ? i * nb + s : N;
+      qv[hb] = (real && vj < nb) ? i * nb + vj : N;
+      // this lane's output rows of P and dA: query members 4grp + r
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dd[hb][r] = (real && roff[r] >= 0) ? sdd[bb + roff[r]] : 0.0f;
+      for (int r = 0; r < 4; ++r)
+        dd[hb][r] = (real && 4 * grp + r < nb) ? sdd[i * nb + 4 * grp + r] : 0.0f;
     }
     // row operands (query member s): phi(Q) over features, dnum over values
     u16x8_t qa[2][KSF], na[2][CS], nl[2][CS];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int ks = 0; ks < KSF; ++ks) qa[hb][ks] = feat_row(sQ, qr[hb], RSQ, ks, KS, grp);
+      for (int ks = 0; ks < KSF; ++ks) qa[hb][ks] = feat_row(sQ, prow(qr[hb], RSQ), 1, ks, KS, grp);
 #pragma unroll
       for (int m = 0; m < CS; ++m) {
-        na[hb][m] = acc8_row<CT>(sD, qr[hb], RSD, m, grp);
-        nl[hb][m] = acc8_row<CT>(sDl, qr[hb], RSD, m, grp);
+        na[hb][m] = acc8_row<CT>(sD, prow(qr[hb], RSD), 1, m, grp);
+        nl[hb][m] = acc8_row<CT>(sDl, prow(qr[hb], RSD), 1, m, grp);
       }
     }
     // transposed operands: rows c (dnum^T) and f (phi(Q)^T) = 16t + s,
@@ -436,8 +440,8 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
     u16x8_t nT[FT], qT[FT];
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      nT[f] = lds_tr8_rows(sD + 16 * f + 4 * (s & 3), RSD, qv[0], qv[1]);
-      qT[f] = lds_tr8_rows(sQ + 16 * f + 4 * (s & 3), RSQ, qv[0], qv[1]);
+      nT[f] = lds_tr8_rows(sD + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSD), prow(qv[1], RSD));
+      qT[f] = lds_tr8_rows(sQ + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSQ), prow(qv[1], RSQ));
     }
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
