@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="deit_t")
     ap.add_argument("--path", default="auto",
-                    choices=["auto", "generic", "fused", "pairs", "blocked"])
+                    choices=["auto", "generic", "fused", "pairs", "blocked", "columns"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -95,14 +95,15 @@ def main():
     wl = WORKLOADS[args.workload]
     path = {"auto": m.MHLA_PATH_AUTO, "generic": m.MHLA_PATH_GENERIC,
             "fused": m.MHLA_PATH_FUSED, "pairs": m.MHLA_PATH_PAIRS,
-            "blocked": m.MHLA_PATH_BLOCKED}[args.path]
+            "blocked": m.MHLA_PATH_BLOCKED, "columns": m.MHLA_PATH_COLUMNS}[args.path]
     shape = (wl.grid, wl.block)
     if path == m.MHLA_PATH_AUTO:
         path = m.mhla_plan_ex(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi,
                               wl.dtype, wl.flags)
-    path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked"}[path]
+    path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked", 5: "columns"}[path]
     kernels = {1: ["k_summary_valu", "k_mix_valu", "k_readout_valu"], 2: ["k_fused"],
-               3: ["k_pairs"], 4: ["k_summary_mfma", "k_mix_mfma", "k_readout_mfma"]}[path]
+               3: ["k_pairs"], 4: ["k_summary_mfma", "k_mix_mfma", "k_readout_mfma"],
+               5: ["k_cols"]}[path]
     if wl.causal:
         kernels = ["k_summary_mfma", "k_mix_mfma", "k_readout_causal"]
 
@@ -313,7 +314,8 @@ def decode_bench(args):
 
 # Sources that define each roofline kernel; a committed byte count applies only
 # while these files are unchanged.
-KERNEL_SOURCES = {"k_fused": ["k_fused.hpp", "mhla_mfma.hpp", "mhla_common.hpp"]}
+KERNEL_SOURCES = {"k_fused": ["k_fused.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+                  "k_cols": ["k_cols.hpp", "mhla_mfma.hpp", "mhla_common.hpp"]}
 
 
 def measured_traffic(kernel, workload):

@@ -70,7 +70,12 @@ enum {
   MHLA_PATH_GENERIC = 1,    /* summary -> mixing -> readout, three kernels   */
   MHLA_PATH_FUSED = 2,      /* one workgroup per slice, summaries kept in LDS */
   MHLA_PATH_PAIRS = 3,      /* token-pair form of Eq. 5, no summaries        */
-  MHLA_PATH_BLOCKED = 4     /* summary, mixing GEMM, readout on bf16 MFMA     */
+  MHLA_PATH_BLOCKED = 4,    /* summary, mixing GEMM, readout on bf16 MFMA     */
+  MHLA_PATH_COLUMNS = 5     /* one workgroup per (slice, 16 value columns):
+                               summaries, mixing and readout on chip; bf16,
+                               d <= 64, M <= 64, blocks of <= 256 tokens
+                               (output column c needs only column c of every
+                               S_b, plus z_b).  Never picked by AUTO.       */
 };
 
 /* Option bits for mhla_forward_ex (any combination). */

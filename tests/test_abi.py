@@ -96,6 +96,40 @@ def test_plan_and_workspace():
     assert m.mhla_plan(0, 1, 64, 16, m.BlockShape.make((8, 8), (4, 4)), 0, 0) < 0
 
 
+def test_columns_path_host_checks():
+    """The column-split path keeps everything on chip (no workspace), takes
+    bf16 with d <= 64, M <= 64 and blocks of at most 256 tokens, and is never
+    the automatic choice."""
+    wl = WORKLOADS["hires"]
+    bs = m.BlockShape.make(wl.grid, wl.block)
+    assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) == m.MHLA_PATH_BLOCKED
+    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_COLUMNS) == 0
+    for name in WORKLOADS:
+        w = WORKLOADS[name]
+        b = m.BlockShape.make(w.grid, w.block)
+        assert m.mhla_plan_ex(w.B, w.H, w.N, w.d, b, w.phi, w.dtype, w.flags) != m.MHLA_PATH_COLUMNS
+    lib = m.load_library()
+    # null pointers are rejected before the path is looked at; an unsupported
+    # shape for the path (d = 72 > 64) returns UNSUPPORTED before any launch
+    base = 1 << 20
+    sz = 1 << 16
+    bs = m.BlockShape.make((1, 16, 16), (1, 4, 4))
+    rc = lib.mhla_forward_path(ctypes.c_void_p(base), ctypes.c_void_p(base + sz),
+                               ctypes.c_void_p(base + 2 * sz), ctypes.c_void_p(base + 3 * sz),
+                               ctypes.c_void_p(base + 4 * sz), 1, 1, 256, 72, ctypes.byref(bs), 0,
+                               m.MHLA_DTYPE_BF16, m.MHLA_PATH_COLUMNS, None)
+    assert rc == m.MHLA_ERR_UNSUPPORTED
+    # a block of 512 tokens is beyond the member-offset table
+    bs = m.BlockShape.make((1, 32, 32), (1, 16, 32))
+    rc = lib.mhla_forward_path(ctypes.c_void_p(base), ctypes.c_void_p(base + 4 * sz),
+                               ctypes.c_void_p(base + 8 * sz), ctypes.c_void_p(base + 12 * sz),
+                               ctypes.c_void_p(base + 16 * sz), 1, 1, 1024, 32, ctypes.byref(bs),
+                               0, m.MHLA_DTYPE_BF16, m.MHLA_PATH_COLUMNS, None)
+    assert rc == m.MHLA_ERR_UNSUPPORTED
+    assert lib.mhla_forward_path(None, None, None, None, None, 1, 1, 64, 16, ctypes.byref(bs), 0,
+                                 0, 6, None) == m.MHLA_ERR_INVALID_ARG
+
+
 def test_forward_rejects_null_pointers_before_any_launch():
     lib = m.load_library()
     bs = m.BlockShape.make((8, 8), (4, 4))

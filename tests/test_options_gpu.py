@@ -39,6 +39,8 @@ NO_NORM_CASES = [
     (2, 3, (1, 9, 9), (1, 3, 3), 48, PHI_ELU1, DTYPE_BF16, m.MHLA_PATH_PAIRS),
     (1, 4, (1, 32, 32), (1, 8, 8), 64, PHI_RELU, DTYPE_BF16, m.MHLA_PATH_BLOCKED),
     (2, 2, (2, 16, 16), (1, 4, 8), 96, PHI_ELU1, DTYPE_BF16, m.MHLA_PATH_BLOCKED),
+    (1, 4, (1, 32, 32), (1, 8, 8), 64, PHI_RELU, DTYPE_BF16, m.MHLA_PATH_COLUMNS),
+    (2, 2, (2, 16, 16), (1, 4, 8), 40, PHI_ELU1, DTYPE_BF16, m.MHLA_PATH_COLUMNS),
 ]
 
 
@@ -134,7 +136,7 @@ def test_options_rejected_before_launch():
     assert e.value.code == m.MHLA_ERR_SHAPE
     wl = custom_workload(1, 1, 64, (1, 1, 256), (1, 1, 64), PHI_ELU1, DTYPE_BF16, index=3,
                          flags=FLAG_CAUSAL)
-    for path in (m.MHLA_PATH_FUSED, m.MHLA_PATH_PAIRS, m.MHLA_PATH_GENERIC):
+    for path in (m.MHLA_PATH_FUSED, m.MHLA_PATH_PAIRS, m.MHLA_PATH_GENERIC, m.MHLA_PATH_COLUMNS):
         with pytest.raises(m.MhlaError) as e:
             run(make_inputs(wl), path)
         assert e.value.code == m.MHLA_ERR_UNSUPPORTED

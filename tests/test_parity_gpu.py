@@ -16,7 +16,10 @@ from gpu_util import TOL, run, slice_error, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
-ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED, m.MHLA_PATH_BLOCKED, m.MHLA_PATH_PAIRS]
+ALL_PATHS = [m.MHLA_PATH_GENERIC, m.MHLA_PATH_FUSED, m.MHLA_PATH_BLOCKED, m.MHLA_PATH_PAIRS,
+             m.MHLA_PATH_COLUMNS]
+# paths that take only some shapes: an unsupported shape skips the case
+PARTIAL_PATHS = (m.MHLA_PATH_PAIRS, m.MHLA_PATH_COLUMNS)
 
 
 def _oracle_full(inp):
@@ -48,13 +51,14 @@ def _check_sampled(inp, y, n_slices, n_rows, seed=0):
 
 @pytest.mark.parametrize("name", ["tiny", "deit_t", "dit_xl2", "hires"])
 @pytest.mark.parametrize("path", [m.MHLA_PATH_AUTO, m.MHLA_PATH_GENERIC, m.MHLA_PATH_BLOCKED,
-                                  m.MHLA_PATH_PAIRS])
+                                  m.MHLA_PATH_PAIRS, m.MHLA_PATH_COLUMNS])
 def test_workload_full(name, path):
-    if path in (m.MHLA_PATH_BLOCKED, m.MHLA_PATH_PAIRS) and WORKLOADS[name].dtype != DTYPE_BF16:
+    if path != m.MHLA_PATH_AUTO and path != m.MHLA_PATH_GENERIC and \
+            WORKLOADS[name].dtype != DTYPE_BF16:
         pytest.skip("the MFMA paths take bf16 inputs")
     wl = WORKLOADS[name]
     inp = make_inputs(wl)
-    y = to_f64(run(inp, path, skip_unsupported=(path == m.MHLA_PATH_PAIRS)))
+    y = to_f64(run(inp, path, skip_unsupported=(path in PARTIAL_PATHS)))
     ref = _oracle_full(inp)
     err = slice_error(y, ref)
     print("PARITY %s path=%d err=%.3e" % (name, path, err))
@@ -92,7 +96,7 @@ FUSED_CASES = [
 def test_small_shapes(grid, block, d, phi, path):
     wl = custom_workload(3, 2, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 997)
     inp = make_inputs(wl)
-    y = to_f64(run(inp, path, skip_unsupported=(path == m.MHLA_PATH_PAIRS)))
+    y = to_f64(run(inp, path, skip_unsupported=(path in PARTIAL_PATHS)))
     err = slice_error(y, _oracle_full(inp))
     print("PARITY small %s %s d=%d phi=%d path=%d err=%.3e" % (grid, block, d, phi, path, err))
     assert err <= TOL[DTYPE_BF16]
@@ -146,6 +150,42 @@ def test_pairs_shapes(grid, block, d, phi):
     assert np.all(np.isfinite(y))
     err = slice_error(y, _oracle_full(inp))
     print("PARITY pairs %s %s d=%d phi=%d M=%d err=%.3e" % (grid, block, d, phi, wl.M, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+COLS_CASES = [
+    # (grid, block, d, phi): the column-split path, up to 64 blocks and d <= 64
+    ((1, 64, 64), (1, 8, 8), 64, PHI_RELU),     # the 4096-token image geometry, M = 64
+    ((1, 32, 48), (1, 4, 8), 64, PHI_ELU1),     # M = 48: a partial second block group
+    ((1, 33, 8), (1, 1, 8), 40, PHI_RELU),      # M = 33: one block in the second group
+    ((1, 20, 20), (1, 10, 10), 56, PHI_ELU1),   # 100-token blocks: four 32-token steps
+    ((1, 28, 28), (1, 7, 7), 64, PHI_RELU),     # M = 16, 49-token ragged blocks
+    ((4, 16, 16), (2, 4, 4), 32, PHI_ELU1),     # 3-D blocks, M = 32, d = 32
+    ((1, 1, 600), (1, 1, 24), 16, PHI_RELU),    # 1-D chunks, M = 25, d = 16
+    ((3, 8, 12), (1, 4, 4), 24, PHI_ELU1),      # 3-D grid, M = 18, d = 24 (partial chunk)
+    ((1, 12, 12), (1, 12, 12), 8, PHI_RELU),    # M = 1, d = 8
+    ((2, 24, 24), (1, 6, 6), 48, PHI_RELU),     # M = 32 exactly, 36-token blocks
+]
+
+
+@pytest.mark.parametrize("grid,block,d,phi", COLS_CASES)
+def test_cols_shapes(grid, block, d, phi):
+    wl = custom_workload(3, 2, d, grid, block, phi, DTYPE_BF16, index=hash((grid, block, d)) % 971)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_COLUMNS))
+    assert np.all(np.isfinite(y))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY cols %s %s d=%d phi=%d M=%d err=%.3e" % (grid, block, d, phi, wl.M, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
+def test_cols_odd_slice_count():
+    """B*H = 7 slices: the XCD-grouped grid has workgroups with no slice."""
+    wl = custom_workload(7, 1, 64, (1, 32, 32), (1, 8, 8), PHI_ELU1, DTYPE_BF16, index=12)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_COLUMNS))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY cols 7 slices err=%.3e" % err)
     assert err <= TOL[DTYPE_BF16]
 
 

@@ -10,7 +10,8 @@ library: ``python -m token_level_head_mhla_amd.build``.
 from ._binding import (  # noqa: F401
     MHLA_DTYPE_BF16, MHLA_DTYPE_F32, MHLA_ERR_ALIAS, MHLA_ERR_HIP, MHLA_ERR_INVALID_ARG,
     MHLA_ERR_SHAPE, MHLA_ERR_UNSUPPORTED, MHLA_FLAG_CAUSAL, MHLA_FLAG_NO_NORM, MHLA_OK,
-    MHLA_PATH_AUTO, MHLA_PATH_BLOCKED, MHLA_PATH_FUSED, MHLA_PATH_GENERIC, MHLA_PATH_PAIRS,
+    MHLA_PATH_AUTO, MHLA_PATH_BLOCKED, MHLA_PATH_COLUMNS, MHLA_PATH_FUSED, MHLA_PATH_GENERIC,
+    MHLA_PATH_PAIRS,
     MHLA_PHI_ELU1, MHLA_PHI_RELU, MhlaError, BlockShape, EXPORTED_SYMBOLS, library_path,
     load_library, mhla_backward, mhla_decode_state_bytes, mhla_decode_step, mhla_error_string,
     mhla_forward, mhla_forward_ex, mhla_forward_path,

@@ -14,7 +14,8 @@ MHLA_PHI_RELU, MHLA_PHI_ELU1 = 0, 1
 MHLA_DTYPE_F32, MHLA_DTYPE_BF16 = 0, 1
 (MHLA_OK, MHLA_ERR_INVALID_ARG, MHLA_ERR_SHAPE, MHLA_ERR_UNSUPPORTED, MHLA_ERR_HIP,
  MHLA_ERR_ALIAS) = range(6)
-MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_BLOCKED = range(5)
+(MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_BLOCKED,
+ MHLA_PATH_COLUMNS) = range(6)
 MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL = 1, 2
 
 EXPORTED_SYMBOLS = (

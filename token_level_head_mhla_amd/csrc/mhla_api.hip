@@ -19,6 +19,7 @@
 #include "mhla_common.hpp"
 #include "k_generic.hpp"
 #include "k_fused.hpp"
+#include "k_cols.hpp"
 #include "k_blocked.hpp"
 #include "k_pairs.hpp"
 #include "k_causal.hpp"
@@ -124,6 +125,7 @@ bool path_supports(int path, const Problem& p) {
     case MHLA_PATH_FUSED: return fused_supports(p.dtype, p.d, p.g.M, p.g.nb);
     case MHLA_PATH_BLOCKED: return blocked_supports(p.dtype, p.d, p.g.M, p.slices());
     case MHLA_PATH_PAIRS: return pairs_supports(p.dtype, p.d, p.g.M, p.g.nb, p.N);
+    case MHLA_PATH_COLUMNS: return cols_supports(p.dtype, p.d, p.g.M, p.g.nb, p.slices());
     default: return false;
   }
 }
@@ -133,6 +135,9 @@ int choose_path(const Problem& p) {
     return path_supports(MHLA_PATH_BLOCKED, p) ? MHLA_PATH_BLOCKED : -MHLA_ERR_UNSUPPORTED;
   if (path_supports(MHLA_PATH_FUSED, p)) return MHLA_PATH_FUSED;
   if (path_supports(MHLA_PATH_PAIRS, p)) return MHLA_PATH_PAIRS;
+  // MHLA_PATH_COLUMNS is never chosen here: every column chunk re-reads the
+  // slice's K and Q through L2, and on the 4096-token image shape it took
+  // 64 us against 54 us for the blocked path.
   if (path_supports(MHLA_PATH_BLOCKED, p)) return MHLA_PATH_BLOCKED;
   if (path_supports(MHLA_PATH_GENERIC, p)) return MHLA_PATH_GENERIC;
   return -MHLA_ERR_UNSUPPORTED;
@@ -248,6 +253,9 @@ int run(const void* Q, const void* K, const void* V, const float* W, void* out, 
   } else if (path == MHLA_PATH_PAIRS) {
     rc = launch_pairs(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
                       (const bf16_t*)V, W, (bf16_t*)out, st);
+  } else if (path == MHLA_PATH_COLUMNS) {
+    rc = launch_cols(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
+                     (const bf16_t*)V, W, (bf16_t*)out, st);
   } else if (path == MHLA_PATH_BLOCKED && p.causal()) {
     rc = launch_causal(p.slices(), p.H, p.N, p.d, p.g, p.phi, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, W, (bf16_t*)out, (bf16_t*)ws, st);
@@ -337,7 +345,7 @@ int mhla_forward_path(const void* Q, const void* K, const void* V, const float* 
                       void* out, int B, int H, int N, int d,
                       const mhla_block_shape* block_shape, int phi_kind, int dtype, int path,
                       void* stream) {
-  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_COLUMNS)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
   return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, 0, path, stream);
 }
@@ -345,7 +353,7 @@ int mhla_forward_path(const void* Q, const void* K, const void* V, const float* 
 int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wmix, void* out,
                     int B, int H, int N, int d, const mhla_block_shape* block_shape,
                     int phi_kind, int dtype, int flags, int path, void* stream) {
-  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_BLOCKED)
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_COLUMNS)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
   return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, flags, path, stream);
 }
