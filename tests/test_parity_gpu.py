@@ -165,7 +165,20 @@ COLS_CASES = [
     ((3, 8, 12), (1, 4, 4), 24, PHI_ELU1),      # 3-D grid, M = 18, d = 24 (partial chunk)
     ((1, 12, 12), (1, 12, 12), 8, PHI_RELU),    # M = 1, d = 8
     ((2, 24, 24), (1, 6, 6), 48, PHI_RELU),     # M = 32 exactly, 36-token blocks
+    ((1, 64, 64), (1, 16, 16), 64, PHI_ELU1),   # 256-token blocks: the largest the path takes
 ]
+
+
+def test_cols_largest_shape():
+    """M = 64 blocks of 256 tokens, d = 64: the largest LDS footprint and the
+    longest summary and readout loops of the column-split path."""
+    wl = custom_workload(1, 2, 64, (1, 128, 128), (1, 16, 16), PHI_RELU, DTYPE_BF16, index=13)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_COLUMNS))
+    assert np.all(np.isfinite(y))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY cols largest M=%d nb=%d err=%.3e" % (wl.M, wl.nb, err))
+    assert err <= TOL[DTYPE_BF16]
 
 
 @pytest.mark.parametrize("grid,block,d,phi", COLS_CASES)
