@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
     }
 
     const float rd = out_scale(g, __shfl(oz[0], s));
-    store_row_tiles<NT>(qj < nb ? Y + off + (size_t)(base + qj) * d : nullptr, d, o, rd, grp);
+    store_row_tiles<NT, true>(qj < nb ? Y + off + (size_t)(base + qj) * d : nullptr, d, o, rd,
+                              grp);
   }
 }
 

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * fused_waves(MM)) void k_fused(
     // row 0 of the z~ tile (lane s of group 0, element 0) is phi(q).z~_i
     const float den = __shfl(oz[0], s);
     const float rd = out_scale(g, den);
-    store_row_tiles<NT>(tok[u] >= 0 ? Y + off + (size_t)tok[u] * d : nullptr, d, o, rd, grp);
+    store_row_tiles<NT, true>(tok[u] >= 0 ? Y + off + (size_t)tok[u] * d : nullptr, d, o, rd, grp);
   }
 }
 

@@ -31,6 +31,7 @@ typedef short i16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b,
@@ -126,8 +127,13 @@ __device__ __forceinline__ u16x8_t from_u2x2(uint2 a, uint2 b) {
 // entries of tile j and odd groups 8 of tile j+1 (a last odd tile is stored
 // with 8-byte stores).  Every lane takes part in the exchange; only the
 // stores are masked: nothing for row == nullptr, and no entry >= limit
-// (limit a multiple of 8; row 16-byte aligned).
-template <int NT>
+// (limit a multiple of 8; row 16-byte aligned).  STREAM = true makes the
+// stores nontemporal, for a final output that no later kernel of the call
+// reads (intermediates keep ordinary stores: the next kernel reads them back
+// through L2 and the last-level cache).  It is set where it measured faster:
+// the fused and the causal readouts (1.5% and 4%); the blocked and token-pair
+// readouts measured 2-6% slower with it.
+template <int NT, bool STREAM = false>
 __device__ __forceinline__ void store_row_tiles(bf16_t* row, int limit, const f32x4_t (&t)[NT],
                                                 float scale, int grp) {
   const bool odd = (grp & 1) != 0;
@@ -141,14 +147,23 @@ __device__ __forceinline__ void store_row_tiles(bf16_t* row, int limit, const f3
     const uint32_t r0 = __shfl_xor(odd ? a0 : b0, 16), r1 = __shfl_xor(odd ? a1 : b1, 16);
     const u32x4_t v = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
     const int c = odd ? 16 * (j + 1) + 4 * (grp - 1) : 16 * j + 4 * grp;
-    if (row != nullptr && c < limit) *reinterpret_cast<u32x4_t*>(row + c) = v;
+    if (row != nullptr && c < limit) {
+      if constexpr (STREAM)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(row + c));
+      else
+        *reinterpret_cast<u32x4_t*>(row + c) = v;
+    }
   }
   if constexpr (NT % 2 != 0) {
     const int c = 16 * (NT - 1) + 4 * grp;
-    if (row != nullptr && c < limit)
-      *reinterpret_cast<uint2*>(row + c) =
-          make_uint2(pack2(t[NT - 1][0] * scale, t[NT - 1][1] * scale),
-                     pack2(t[NT - 1][2] * scale, t[NT - 1][3] * scale));
+    if (row != nullptr && c < limit) {
+      const u32x2_t v = {pack2(t[NT - 1][0] * scale, t[NT - 1][1] * scale),
+                         pack2(t[NT - 1][2] * scale, t[NT - 1][3] * scale)};
+      if constexpr (STREAM)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(row + c));
+      else
+        *reinterpret_cast<u32x2_t*>(row + c) = v;
+    }
   }
 }
 
