@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void k_mix_coef(const float* __restrict__ W,
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = Wh[(size_t)(b + q) * M + i];
   } else {
-    v = *reinterpret_cast<const f32x4_t*>(W + e);
+    v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + e));  // read once
     if constexpr (MODE == kMixCausal) {
       const long r = e % ((long)M * M);
       const int i = (int)(r / M), b = (int)(r - (r / M) * M);
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
 // block 4*blockIdx.x + w, 16 queries per step.  Y^T = S~_i^T phi(Q)^T with the
 // contraction split as features 32ks + 8grp .. +7 on both operands; the z~
 // row (row 0 of one more A tile) gives phi(q).z~_i.  STREAM = true reads Q
-// with the nontemporal hint (see blocked_stream).
+// and writes Y with the nontemporal hint (see blocked_stream).
 template <int DP, int PHI, bool STREAM = false>
 __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ St, bf16_t* __restrict__ Y, Geo g,
@@ -582,7 +582,8 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
       for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
       const float den = __shfl(oz[0], s);
       const float rd = out_scale(g, den);
-      store_row_tiles<NT>(tq[u] >= 0 ? Y + off + (size_t)tq[u] * d : nullptr, d, o, rd, grp);
+      store_row_tiles<NT, STREAM>(tq[u] >= 0 ? Y + off + (size_t)tq[u] * d : nullptr, d, o, rd,
+                                  grp);
     }
   }
 }

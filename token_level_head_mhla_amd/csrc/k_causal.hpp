@@ -101,7 +101,11 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
       const int k0 = 32 * ks + 8 * grp;
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
       if (qj < nb && k0 < d)
-        v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)(base + qj) * d + k0);
+        // Q is read once (nontemporal); K and V are read twice per call (by the
+        // summaries and by this kernel's own-chunk term), so they keep ordinary
+        // loads (an LM-shaped A/B: 130.0-131.0 against 133.9-135.2 us per step)
+        v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(Q + off + (size_t)(base + qj) * d + k0));
       bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
     }
     f32x4_t o[NT], oz = zero4();

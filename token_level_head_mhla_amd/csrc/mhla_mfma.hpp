@@ -131,8 +131,9 @@ __device__ __forceinline__ u16x8_t from_u2x2(uint2 a, uint2 b) {
 // stores nontemporal, for a final output that no later kernel of the call
 // reads (intermediates keep ordinary stores: the next kernel reads them back
 // through L2 and the last-level cache).  It is set where it measured faster:
-// the fused and the causal readouts (1.5% and 4%); the blocked and token-pair
-// readouts measured 2-6% slower with it.
+// the fused and the causal readouts (1.5% and 4%), and the blocked readout of
+// calls larger than the last-level cache; the token-pair readouts, and the
+// blocked readout of smaller calls, measured 2-6% slower with it.
 template <int NT, bool STREAM = false>
 __device__ __forceinline__ void store_row_tiles(bf16_t* row, int limit, const f32x4_t (&t)[NT],
                                                 float scale, int grp) {
