@@ -19,9 +19,10 @@
 //   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
 //   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
 //   4. dS, dz         mixing GEMM with W transposed
-//   5. dW             k_dw_partial (per slice, the rows of dS~ against the rows
-//                     of S over all d*d + d entries) and k_dw_reduce (sum
-//                     over the batch, fixed order: deterministic)
+//   5. dW             k_dw_partial16 (M < 256) or k_dw_partial (per slice,
+//                     the rows of dS~ against the rows of S over all d*d + d
+//                     entries) and k_dw_reduce (sum over the batch, fixed
+//                     order: deterministic)
 //   6. dQ             k_bwd_dphi: S~ staged in LDS and read transposed,
 //                     times G (exact bf16) on MFMA, scaled by 1/den per token
 //                     in fp32, plus z~ dden in fp32, times phi'(Q)
@@ -219,13 +220,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
 }
 
 // ---------------------------------------------------------------------------
-// Step 5.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
-// over the workspace rows (A = dS~, B = S).  grid = (ceil(M/16)^2, slices),
+// Step 5, M < 256.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e]
+// B[slice][b][e] over the workspace rows (A = dS~, B = S).  grid =
+// (ceil(M/16)^2, slices),
 // block = 256: a 16 x 16 output tile per workgroup, the contraction split over
 // the four waves (steps of 32 entries, wave w takes steps w, w + 4, ...) and
 // summed in LDS.  Rows past M are clamped on load and never stored.
 template <int DP>
-__global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __restrict__ A,
+__global__ __launch_bounds__(kBlkThreads) void k_dw_partial16(const bf16_t* __restrict__ A,
                                                             const bf16_t* __restrict__ Bm,
                                                             float* __restrict__ P, int M) {
   using D = BlockedDims<DP>;
@@ -269,6 +271,100 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Step 5, M >= 256.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
+// over the workspace rows (A = dS~, B = S).  grid = (ceil(M/T)^2, slices),
+// block = 256: a T x T output tile per workgroup, a (T/2) x (T/2) quarter per
+// wave.  Both operands are contiguous in e,
+// so the MFMA fragments are 16-byte row reads of an LDS tile (no transpose);
+// 32-entry steps pass through a double-buffered tile, loaded one step ahead.
+// Each operand row is read once per T output columns (a 16 x 16 tile per
+// workgroup read every row once per 16 and moved 6.5 GB through L2 on the video
+// shape).  Rows past M are clamped on load and never stored.
+template <int DP, int T>
+__global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __restrict__ A,
+                                                            const bf16_t* __restrict__ Bm,
+                                                            float* __restrict__ P, int M) {
+  using D = BlockedDims<DP>;
+  constexpr int EP = D::EP, E = DP * DP + DP, NSTEP = E / 32;
+  static_assert(E % 32 == 0, "contraction steps");
+  constexpr int WT = T / 2, FT = WT / 16;        // wave tile and its 16-row fragments
+  constexpr int RS = 32 + 16;                    // LDS row stride (elements)
+  constexpr int CH = 2 * T * 32 / 8 / kBlkThreads;  // 16-byte chunks per thread per step
+  static_assert(CH * 8 * kBlkThreads == 2 * T * 32, "tile");
+  __shared__ __attribute__((aligned(16))) bf16_t sm[2][2 * T * RS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int wi = wave >> 1, wb = wave & 1;
+  const long slice = blockIdx.y;
+  const int nt = (M + T - 1) / T;
+  const int i0 = T * (blockIdx.x / nt), b0 = T * (blockIdx.x % nt);
+  // chunk u of a step: LDS row r = c / 4 (rows 0..T-1 hold A rows i0.., rows
+  // T..2T-1 hold B rows b0..), 16-byte piece c % 4 of the step's 32 entries.
+  // Rows past M are clamped in bounds; they feed outputs that are not stored.
+  const bf16_t* src[CH];
+  int dst[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int c = tid + kBlkThreads * u, r = c >> 2, f = c & 3;
+    const bool isa = r < T;
+    const int row = min((isa ? i0 + r : b0 + r - T), M - 1);
+    src[u] = (isa ? A : Bm) + ((size_t)slice * M + row) * EP + 8 * f;
+    dst[u] = r * RS + 8 * f;
+  }
+  u32x4_t ld[CH];
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) ld[u] = *reinterpret_cast<const u32x4_t*>(src[u] + 32 * k);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) *reinterpret_cast<u32x4_t*>(sm[buf] + dst[u]) = ld[u];
+  };
+  f32x4_t acc[FT][FT];
+#pragma unroll
+  for (int a = 0; a < FT; ++a)
+#pragma unroll
+    for (int b = 0; b < FT; ++b) acc[a][b] = zero4();
+  gload(0);
+  lstore(0);
+  lds_barrier();
+  // Step k reads LDS buffer k & 1; the loads of step k + 1 (clamped, never
+  // skipped) land in the other buffer after this step's fragment reads.
+  for (int k = 0; k < NSTEP; ++k) {
+    const int buf = k & 1;
+    gload(k + 1 < NSTEP ? k + 1 : k);
+    // A fragment: row i (lane s), entries 8grp .. 8grp+7; B likewise for row b
+    u16x8_t af[FT], bf[FT];
+#pragma unroll
+    for (int t = 0; t < FT; ++t) {
+      af[t] = *reinterpret_cast<const u16x8_t*>(sm[buf] + (WT * wi + 16 * t + s) * RS + 8 * grp);
+      bf[t] = *reinterpret_cast<const u16x8_t*>(sm[buf] + (T + WT * wb + 16 * t + s) * RS +
+                                                8 * grp);
+    }
+#pragma unroll
+    for (int a = 0; a < FT; ++a)
+#pragma unroll
+      for (int b = 0; b < FT; ++b) acc[a][b] = mfma_bf16(af[a], bf[b], acc[a][b]);
+    lstore(buf ^ 1);
+    lds_barrier();
+  }
+  // acc[a][b] lane (s, grp) element r = P[i0 + WT wi + 16a + 4grp + r][b0 + WT wb + 16b + s]
+#pragma unroll
+  for (int a = 0; a < FT; ++a)
+#pragma unroll
+    for (int b = 0; b < FT; ++b) {
+      const int bc = b0 + WT * wb + 16 * b + s;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + WT * wi + 16 * a + 4 * grp + r;
+        if (i < M && bc < M) P[((size_t)slice * M + i) * M + bc] = acc[a][b][r];
+      }
+    }
+}
+
 // dW[h][i][b] = sum over the batch of P[batch * H + h][i][b], in batch order.
 __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
                                                    float* __restrict__ dW, int B, int H, int M) {
@@ -292,7 +388,8 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
 inline bool backward_supports(int dtype, int d, int M, long slices) {
   if (!blocked_supports(dtype, d, M, slices)) return false;
   // the precise mixing GEMM runs 64 query blocks per workgroup on a 1-D grid,
-  // and the dW tile grid is ceil(M/16)^2 workgroups along x
+  // and the dW tile grid is ceil(M/16)^2 (M < 256) or ceil(M/128)^2 workgroups
+  // along x
   const long n = (slices + 7) / 8 * 8 * (long)(blocked_ws_elems(d) / kMixEB) * ((M + 63) / 64);
   return n * kBlkThreads < (1L << 31) && (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
 }
@@ -355,8 +452,13 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   // 4. dS = W^T-mixing of dS~
   launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, wc, st);
   // 5. dW
-  const unsigned nt = (unsigned)((M + 15) / 16);
-  k_dw_partial<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+  if (M >= 256) {
+    const unsigned nt = (unsigned)((M + 127) / 128);
+    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+  } else {
+    const unsigned nt = (unsigned)((M + 15) / 16);
+    k_dw_partial16<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+  }
   const long nw = (long)H * M * M;
   k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
   // 6. dQ, against the precise S~

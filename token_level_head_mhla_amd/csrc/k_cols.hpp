@@ -15,9 +15,9 @@
 //      (phi applied) and the chunk's V columns go to the wave's own LDS
 //      staging area with 16-byte writes; transpose reads give the MFMA
 //      operands, D[c][k] = sum_t V[t][c] phi(K)[t][k] and, with one-hot
-//      rows of ones as the other operand, z_b[k].  The finished S_b[:, chunk] and z_b are written as
-//      bf16 into column b % 32 of an entry-major table (entry e = c*DP + k,
-//      then DP entries of z).
+//      rows of ones as the other operand, z_b[k].  The finished S_b[:, chunk]
+//      and z_b are written as bf16 into column b % 32 of an entry-major table
+//      (entry e = c*DP + k, then DP entries of z).
 //   2. Every 32 blocks the table is mixed on MFMA:
 //      S~[i][e] += sum_b W[i][b] S[b][e] (W rounded to bf16), with the
 //      accumulators for all query blocks i of the wave's entries in
