@@ -71,6 +71,7 @@ BACKWARD_CASES = [
     (1, 2, (1, 16, 16), (1, 16, 8), 96, PHI_ELU1),   # 128-token blocks, d = 96
     (1, 2, (1, 32, 32), (1, 2, 2), 32, PHI_ELU1),    # M = 256: large-M mixing, both directions
     (2, 2, (1, 48, 48), (1, 2, 4), 64, PHI_RELU),    # M = 288: partial 128-row dW tiles, d = 64
+    (2, 2, (1, 20, 16), (1, 4, 4), 64, PHI_ELU1),    # M = 20: streamed mixing, both directions
 ]
 
 

@@ -357,6 +357,118 @@ __global__ __launch_bounds__(256) void k_mix_coef(const float* __restrict__ W,
   *reinterpret_cast<uint2*>(Wc + e) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
 }
 
+// Mixing for 16 < M <= 32 (MP = 32, M padded): the contraction is a single
+// 32-block step, so a workgroup that takes a single 128-entry tile spends its
+// life waiting for one load.  Here a workgroup (4 waves) loads the
+// head's coefficients into LDS once (bf16, the mode applied, zero past M) and
+// then streams kStreamTiles consecutive 128-entry tiles of one slice: the S
+// tile of tile t + 1 is loaded into registers while tile t is multiplied.
+// Wave w owns entries 32w .. 32w+31 of a tile for all MP query blocks.
+// grid = xslices * ceil(nE / kStreamTiles), XCD-aware like k_mix_mfma.
+// Same-box A/B against k_mix_mfma: the LM shape (M = 32) 127.5 against
+// 129.8 us per step; with MP = 64 the 4096-token image shape (M = 64) was
+// 2.6% slower, so k_mix_mfma keeps M > 32.
+constexpr int kStreamTiles = 3;
+
+template <int EP, int MODE, int MP>
+__global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __restrict__ S,
+                                                            const float* __restrict__ W,
+                                                            bf16_t* __restrict__ St, int M,
+                                                            int H, long nslices) {
+  constexpr int TE = 128, KS = MP / 32, BT = MP / 16, AT = 2;
+  constexpr int SRS = TE + 8;          // S tile row stride (rows = key blocks)
+  constexpr int WRS = MP + 16;         // coefficient row stride (rows = query blocks)
+  constexpr int SCH = MP * TE / 8 / kBlkThreads;  // 16-byte S chunks per thread per tile
+  constexpr int nE = EP / TE;
+  constexpr int NG = (nE + kStreamTiles - 1) / kStreamTiles;  // tile groups per slice
+  __shared__ __attribute__((aligned(16))) bf16_t sS[2][MP * SRS];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[MP * WRS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const long slice = (long)(j / NG) * 8 + xcd;
+  if (slice >= nslices) return;  // before any barrier
+  const int t0 = (j - (j / NG) * NG) * kStreamTiles;
+  const int nt = min(kStreamTiles, nE - t0);
+  const int h = (int)(slice % H);
+  const bf16_t* Ss = S + (size_t)slice * M * EP;
+  const float* Wh = W + (size_t)h * M * M;
+
+  // coefficients coef(i, b) as bf16, [i][b]; zero for i, b >= M
+  for (int e = tid; e < MP * MP; e += kBlkThreads) {
+    const int i = e / MP, b = e - (e / MP) * MP;
+    float w = 0.0f;
+    if (i < M && b < M) {
+      if constexpr (MODE == kMixTransposed) w = Wh[(size_t)b * M + i];
+      else w = Wh[(size_t)i * M + b];
+      if constexpr (MODE == kMixCausal) w = b < i ? w : 0.0f;
+    }
+    sW[i * WRS + b] = f32_to_bf16(w);
+  }
+  // S chunk u of a tile: key-block row r (clamped in bounds; its coefficients
+  // are zero past M), 16-byte piece f
+  u32x4_t sr[SCH];
+  auto sload = [&](int t) {
+    const int e0 = (t0 + min(t, nt - 1)) * TE;
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c / (TE / 8), f = c % (TE / 8);
+      sr[u] = *reinterpret_cast<const u32x4_t*>(Ss + (size_t)min(r, M - 1) * EP + e0 + 8 * f);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int c = tid + kBlkThreads * u;
+      const int r = c / (TE / 8), f = c % (TE / 8);
+      *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) = sr[u];
+    }
+  };
+  sload(0);
+  lstore(0);
+  lds_barrier();
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    sload(t + 1);  // clamped: the last tile repeats, harmlessly
+    // A = S^T (rows e, contraction b via transpose reads), B = coef^T (column
+    // i, b contiguous in the [i][b] tile)
+    f32x4_t acc[AT][BT];
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int c = 0; c < BT; ++c) acc[a][c] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u16x8_t af[AT], bw[BT];
+#pragma unroll
+      for (int a = 0; a < AT; ++a) af[a] = lds_tr8(sS[buf], SRS, 32 * ks, 32 * wave + 16 * a, lane);
+#pragma unroll
+      for (int c = 0; c < BT; ++c)
+        bw[c] = *reinterpret_cast<const u16x8_t*>(sW + (16 * c + s) * WRS + 32 * ks + 8 * grp);
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
+    }
+    // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 32 wave + 16a + 4grp + r]
+    const int e0 = (t0 + t) * TE + 32 * wave;
+#pragma unroll
+    for (int c = 0; c < BT; ++c) {
+      const int i = 16 * c + s;
+      f32x4_t tt[AT];
+#pragma unroll
+      for (int a = 0; a < AT; ++a) tt[a] = acc[a][c];
+      store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 : nullptr, 32, tt, 1.0f,
+                          grp);
+    }
+    lstore(buf ^ 1);
+    lds_barrier();
+  }
+}
+
 // The transposed coefficients Wc[h][i][b] = W[h][b][i] (the backward's dS
 // mixing), through a 32 x 32 LDS tile so that both the fp32 reads and the bf16
 // writes are coalesced rows (reading W down its columns took 36 us on the
@@ -733,6 +845,12 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
       k_mix_coef<MODE><<<dim3((unsigned)((tot / 4 + 255) / 256)), 256, 0, st>>>(W, wc, M, tot);
     const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 255) / 256));
     k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+    return;
+  }
+  if (M <= 32) {
+    constexpr int NG = (D::EP / 128 + kStreamTiles - 1) / kStreamTiles;
+    const unsigned n = (unsigned)(xslices * NG);
+    k_mix_stream<D::EP, MODE, 32><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
     return;
   }
   const int ib = mix_ib(M);
