@@ -7,10 +7,13 @@
 // of Y_q needs only column c of every S_b and the whole z_b.  So each
 // workgroup forms S_b[:, chunk] and z_b for every block of its slice, mixes
 // them with the head's coefficients and reads out its 16 columns of every
-// query, all on chip; HBM sees Q, K, V, W and Y only (K and Q are read by every
-// chunk of a slice, which the grid places on one XCD so that the re-reads are
-// L2 hits).
+// query, all on chip: there is no workspace.  K and Q are read by every chunk
+// of a slice; the grid places the chunks of a slice on one XCD so that the
+// re-reads can hit in its L2.  (Measured on the 4096-token image shape this is
+// slower than the three-kernel blocked path, so it is an explicit path only.)
 //
+//   0. Block bases and member offsets go to a small LDS table once, so the
+//      loops below do no integer division.
 //   1. Wave w summarises blocks b = w, w + 8, ... in 32-token steps: K rows
 //      (phi applied) and the chunk's V columns go to the wave's own LDS
 //      staging area with 16-byte writes; transpose reads give the MFMA
@@ -26,9 +29,9 @@
 //   3. S~ (and z~) go to LDS as bf16, laid out [i][c][k] (c = 16 is z~).
 //   4. Readout: work item = 16 queries of one block.  Y^T[c][q] =
 //      S~_i^T phi(Q)^T on MFMA with phi(Q) loaded straight from global memory
-//      (8 consecutive features per lane); the denominator phi(q).z~_i is a
-//      per-lane dot product summed over the four lane groups; the divide and
-//      the bf16 rounding are fused into 8-byte stores.
+//      (8 consecutive features per lane); a second accumulator whose A
+//      operand holds z~_i in row 0 gives the denominators phi(q).z~_i; the
+//      divide and the bf16 rounding are fused into 8-byte stores.
 //
 // A denominator of exactly 0 (ReLU with phi(q) = 0) writes a zero row.
 #pragma once
