@@ -339,22 +339,38 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 // prefix mode a tile stops at the last key block its rows can use.
 constexpr int kMixBigM = 256;
 
+// Coefficient layout of the large-M mixing: for every head, query-block tile
+// (256 rows, padded with zero rows past M) and 32-block step, one contiguous
+// 256 x 32 bf16 tile (16 KB), so that each mixing step loads whole cache lines.
+__host__ __device__ inline size_t coef_tiled(int M, int h, int i, int b) {
+  const int nit = (M + 255) / 256, nk = M / 32;
+  return (((size_t)h * nit + i / 256) * nk + b / 32) * 8192 + (size_t)(i % 256) * 32 + b % 32;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256) void k_mix_coef(const float* __restrict__ W,
                                                   bf16_t* __restrict__ Wc, int M, long total) {
-  // grid = ceil(total / 1024), four consecutive entries per thread (M % 4 == 0)
+  // grid = total / 1024 over the padded [H][MI][M] entries (MI = M rounded up
+  // to 256), four consecutive entries per thread (M % 32 == 0)
+  static_assert(MODE != kMixTransposed, "the transposed mode uses k_mix_coef_t");
   const long e = 4 * ((long)blockIdx.x * 256 + threadIdx.x);
   if (e >= total) return;
-  static_assert(MODE != kMixTransposed, "the transposed mode uses k_mix_coef_t");
-  f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + e));  // read once
-  if constexpr (MODE == kMixCausal) {
-    const long r = e % ((long)M * M);
-    const int i = (int)(r / M), b = (int)(r - (r / M) * M);
+  const long mi = (long)(M + 255) / 256 * 256;
+  const int h = (int)(e / (mi * M));
+  const long r = e - h * mi * M;
+  const int i = (int)(r / M), b = (int)(r - (r / M) * M);
+  f32x4_t v = zero4();
+  if (i < M) {
+    v = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_t*>(W + ((size_t)h * M + i) * M + b));  // read once
+    if constexpr (MODE == kMixCausal) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (b + q >= i) v[q] = 0.0f;
+      for (int q = 0; q < 4; ++q)
+        if (b + q >= i) v[q] = 0.0f;
+    }
   }
-  *reinterpret_cast<uint2*>(Wc + e) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+  *reinterpret_cast<uint2*>(Wc + coef_tiled(M, h, i, b)) =
+      make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
 }
 
 // Mixing for 16 < M <= 32 (MP = 32, M padded): the contraction is a single
@@ -469,26 +485,31 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
   }
 }
 
-// The transposed coefficients Wc[h][i][b] = W[h][b][i] (the backward's dS
+// The transposed coefficients coef(i, b) = W[h][b][i] (the backward's dS
 // mixing), through a 32 x 32 LDS tile so that both the fp32 reads and the bf16
 // writes are coalesced rows (reading W down its columns took 36 us on the
-// video shape, against 8.5 us for the plain conversion).  grid = H * (M/32)^2
-// (head-major), block = 256; M % 32 == 0.
+// video shape, against 8.5 us for the plain conversion).  grid =
+// H * (MI/32) * (M/32) (head-major; MI = M rounded up to 256, the tiles past
+// M write the zero padding rows), block = 256; M % 32 == 0.
 __global__ __launch_bounds__(256) void k_mix_coef_t(const float* __restrict__ W,
                                                     bf16_t* __restrict__ Wc, int M) {
   __shared__ float tile[32][33];
-  const int nt = M / 32;
-  const int h = blockIdx.x / (nt * nt), rem = blockIdx.x - h * nt * nt;
-  const int b0 = 32 * (rem / nt), i0 = 32 * (rem % nt);
-  const size_t hoff = (size_t)h * M * M;
+  const int nti = (M + 255) / 256 * 8, ntb = M / 32;
+  const int h = blockIdx.x / (nti * ntb), rem = blockIdx.x - h * nti * ntb;
+  const int b0 = 32 * (rem / nti), i0 = 32 * (rem % nti);
   const int t = threadIdx.x, r = t >> 3, c4 = 4 * (t & 7);
-  // read row b0 + r of W, columns i0 + c4 .. + 3
-  const f32x4_t v = *reinterpret_cast<const f32x4_t*>(W + hoff + (size_t)(b0 + r) * M + i0 + c4);
+  if (i0 < M) {  // uniform: read row b0 + r of W, columns i0 + c4 .. + 3
+    const f32x4_t v =
+        *reinterpret_cast<const f32x4_t*>(W + ((size_t)h * M + b0 + r) * M + i0 + c4);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) tile[r][c4 + q] = v[q];
+    for (int q = 0; q < 4; ++q) tile[r][c4 + q] = v[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[r][c4 + q] = 0.0f;
+  }
   __syncthreads();
-  // write row i0 + r of Wc, columns b0 + c4 .. + 3: tile[c4 + q][r]
-  *reinterpret_cast<uint2*>(Wc + hoff + (size_t)(i0 + r) * M + b0 + c4) =
+  // coefficient row i0 + r, columns b0 + c4 .. + 3: tile[c4 + q][r]
+  *reinterpret_cast<uint2*>(Wc + coef_tiled(M, h, i0 + r, b0 + c4)) =
       make_uint2(pack2(tile[c4][r], tile[c4 + 1][r]), pack2(tile[c4 + 2][r], tile[c4 + 3][r]));
 }
 
@@ -534,7 +555,8 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
   const int e0 = (rem / nI) * TE, i0 = (rem - (rem / nI) * nI) * TI;
   const int h = (int)(slice % H);
   const bf16_t* Ss = S + (size_t)slice * M * EP;
-  const bf16_t* Wh = Wc + (size_t)h * M * M;
+  // this tile's coefficients: contiguous 256 x 32 tiles, one per step
+  const bf16_t* Wt = Wc + coef_tiled(M, h, i0, 0);
   int nk = M / KB;
   if constexpr (MODE == kMixCausal) {
     // coefficients vanish for b >= i: stop below the tile's last row
@@ -561,15 +583,11 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
       const int r = c / (TE / 8), f = c % (TE / 8);
       sr[u] = *reinterpret_cast<const u32x4_t*>(Ss + (size_t)(b0 + r) * EP + e0 + 8 * f);
     }
+    // chunk c of the step's 16 KB tile is row c / 4, columns 8 (c % 4) ..;
+    // rows past M are zero padding
 #pragma unroll
-    for (int u = 0; u < WCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (KB / 8), f = c % (KB / 8);
-      // rows past M are clamped in bounds; they feed outputs that are never
-      // stored (unconditional loads keep the wait counts exact)
-      const int i = i0 + r < M ? i0 + r : M - 1;
-      wr[u] = *reinterpret_cast<const u32x4_t*>(Wh + (size_t)i * M + b0 + 8 * f);
-    }
+    for (int u = 0; u < WCH; ++u)
+      wr[u] = *reinterpret_cast<const u32x4_t*>(Wt + (size_t)k * 8192 + 8 * (tid + 256 * u));
   };
   auto lstore = [&](const u32x4_t (&sr)[SCH], const u32x4_t (&wr)[WCH], int buf) {
 #pragma unroll
@@ -741,11 +759,12 @@ inline size_t blocked_ws_elems(int d) {
 // kernel is not used), 256-byte aligned.
 inline size_t mix_coef_bytes(int H, int M) {
   if (M < kMixBigM || M % 32 != 0) return 0;
-  return ((size_t)H * M * M * sizeof(bf16_t) + 255) / 256 * 256;
+  const size_t mi = (size_t)(M + 255) / 256 * 256;  // query-block rows, zero-padded
+  return ((size_t)H * mi * M * sizeof(bf16_t) + 255) / 256 * 256;
 }
 
 // Workspace: S and S~, [slices][M][EP] bf16 each, then the mixing's bf16
-// coefficients ([H][M][M], large M only).
+// coefficients (large M only; tiled, see coef_tiled).
 inline size_t blocked_workspace(long slices, int H, int M, int d) {
   return 2 * (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t) + mix_coef_bytes(H, M);
 }
@@ -838,11 +857,11 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
   }
   const long xslices = (slices + 7) / 8 * 8;
   if (mix_coef_bytes(H, M) != 0) {
-    const long tot = (long)H * M * M;
+    const long tot = (long)H * ((M + 255) / 256 * 256) * M;  // padded entries
     if constexpr (MODE == kMixTransposed)
       k_mix_coef_t<<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M);
     else
-      k_mix_coef<MODE><<<dim3((unsigned)((tot / 4 + 255) / 256)), 256, 0, st>>>(W, wc, M, tot);
+      k_mix_coef<MODE><<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M, tot);
     const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 255) / 256));
     k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
     return;
