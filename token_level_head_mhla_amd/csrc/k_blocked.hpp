@@ -219,9 +219,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 #pragma unroll
     for (int c = 0; c < BT; ++c) acc[a][c] = zero4();
 
-  u32x4_t sr[SCH];
-  f32x4_t wr[WCH];
-#define MHLA_MIX_GLOAD(b0)                                                                \
+  u32x4_t sr[SCH], sr1[SCH];
+  f32x4_t wr[WCH], wr1[WCH];
+#define MHLA_MIX_GLOAD(b0, sr, wr)                                                        \
   _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
     const int c = tid + kBlkThreads * u;                                                  \
     const int r = c / (EB / 8), f = c % (EB / 8);                                         \
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
     }                                                                                     \
     wr[u] = v;                                                                            \
   }
-#define MHLA_MIX_LSTORE(buf)                                                              \
+#define MHLA_MIX_LSTORE(buf, sr, wr)                                                      \
   _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
     const int c = tid + kBlkThreads * u;                                                  \
     const int r = c / (EB / 8), f = c % (EB / 8);                                         \
@@ -269,14 +269,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   }
 
   const int nk = (M + KB - 1) / KB;
-  MHLA_MIX_GLOAD(0)
-  MHLA_MIX_LSTORE(0)
-  lds_barrier();
-  for (int k = 0; k < nk; ++k) {
-    const int buf = k & 1;
-    if (k + 1 < nk) { MHLA_MIX_GLOAD((k + 1) * KB) }
-    // A = S^T (rows e, contraction b via transpose reads: b = 8grp .. 8grp+7),
-    // B = W^T (column i, the same b: W[i][8grp .. 8grp+7] is contiguous).
+  // A = S^T (rows e, contraction b via transpose reads: b = 8grp .. 8grp+7),
+  // B = W^T (column i, the same b: W[i][8grp .. 8grp+7] is contiguous).
+  auto compute = [&](int buf) {
     u16x8_t af[AT], bw[BT];
 #pragma unroll
     for (int a = 0; a < AT; ++a) af[a] = lds_tr8(sS[buf], SRS, 0, EW * we + 16 * a, lane);
@@ -297,8 +292,28 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 #pragma unroll
         for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
     }
-    if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1) }
+  };
+  if (nk <= 2) {
+    // M <= 64: both steps' loads go out together (the second one repeats the
+    // first when nk = 1; loads stay unconditional so the waits are exact)
+    MHLA_MIX_GLOAD(0, sr, wr)
+    MHLA_MIX_GLOAD((nk - 1) * KB, sr1, wr1)
+    MHLA_MIX_LSTORE(0, sr, wr)
+    MHLA_MIX_LSTORE(1, sr1, wr1)
     lds_barrier();
+    compute(0);
+    if (nk == 2) compute(1);
+  } else {
+    MHLA_MIX_GLOAD(0, sr, wr)
+    MHLA_MIX_LSTORE(0, sr, wr)
+    lds_barrier();
+    for (int k = 0; k < nk; ++k) {
+      const int buf = k & 1;
+      if (k + 1 < nk) { MHLA_MIX_GLOAD((k + 1) * KB, sr, wr) }
+      compute(buf);
+      if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1, sr, wr) }
+      lds_barrier();
+    }
   }
 #undef MHLA_MIX_GLOAD
 #undef MHLA_MIX_LSTORE
