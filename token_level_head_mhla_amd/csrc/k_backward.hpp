@@ -158,6 +158,34 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
   const size_t off = (size_t)slice * N * d;
   const TT* row = T + ((size_t)slice * g.M + blk) * EP;
   constexpr int F8P = DP / 8;
+  const int bb = g.blockbase(blk);
+  // Loads of one 16-token tile: the u^T operand (lane (s, grp), step kc holds
+  // u[token][32kc + 8grp .. +7]), x at this lane's output features and the
+  // per-token factors.  Rows and features are clamped in bounds, so every
+  // load is issued; pad tokens and features are masked when used.
+  int tq;
+  u16x8_t bu[DS];
+  uint2 xv[NT];
+  float us, ue;
+  auto load_tile = [&](int t0) {
+    const int j = t0 + s;
+    tq = j < g.nb ? bb + g.tokoff(j) : -1;
+    const int tc = bb + g.tokoff(min(j, g.nb - 1));
+#pragma unroll
+    for (int kc = 0; kc < DS; ++kc)
+      bu[kc] = *reinterpret_cast<const u16x8_t*>(U + off + (size_t)tc * d +
+                                                 min(32 * kc + 8 * grp, d - 8));
+#pragma unroll
+    for (int ft = 0; ft < NT; ++ft)
+      xv[ft] = *reinterpret_cast<const uint2*>(X + off + (size_t)tc * d +
+                                               min(16 * ft + 4 * grp, d - 4));
+    us = uscale != nullptr ? uscale[(size_t)slice * N + tc] : 1.0f;
+    ue = uext != nullptr ? uext[(size_t)slice * N + tc] : 1.0f;
+  };
+  // the wave's first tile is requested before the state is staged, so that
+  // both transfers are in flight together
+  const int first = 16 * wave;
+  if (first < g.nb) load_tile(first);
   for (int it = tid; it < DP * F8P; it += kBlkThreads) {
     const int c = it / F8P, f = it - (it / F8P) * F8P;
     if constexpr (SPLIT) {
@@ -181,21 +209,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
     else sz[f] = bf16_to_f32(row[DP * DP + f]);
   }
   lds_barrier();
-  const int bb = g.blockbase(blk);
-  for (int t0 = 16 * wave; t0 < g.nb; t0 += 16 * kBlkWaves) {
-    const int j = t0 + s;
-    const int tq = j < g.nb ? bb + g.tokoff(j) : -1;
-    // B operand u^T: lane (s, grp), step kc holds u[token][32kc + 8grp .. +7]
-    u16x8_t bu[DS];
+  for (int t0 = first; t0 < g.nb; t0 += 16 * kBlkWaves) {
+    if (t0 != first) load_tile(t0);
+    const u16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    u16x8_t bm[DS];
 #pragma unroll
-    for (int kc = 0; kc < DS; ++kc) {
-      const int c0 = 32 * kc + 8 * grp;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (tq >= 0 && c0 < d) v = *reinterpret_cast<const u32x4_t*>(U + off + (size_t)tq * d + c0);
-      bu[kc] = __builtin_bit_cast(u16x8_t, v);
-    }
-    const float us = (tq >= 0 && uscale != nullptr) ? uscale[(size_t)slice * N + tq] : 1.0f;
-    const float ue = tq < 0 ? 0.0f : (uext != nullptr ? uext[(size_t)slice * N + tq] : 1.0f);
+    for (int kc = 0; kc < DS; ++kc) bm[kc] = (tq >= 0 && 32 * kc + 8 * grp < d) ? bu[kc] : zero8;
+    const float usm = tq >= 0 ? us : 1.0f, uem = tq >= 0 ? ue : 0.0f;
 #pragma unroll
     for (int ft = 0; ft < NT; ++ft) {
       f32x4_t acc = zero4();
@@ -203,15 +223,16 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int kc = 0; kc < DS; ++kc)
-          acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), bu[kc], acc);
+          acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), bm[kc], acc);
       // acc lane (s, grp) element r = sum_c T[f][c] u[token t0 + s][c], f = 16ft + 4grp + r
       const int f = 16 * ft + 4 * grp;
       if (tq >= 0 && f < d) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(X + off + (size_t)tq * d + f);
-        const float x[4] = {lo_f32(xv.x), hi_f32(xv.x), lo_f32(xv.y), hi_f32(xv.y)};
+        const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y),
+                            hi_f32(xv[ft].y)};
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (acc[r] * us + sz[f + r] * ue) * dphi_apply<PHI>(x[r]);
+        for (int r = 0; r < 4; ++r)
+          o[r] = (acc[r] * usm + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
         *reinterpret_cast<uint2*>(dX + off + (size_t)tq * d + f) =
             make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
       }
