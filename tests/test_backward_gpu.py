@@ -93,6 +93,7 @@ PAIRS_BACKWARD_CASES = [
     (2, 2, (1, 8, 8), (1, 4, 4), 48, PHI_RELU),      # M = 4: waves without a block
     (2, 2, (1, 10, 16), (1, 2, 8), 80, PHI_ELU1),    # d = 80, M = 10
     (2, 2, (1, 9, 15), (1, 3, 5), 48, PHI_ELU1),     # odd M = 9, 15-token blocks
+    (1, 3, (1, 16, 16), (1, 4, 4), 64, PHI_RELU),    # one batch item: dW written directly
 ]
 
 

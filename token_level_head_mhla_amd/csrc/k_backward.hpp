@@ -472,16 +472,19 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
                                                                            dden);
   // 4. dS = W^T-mixing of dS~
   launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, wc, st);
-  // 5. dW
+  // 5. dW (with one batch item the per-slice partials are dW itself)
+  float* Pd = B == 1 ? dW : P;
   if (M >= 256) {
     const unsigned nt = (unsigned)((M + 127) / 128);
-    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M);
   } else {
     const unsigned nt = (unsigned)((M + 15) / 16);
-    k_dw_partial16<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, P, M);
+    k_dw_partial16<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M);
   }
-  const long nw = (long)H * M * M;
-  k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
+  if (B > 1) {
+    const long nw = (long)H * M * M;
+    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
+  }
   // 6. dQ, against the precise S~
   launch_mix_f32<DP>(slices, H, M, S, W, St32, st);
   k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(

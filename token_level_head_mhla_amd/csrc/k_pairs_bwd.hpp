@@ -555,12 +555,16 @@ int launch_pairs_bwd_t(long slices, int B, int H, int N, int d, const Geo& g, co
       lds_limit_once(reinterpret_cast<const void*>(&k_pbwd_k<DK, DO, QB, PHI>), set_k,
                      160 * 1024) != 0)
     return -1;
+  // with one batch item the per-slice dW partials are dW itself
+  float* Pd = B == 1 ? dW : Pw;
   k_pbwd_q<DK, DO, QB, PHI><<<dim3((unsigned)slices), dim3(kPairsThreads), lq, st>>>(
-      Q, K, V, W, dY, dQ, dN, dNlo, dd, Pw, g, H, N, d);
+      Q, K, V, W, dY, dQ, dN, dNlo, dd, Pd, g, H, N, d);
   k_pbwd_k<DK, DO, QB, PHI><<<dim3((unsigned)slices), dim3(kPairsThreads), lk, st>>>(
       Q, K, V, W, dN, dNlo, dd, dK, dV, g, H, N, d);
-  const long nw = (long)H * M * M;
-  k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(Pw, dW, B, H, M);
+  if (B > 1) {
+    const long nw = (long)H * M * M;
+    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(Pw, dW, B, H, M);
+  }
   return 0;
 }
 
