@@ -19,10 +19,10 @@
 //   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
 //   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
 //   4. dS, dz         mixing GEMM with W transposed
-//   5. dW             k_dw_partial16 (M < 256) or k_dw_partial (per slice,
+//   5. dW             k_dw_partial16 (M <= 16) or k_dw_partial (per slice,
 //                     the rows of dS~ against the rows of S over all d*d + d
-//                     entries) and k_dw_reduce (sum over the batch, fixed
-//                     order: deterministic)
+//                     entries, in up to 8 parts) and k_dw_reduce (sum over
+//                     the parts and the batch, fixed order: deterministic)
 //   6. dQ             k_bwd_dphi: S~ staged in LDS and read transposed,
 //                     times G (exact bf16) on MFMA, scaled by 1/den per token
 //                     in fp32, plus z~ dden in fp32, times phi'(Q)
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
 }
 
 // ---------------------------------------------------------------------------
-// Step 5, M < 256.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e]
+// Step 5, M <= 16.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e]
 // B[slice][b][e] over the workspace rows (A = dS~, B = S).  grid =
 // (ceil(M/16)^2, slices),
 // block = 256: a 16 x 16 output tile per workgroup, the contraction split over
@@ -293,19 +293,24 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial16(const bf16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Step 5, M >= 256.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
-// over the workspace rows (A = dS~, B = S).  grid = (ceil(M/T)^2, slices),
-// block = 256: a T x T output tile per workgroup, a (T/2) x (T/2) quarter per
-// wave.  Both operands are contiguous in e,
-// so the MFMA fragments are 16-byte row reads of an LDS tile (no transpose);
-// 32-entry steps pass through a double-buffered tile, loaded one step ahead.
-// Each operand row is read once per T output columns (a 16 x 16 tile per
-// workgroup read every row once per 16 and moved 6.5 GB through L2 on the video
-// shape).  Rows past M are clamped on load and never stored.
+// Step 5, M > 16.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
+// over the workspace rows (A = dS~, B = S).  grid = (ceil(M/T)^2 * nsplit,
+// slices), block = 256: a T x T output tile per workgroup (T = 128 for
+// M >= 256, else 64), a (T/2) x (T/2) quarter per wave.  Both operands are
+// contiguous in e, so the MFMA fragments are 16-byte row reads of an LDS tile
+// (no transpose); 32-entry steps pass through a double-buffered tile, loaded
+// one step ahead.  Each operand row is read once per T output columns (the
+// 16 x 16-tile kernel above reads it once per 16: 6.5 GB through L2 and
+// 712 us on the video shape, against 122 us here).  For 16 < M < 256 the
+// contraction is split into nsplit parts (dw_split) that write separate
+// partial sums, so that the few 64 x 64 tiles still give enough workgroups
+// (4096-token image backward: 0.242 against 0.249 ms with the 16 x 16
+// kernel).  Rows past M are clamped on load and never stored.
 template <int DP, int T>
 __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __restrict__ A,
                                                             const bf16_t* __restrict__ Bm,
-                                                            float* __restrict__ P, int M) {
+                                                            float* __restrict__ P, int M,
+                                                            int nsplit, size_t pstride) {
   using D = BlockedDims<DP>;
   constexpr int EP = D::EP, E = DP * DP + DP, NSTEP = E / 32;
   static_assert(E % 32 == 0, "contraction steps");
@@ -321,7 +326,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
   const int wi = wave >> 1, wb = wave & 1;
   const long slice = blockIdx.y;
   const int nt = (M + T - 1) / T;
-  const int i0 = T * (blockIdx.x / nt), b0 = T * (blockIdx.x % nt);
+  // blockIdx.x = tile * nsplit + part: part takes steps [k0, k1) of the
+  // contraction and writes its partial sums at P + part * pstride
+  const int tile = blockIdx.x / nsplit, part = blockIdx.x - tile * nsplit;
+  const int i0 = T * (tile / nt), b0 = T * (tile % nt);
+  const int k0 = part * NSTEP / nsplit, k1 = (part + 1) * NSTEP / nsplit;
+  P += (size_t)part * pstride;
   // chunk u of a step: LDS row r = c / 4 (rows 0..T-1 hold A rows i0.., rows
   // T..2T-1 hold B rows b0..), 16-byte piece c % 4 of the step's 32 entries.
   // Rows past M are clamped in bounds; they feed outputs that are not stored.
@@ -349,14 +359,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
   for (int a = 0; a < FT; ++a)
 #pragma unroll
     for (int b = 0; b < FT; ++b) acc[a][b] = zero4();
-  gload(0);
+  gload(k0);
   lstore(0);
   lds_barrier();
-  // Step k reads LDS buffer k & 1; the loads of step k + 1 (clamped, never
-  // skipped) land in the other buffer after this step's fragment reads.
-  for (int k = 0; k < NSTEP; ++k) {
-    const int buf = k & 1;
-    gload(k + 1 < NSTEP ? k + 1 : k);
+  // Step k reads LDS buffer (k - k0) & 1; the loads of step k + 1 (clamped,
+  // never skipped) land in the other buffer after this step's fragment reads.
+  for (int k = k0; k < k1; ++k) {
+    const int buf = (k - k0) & 1;
+    gload(k + 1 < k1 ? k + 1 : k);
     // A fragment: row i (lane s), entries 8grp .. 8grp+7; B likewise for row b
     u16x8_t af[FT], bf[FT];
 #pragma unroll
@@ -386,9 +396,11 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
     }
 }
 
-// dW[h][i][b] = sum over the batch of P[batch * H + h][i][b], in batch order.
+// dW[h][i][b] = sum over the parts of the contraction and over the batch of
+// P[part][batch * H + h][i][b], in a fixed order (parts outer, batch inner).
 __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
-                                                   float* __restrict__ dW, int B, int H, int M) {
+                                                   float* __restrict__ dW, int B, int H, int M,
+                                                   int nsplit, size_t pstride) {
   const long e = (long)blockIdx.x * 256 + threadIdx.x;
   const long MM = (long)M * M;
   if (e >= (long)H * MM) return;
@@ -396,13 +408,26 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
   // eight partial sums in a fixed order (batch items b, b+8, ...), so that
   // eight loads are in flight at a time
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int b = 0;
-  for (; b + 8 <= B; b += 8) {
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* Ps = P + (size_t)sp * pstride;
+    int b = 0;
+    for (; b + 8 <= B; b += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += P[((long)(b + u) * H + h) * MM + ib];
+      for (int u = 0; u < 8; ++u) acc[u] += Ps[((long)(b + u) * H + h) * MM + ib];
+    }
+    for (int u = 0; b + u < B; ++u) acc[u] += Ps[((long)(b + u) * H + h) * MM + ib];
   }
-  for (int u = 0; b + u < B; ++u) acc[u] += P[((long)(b + u) * H + h) * MM + ib];
   dW[e] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// Parts of the dW contraction for 16 < M < 256, where the 64 x 64 tiles
+// alone give few workgroups (one per slice at M = 64): about 512 workgroups,
+// at most 8 parts.
+inline int dw_split(long slices, int M) {
+  if (M <= 16 || M >= 256) return 1;
+  const long tiles = slices * (long)((M + 63) / 64) * ((M + 63) / 64);
+  const long sp = (512 + tiles - 1) / tiles;
+  return (int)(sp < 1 ? 1 : (sp > 8 ? 8 : sp));
 }
 
 // ---------------------------------------------------------------------------
@@ -423,7 +448,8 @@ inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   const size_t al = 256;
   auto up = [&](size_t x) { return (x + al - 1) / al * al; };
   return 4 * up(rows) + 2 * up(rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
-         2 * up((size_t)slices * N * sizeof(float)) + up((size_t)slices * M * M * sizeof(float)) +
+         2 * up((size_t)slices * N * sizeof(float)) +
+         up((size_t)dw_split(slices, M) * slices * M * M * sizeof(float)) +
          mix_coef_bytes(H, M);
 }
 
@@ -453,7 +479,9 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   float* rq = reinterpret_cast<float*>(p);
   p += up((size_t)slices * N * sizeof(float));
   float* P = reinterpret_cast<float*>(p);
-  p += up((size_t)slices * M * M * sizeof(float));
+  const int nsp = dw_split(slices, M);
+  const size_t pstride = (size_t)slices * M * M;
+  p += up((size_t)nsp * pstride * sizeof(float));
   bf16_t* wc = reinterpret_cast<bf16_t*>(p);
   static_assert(sizeof(bf16_t) == 2, "bf16");
   if (2 * up(rows * sizeof(bf16_t)) != 2 * rows * sizeof(bf16_t)) {
@@ -472,18 +500,25 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
                                                                            dden);
   // 4. dS = W^T-mixing of dS~
   launch_mix<DP>(slices, H, M, dSt, W, dS, kMixTransposed, wc, st);
-  // 5. dW (with one batch item the per-slice partials are dW itself)
-  float* Pd = B == 1 ? dW : P;
+  // 5. dW (with one batch item and one part the partials are dW itself)
+  const bool direct = B == 1 && nsp == 1;
+  float* Pd = direct ? dW : P;
   if (M >= 256) {
     const unsigned nt = (unsigned)((M + 127) / 128);
-    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M);
+    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M, 1,
+                                                                      pstride);
+  } else if (M > 16) {
+    const unsigned nt = (unsigned)((M + 63) / 64);
+    k_dw_partial<DP, 64><<<dim3(nt * nt * nsp, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M, nsp,
+                                                                          pstride);
   } else {
     const unsigned nt = (unsigned)((M + 15) / 16);
     k_dw_partial16<DP><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M);
   }
-  if (B > 1) {
+  if (!direct) {
     const long nw = (long)H * M * M;
-    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M);
+    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M, nsp,
+                                                                    pstride);
   }
   // 6. dQ, against the precise S~
   launch_mix_f32<DP>(slices, H, M, S, W, St32, st);

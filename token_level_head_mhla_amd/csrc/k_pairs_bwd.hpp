@@ -563,7 +563,7 @@ int launch_pairs_bwd_t(long slices, int B, int H, int N, int d, const Geo& g, co
       Q, K, V, W, dN, dNlo, dd, dK, dV, g, H, N, d);
   if (B > 1) {
     const long nw = (long)H * M * M;
-    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(Pw, dW, B, H, M);
+    k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(Pw, dW, B, H, M, 1, 0);
   }
   return 0;
 }
