@@ -5,11 +5,20 @@ One step = one mhla_forward call: the whole hot path (block summaries,
 multi-head mixing, readout) over one batch of seeded synthetic input that is
 already resident in HBM.  Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload deit_t] [--path auto]
+  python bench.py [--steps K] [--warmup W] [--workload video] [--path auto]
 
-The default workload is the DeiT-T-shaped bf16 case (B64 H3 N196 as a 14x14
-grid of 7x7 blocks, so M=4; d64; elu+1).  The other workloads (tiny,
-dit_xl2, hires, video) can be selected for study.
+The default workload is the video-latent case (B1 H24 N32768 as an 8x64x64
+grid of 1x8x8 blocks, so M=512; d64; elu+1), the largest configuration and
+the one where the M^2 d^2 mixing term dominates.  The other workloads (tiny,
+deit_t, dit_xl2, hires, lm_causal) can be selected for study.
+
+Timing: the K steps are enqueued back to back from arguments marshalled once
+(no Python checks inside the loop) and bracketed by HIP events on the launch
+stream; `ms_per_step` and `value` come from that bracket.  A second run of at
+least 50 calls records events around every kernel launch of every call
+(mhla_forward_profiled): the median call time and each kernel's median launch
+time come from it, and the roofline object is that of the kernel with the
+largest median time.
 
   python bench.py --copy-mb 256
 
@@ -19,6 +28,7 @@ scaling the HBM byte counters of a profiler run).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -28,7 +38,9 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
 METRIC = "MHLA fwd tokens/s per GPU and % of bf16 MFMA / HBM roofline"
+MIN_PROFILED_CALLS = 50
 
 
 def parse():
@@ -36,10 +48,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="deit_t")
+    ap.add_argument("--workload", default="video")
     ap.add_argument("--path", default="auto",
                     choices=["auto", "generic", "fused", "pairs", "blocked", "columns"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-core", action="store_true",
+                    help="skip the single-core oracle timings of the four smaller workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -50,6 +64,33 @@ def parse():
                     help="time token-by-token causal inference (mhla_decode_step) over the "
                          "workload's sequence instead (1-D chunked workloads, e.g. lm_causal)")
     return ap.parse_args()
+
+
+class HipEvents:
+    """A pool of timing events of the HIP runtime (the same runtime torch
+    uses), created once; elapsed() reads the time between two of them."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def elapsed(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.ev = []
 
 
 def copy_bench(args):
@@ -71,6 +112,53 @@ def copy_bench(args):
     print(json.dumps({"copy_bytes_each_way": n * 4, "steps": args.steps, "ms_per_copy": ms,
                       "GBs_read_plus_write": 2 * n * 4 / (ms / 1e3) / 1e9}), flush=True)
     return 0
+
+
+def kernel_work(name, wl, path_name):
+    """(bytes, flops) that one launch of kernel `name` must move and compute on
+    workload wl, by design: its own inputs read once and outputs written once
+    (the block summary tables S and S~ count for the kernels that write and
+    read them), and the method's flops of its step (summaries and readout
+    2*N*d^2, mixing 2*M^2*d^2 per slice).  Single-kernel paths move exactly
+    the algorithmic bytes of the call."""
+    S = wl.B * wl.H
+    T = S * wl.N * wl.d * wl.elt_bytes                 # one of Q, K, V, Y
+    ws_elt = 4 if path_name == "generic" else 2
+    E = S * wl.M * (wl.d * wl.d + wl.d) * ws_elt        # one summary table
+    Wb = wl.H * wl.M * wl.M * 4
+    f_side = 2 * wl.N * wl.d * wl.d * S                 # summaries or readout
+    f_mix = 2 * wl.M * wl.M * wl.d * wl.d * S
+    if name in ("k_fused", "k_pairs", "k_cols"):
+        return wl.algorithmic_bytes(), wl.algorithmic_flops()
+    if name.startswith("k_summary"):
+        return 2 * T + E, f_side
+    if name == "k_mix_coef":
+        return Wb + Wb // 2, 0
+    if name == "k_mix_big":
+        return 2 * E + Wb // 2, f_mix
+    if name.startswith("k_mix"):
+        return 2 * E + Wb, f_mix
+    if name == "k_readout_causal":
+        return 4 * T + E, f_side + 2 * wl.N * wl.nb * wl.d * S
+    if name.startswith("k_readout"):
+        return 2 * T + E, f_side
+    return 0, 0
+
+
+def roofline_entry(nbytes, flops, ms, fp32=False):
+    """Fractions of the HBM and the matrix-core (or fp32 vector) peak for one
+    kernel or call; the binding one is the larger."""
+    gbs = nbytes / (ms / 1e3) / 1e9
+    peak_f = FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS
+    tfs = flops / (ms / 1e3) / 1e12
+    if gbs / HBM_PEAK_GBS >= tfs / peak_f:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        r = {"bound": "alu" if fp32 else "mfma", "achieved": round(tfs, 1), "peak": peak_f,
+             "unit": "TFLOP/s", "frac": round(tfs / peak_f, 4)}
+    r.update({"hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "flop_frac": round(tfs / peak_f, 4)})
+    return r
 
 
 def main():
@@ -101,11 +189,6 @@ def main():
         path = m.mhla_plan_ex(wl.B, wl.H, wl.N, wl.d, m.BlockShape.make(*shape), wl.phi,
                               wl.dtype, wl.flags)
     path_name = {1: "generic", 2: "fused", 3: "pairs", 4: "blocked", 5: "columns"}[path]
-    kernels = {1: ["k_summary_valu", "k_mix_valu", "k_readout_valu"], 2: ["k_fused"],
-               3: ["k_pairs"], 4: ["k_summary_mfma", "k_mix_mfma", "k_readout_mfma"],
-               5: ["k_cols"]}[path]
-    if wl.causal:
-        kernels = ["k_summary_mfma", "k_mix_mfma", "k_readout_causal"]
 
     inp = make_inputs(wl)
 
@@ -119,46 +202,67 @@ def main():
     out = torch.empty_like(q)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()  # the stream the library launches on
-
-    def step():
-        m.mhla_forward_ex(q, k, v, w, out, shape, wl.phi, wl.flags, path, stream=stream)
+    call = m.PreparedForward(q, k, v, w, out, shape, wl.phi, wl.flags, path, stream=stream)
 
     for _ in range(args.warmup):
-        step()
+        call.call()
     torch.cuda.synchronize()
-    # HIP events recorded on the launch stream bracket exactly the K steps.
+    # K steps back to back, bracketed by HIP events on the launch stream; the
+    # host's enqueue time is measured alongside.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    h0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        call.call()
+    host_s = time.perf_counter() - h0
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     tokens = wl.B * wl.N
     value = tokens / (ms / 1e3)
 
+    # Per-call and per-launch times: >= 50 profiled calls, each with its own
+    # events, enqueued back to back.
+    nprof = max(args.steps, MIN_PROFILED_CALLS)
+    per = m.MHLA_MAX_LAUNCHES + 1
+    pool = HipEvents(per * nprof)
+    names = None
+    for c in range(nprof):
+        names = call.profiled(pool.ev[c * per:(c + 1) * per])
+    torch.cuda.synchronize()
+    nl = len(names)
+    launch_ms = np.array([[pool.elapsed(pool.ev[c * per + j], pool.ev[c * per + j + 1])
+                           for j in range(nl)] for c in range(nprof)])
+    call_ms = np.array([pool.elapsed(pool.ev[c * per], pool.ev[c * per + nl])
+                        for c in range(nprof)])
+    pool.close()
+    med_call = float(np.median(call_ms))
+    kernels = []
+    for j, nm in enumerate(names):
+        kb, kf = kernel_work(nm, wl, path_name)
+        t = float(np.median(launch_ms[:, j]))
+        e = {"kernel": nm, "median_us": round(t * 1e3, 3), "bytes": kb, "flops": kf}
+        e.update(roofline_entry(kb, kf, t, fp32=(path_name == "generic")))
+        kernels.append(e)
+    dom = max(range(nl), key=lambda j: kernels[j]["median_us"])
+    dk = kernels[dom]
+    roofline = {k_: dk[k_] for k_ in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline.update({
+        "kernel": dk["kernel"],
+        "traffic": measured_traffic(path_name, wl.name, dk["kernel"]),
+        "avg_launch_us": round(float(np.mean(launch_ms[:, dom])) * 1e3, 3),
+        "median_launch_us": dk["median_us"],
+        "work_per_launch": {"bytes": dk["bytes"], "flops": dk["flops"]},
+        "launches_timed": nprof,
+    })
     alg_bytes = wl.algorithmic_bytes()
     alg_flops = wl.algorithmic_flops()
-    hbm_frac = alg_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
-    mfma_frac = alg_flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS
-    bound = "hbm" if hbm_frac >= mfma_frac else "mfma"
-    if bound == "hbm":
-        achieved, peak, unit = alg_bytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved, peak, unit = alg_flops / (ms / 1e3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
-    roofline = {
-        "bound": bound,
-        "kernel": kernels[0] if len(kernels) == 1 else "+".join(kernels),
-        "achieved": round(achieved, 1),
-        "peak": peak,
-        "unit": unit,
-        "frac": round(achieved / peak, 4),
-        "traffic": measured_traffic(kernels[0], wl.name) if len(kernels) == 1 else None,
-        "algorithmic_bytes_per_launch": alg_bytes,
-        "algorithmic_flops_per_launch": alg_flops,
-        "avg_launch_us": round(ms * 1e3, 3),
-    }
+    whole = roofline_entry(alg_bytes, alg_flops, med_call)
+    whole.update({"median_call_us": round(med_call * 1e3, 3),
+                  "algorithmic_bytes_per_call": alg_bytes,
+                  "algorithmic_flops_per_call": alg_flops,
+                  "traffic": measured_traffic(path_name, wl.name, None)})
 
     result = {
         "metric": METRIC,
@@ -183,10 +287,22 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": roofline,
+        "call_roofline": whole,
+        "kernels": kernels,
+        "timing": {
+            "bracket_ms_per_step": round(ms, 6),
+            "median_profiled_call_ms": round(med_call, 6),
+            "host_enqueue_us_per_call": round(host_s / args.steps * 1e6, 2),
+            "host_calls_per_s": round(args.steps / host_s, 1),
+            "launch_overhead_frac": round(max(0.0, (ms - med_call) / ms), 4),
+        },
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(inp, out, args.cpu_seconds)
+        if not args.no_single_core:
+            result["cpu_baseline_single_core"] = single_core_baselines(
+                [n for n in ("tiny", "deit_t", "dit_xl2", "hires") if n != wl.name])
 
     print(json.dumps(result), flush=True)
     return 0
@@ -312,73 +428,125 @@ def decode_bench(args):
     return 0
 
 
-# Sources that define each roofline kernel; a committed byte count applies only
-# while these files are unchanged.
-KERNEL_SOURCES = {"k_fused": ["k_fused.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
-                  "k_cols": ["k_cols.hpp", "mhla_mfma.hpp", "mhla_common.hpp"]}
+# Sources of each path's kernels: a committed byte count applies only while
+# these files are unchanged.
+PATH_SOURCES = {
+    "fused": ["k_fused.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+    "columns": ["k_cols.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+    "pairs": ["k_pairs.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+    "blocked": ["k_blocked.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+}
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary for this kernel and workload, or None when there is none or the
-    kernel's sources changed since it was taken."""
+def sources_digest(path_name):
     import hashlib
-    import re
     root = os.path.dirname(os.path.abspath(__file__))
-    summary = os.path.join(root, "profiles", "%s_%s_hbm_bytes.md" % (kernel, workload))
-    if kernel not in KERNEL_SOURCES or not os.path.exists(summary):
-        return None
-    text = open(summary).read()
-    nbytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    digest = re.search(r"source_sha256_16: ([0-9a-f]{16})", text)
-    if not nbytes or not digest:
-        return None
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[kernel]:
+    for name in PATH_SOURCES[path_name]:
         with open(os.path.join(root, "token_level_head_mhla_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    return int(nbytes.group(1)) if h.hexdigest()[:16] == digest.group(1) else None
+    return h.hexdigest()[:16]
 
 
-def cpu_baseline(inp, out_dev, target_s):
-    """The fp64 oracle (blockwise C, OpenMP over slices) timed on this host on
-    a bounded sample of the same workload; also reports the GPU output's error
-    on that sample."""
+def measured_traffic(path_name, workload, kernel):
+    """HBM bytes per launch of `kernel` (per call when kernel is None) from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of this path and
+    workload, or None when there is none or the path's sources changed since
+    it was taken."""
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    summary = os.path.join(root, "profiles", "%s_%s_hbm_bytes.md" % (path_name, workload))
+    if path_name not in PATH_SOURCES or not os.path.exists(summary):
+        return None
+    text = open(summary).read()
+    digest = re.search(r"source_sha256_16: ([0-9a-f]{16})", text)
+    if not digest or digest.group(1) != sources_digest(path_name):
+        return None
+    if kernel is None:
+        key = "traffic_bytes_per_call"
+    else:
+        key = "traffic_bytes_per_launch\\[%s\\]" % kernel
+    nbytes = re.search(key + r": (\d+)", text)
+    return int(nbytes.group(1)) if nbytes else None
+
+
+def _slice_inputs(inp, s0, s1):
+    """fp64 Q, K, V of slices [s0, s1) (flattened over batch and head) as
+    [1, s1-s0, N, d], and the matching per-slice W."""
+    wl = inp.wl
+    S = wl.B * wl.H
+    flat = lambda x: x.reshape(S, wl.N, wl.d)[s0:s1][None]
+    q, k, v = (inp.as_f64(flat(x)) for x in (inp.q, inp.k, inp.v))
+    w = inp.w_f64[np.arange(s0, s1) % wl.H]
+    return q, k, v, w
+
+
+def time_oracle(inp, target_s, nthreads):
+    """Times the fp64 blockwise oracle on a bounded sample of whole slices of
+    the workload (repeated when one pass is short).  Returns (tokens/s,
+    threads used, slices, runs, seconds, the sample's output)."""
     import oracle
     wl = inp.wl
-    q, k, v, w = inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64
-    threads = oracle.threads()
-    # size the sample (whole batch items, all heads) for about target_s seconds
+    S = wl.B * wl.H
+    q, k, v, w = _slice_inputs(inp, 0, 1)
     t0 = time.perf_counter()
-    oracle.blockwise(q[:1, :1], k[:1, :1], v[:1, :1], w[:1], wl.grid, wl.block, wl.phi,
-                     norm=wl.norm, causal=wl.causal)
+    oracle.blockwise(q, k, v, w, wl.grid, wl.block, wl.phi, nthreads=nthreads, norm=wl.norm,
+                     causal=wl.causal)
     per_slice = max(time.perf_counter() - t0, 1e-6)
-    n_b = max(1, min(wl.B, int(target_s * threads / per_slice / wl.H)))
+    threads = oracle.threads() if nthreads <= 0 else nthreads
+    ns = max(1, min(S, int(target_s * threads / per_slice)))
+    if threads > 1:
+        ns = min(S, max(ns, threads) // threads * threads)  # whole rounds of the thread pool
+    q, k, v, w = _slice_inputs(inp, 0, ns)
     reps, elapsed, ref = 0, 0.0, None
     while True:
         t0 = time.perf_counter()
-        ref = oracle.blockwise(q[:n_b], k[:n_b], v[:n_b], w, wl.grid, wl.block, wl.phi,
+        ref = oracle.blockwise(q, k, v, w, wl.grid, wl.block, wl.phi, nthreads=nthreads,
                                norm=wl.norm, causal=wl.causal)
         elapsed += time.perf_counter() - t0
         reps += 1
         if elapsed >= 0.8 * target_s or reps >= 2000:
             break
-    tokens = reps * n_b * wl.N
-    y = out_dev[:n_b].float().cpu().numpy().astype(np.float64)
-    num = np.abs(y - ref).reshape(n_b * wl.H, -1).max(axis=1)
-    den = np.abs(ref).reshape(n_b * wl.H, -1).max(axis=1)
+    return reps * ns * wl.N / elapsed, threads, ns, reps, elapsed, ref
+
+
+def cpu_baseline(inp, out_dev, target_s):
+    """The fp64 oracle (blockwise C, OpenMP over slices, all host threads)
+    timed on this host on a bounded sample of whole slices of the same
+    workload; also reports the GPU output's error on that sample."""
+    wl = inp.wl
+    S = wl.B * wl.H
+    rate, threads, ns, reps, elapsed, ref = time_oracle(inp, target_s, 0)
+    y = out_dev.reshape(S, wl.N, wl.d)[:ns].float().cpu().numpy().astype(np.float64)
+    ref = ref.reshape(ns, -1)
+    num = np.abs(y.reshape(ns, -1) - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
     err = float((num / np.where(den == 0, 1, den)).max())
     base = {
-        "value": round(tokens / elapsed, 1),
+        "value": round(rate, 1),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "fp64 blockwise oracle on batch items 0..%d of %d (all %d heads), %d run(s), "
-                  "%.1f s wall" % (n_b - 1, wl.B, wl.H, reps, elapsed),
+        "sample": "fp64 blockwise oracle on %d of the %d (batch, head) slices (%d tokens each), "
+                  "%d run(s), %.1f s wall, %d threads" % (ns, S, wl.N, reps, elapsed, threads),
     }
-    parity = {"max_slice_rel_err": err, "slices_checked": n_b * wl.H,
+    parity = {"max_slice_rel_err": err, "slices_checked": ns,
               "gate": 1e-5 if wl.dtype == 0 else 1e-2}
     return base, parity
+
+
+def single_core_baselines(names, target_s=2.5):
+    """The same oracle on one thread, on bounded samples of the smaller
+    workloads (their throughput per core)."""
+    from mhla_inputs import WORKLOADS, make_inputs
+    res = []
+    for name in names:
+        inp = make_inputs(WORKLOADS[name])
+        rate, threads, ns, reps, elapsed, _ = time_oracle(inp, target_s, 1)
+        res.append({"workload": name, "value": round(rate, 1), "unit": "tokens/s", "cores": 1,
+                    "kind": "oracle", "sample": "%d of %d slices, %d run(s), %.2f s" % (
+                        ns, inp.wl.B * inp.wl.H, reps, elapsed)})
+    return res
 
 
 if __name__ == "__main__":

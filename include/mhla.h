@@ -28,10 +28,10 @@
  *     per-row scale cancels in the output.
  *   - All pointers are caller-owned; the library never frees them.  Device
  *     pointers must be 16-byte aligned.
- *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
- *     enqueued asynchronously; no host or device-wide synchronisation happens
- *     (except when the library's workspace has to grow, which synchronises the
- *     device once).
+ *   - stream: a hipStream_t (mhla_stream_t below is the same type; NULL = the
+ *     null stream).  Work is enqueued asynchronously; no host or device-wide
+ *     synchronisation happens (except when the library's workspace for that
+ *     (device, stream) has to grow, which synchronises the stream once).
  *   - Argument and shape errors are detected on the host before anything is
  *     enqueued; the return code says which (MHLA_ERR_*), and
  *     mhla_last_error() gives a message for the calling thread.
@@ -46,6 +46,12 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP runtime's stream handle: hip_runtime_api.h defines hipStream_t as
+ * a pointer to this opaque struct, so a hipStream_t converts to mhla_stream_t
+ * without a cast, and this header needs no HIP include. */
+struct ihipStream_t;
+typedef struct ihipStream_t* mhla_stream_t;
 
 typedef struct mhla_block_shape {
   int ndim;      /* 1, 2 or 3: how many trailing grid axes are in use        */
@@ -102,14 +108,14 @@ enum {
 int mhla_forward(const void* Q, const void* K, const void* V, const float* Wmix,
                  void* out, int B, int H, int N, int d,
                  const mhla_block_shape* block_shape, int phi_kind, int dtype,
-                 void* stream);
+                 mhla_stream_t stream);
 
 /* Same as mhla_forward with an explicit kernel path.  A path that does not
  * support the shape returns MHLA_ERR_UNSUPPORTED without enqueuing work. */
 int mhla_forward_path(const void* Q, const void* K, const void* V,
                       const float* Wmix, void* out, int B, int H, int N, int d,
                       const mhla_block_shape* block_shape, int phi_kind,
-                      int dtype, int path, void* stream);
+                      int dtype, int path, mhla_stream_t stream);
 
 /* mhla_forward_path with option bits (MHLA_FLAG_*; 0 = mhla_forward_path).
  * Unknown bits return MHLA_ERR_INVALID_ARG; a causal call whose blocks are not
@@ -118,7 +124,30 @@ int mhla_forward_path(const void* Q, const void* K, const void* V,
 int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wmix,
                     void* out, int B, int H, int N, int d,
                     const mhla_block_shape* block_shape, int phi_kind, int dtype,
-                    int flags, int path, void* stream);
+                    int flags, int path, mhla_stream_t stream);
+
+/* Upper bound on the kernel launches of one forward call (any path and
+ * options). */
+#define MHLA_MAX_LAUNCHES 8
+
+/* mhla_forward_ex that also records HIP events around its kernel launches,
+ * for measuring each kernel of a call (timing only; the results are those of
+ * mhla_forward_ex).  events: max_events caller-created hipEvent_t handles
+ * (passed as void*), max_events >= MHLA_MAX_LAUNCHES + 1.  events[0] is
+ * recorded on `stream` before the first launch and events[k] right after the
+ * k-th launch, so hipEventElapsedTime(events[k-1], events[k]) spans launch k
+ * (plus any gap before it).  On success *n_launches = the number of launches
+ * and, when names is not NULL (MHLA_MAX_LAUNCHES entries), names[k-1] points
+ * at the static name of launch k's kernel.  Errors are those of
+ * mhla_forward_ex, plus MHLA_ERR_INVALID_ARG for a NULL events array or
+ * n_launches, or max_events below the bound; nothing is enqueued or recorded
+ * on error. */
+int mhla_forward_profiled(const void* Q, const void* K, const void* V,
+                          const float* Wmix, void* out, int B, int H, int N,
+                          int d, const mhla_block_shape* block_shape,
+                          int phi_kind, int dtype, int flags, int path,
+                          void* const* events, int max_events, int* n_launches,
+                          const char** names, mhla_stream_t stream);
 
 /* The path MHLA_PATH_AUTO picks for these sizes and option bits (host only),
  * or -code for the error mhla_forward_ex would return before any launch. */
@@ -152,7 +181,7 @@ int mhla_lb_init(const mhla_block_shape* block_shape, float* W, size_t capacity)
 int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix,
                   const void* dY, void* dQ, void* dK, void* dV, float* dWmix,
                   int B, int H, int N, int d, const mhla_block_shape* block_shape,
-                  int phi_kind, int dtype, int flags, void* stream);
+                  int phi_kind, int dtype, int flags, mhla_stream_t stream);
 
 /* Incremental (streaming) inference of the causal form (MHLA paper App. C,
  * "Causal inference"): one new token per (batch, head) slice per call.  The
@@ -180,7 +209,7 @@ int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix
 size_t mhla_decode_state_bytes(int B, int H, int d, int M);
 int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix,
                      void* y, void* state, int B, int H, int d, int M, int nb, int t,
-                     int phi_kind, int dtype, int flags, void* stream);
+                     int phi_kind, int dtype, int flags, mhla_stream_t stream);
 
 /* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
  * would return for these sizes. */
@@ -194,11 +223,21 @@ int mhla_plan(int B, int H, int N, int d, const mhla_block_shape* block_shape,
 /* Number of blocks M for a valid shape, or -code. */
 int mhla_num_blocks(int N, const mhla_block_shape* block_shape);
 
-/* Device workspace in bytes that `path` needs for these sizes (0 when the
- * path keeps its intermediates on chip).  Returns 0 for invalid sizes. */
+/* Device workspace in bytes that mhla_forward needs for these sizes (the
+ * path MHLA_PATH_AUTO picks, no option bits; 0 when that path keeps its
+ * intermediates on chip).  Returns 0 for invalid sizes.  Host only.  The
+ * library allocates and caches this workspace itself (one buffer per device
+ * and stream, freed by mhla_release); the query tells a caller how much
+ * device memory a call will hold. */
 size_t mhla_workspace_bytes(int B, int H, int N, int d,
-                            const mhla_block_shape* block_shape, int dtype,
-                            int path);
+                            const mhla_block_shape* block_shape, int dtype);
+
+/* mhla_workspace_bytes for mhla_forward_ex's option bits and kernel path.
+ * Returns 0 for invalid sizes or options, and for a path that does not take
+ * the shape. */
+size_t mhla_workspace_bytes_ex(int B, int H, int N, int d,
+                               const mhla_block_shape* block_shape, int dtype,
+                               int flags, int path);
 
 /* Static description of a code; never NULL. */
 const char* mhla_error_string(int code);

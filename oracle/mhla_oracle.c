@@ -222,6 +222,9 @@ int oracle_mhla_rows(const double* Q, const double* K, const double* V,
    * blocks are consecutive runs, which the caller checks with blockwise */
   const int jmax_causal = (flags & ORACLE_CAUSAL) != 0;
   size_t sl = (size_t)N * d;
+  if (nrows < 0 || (nrows > 0 && rows == NULL)) return -1;
+  for (int r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= (long)B * H * N) return -1;
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 1)
 #endif

@@ -84,14 +84,14 @@ def test_plan_and_workspace():
     wl = WORKLOADS["deit_t"]
     bs = m.BlockShape.make(wl.grid, wl.block)
     assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) == m.MHLA_PATH_FUSED
-    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_FUSED) == 0
+    assert m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 0, m.MHLA_PATH_FUSED) == 0
     L = wl.d * wl.d + wl.d
-    assert (m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_GENERIC)
+    assert (m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 0, m.MHLA_PATH_GENERIC)
             == 2 * wl.B * wl.H * wl.M * L * 4)
     # the fused path refuses shapes it cannot hold on chip
     wl = WORKLOADS["video"]
     bs = m.BlockShape.make(wl.grid, wl.block)
-    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_FUSED) == 0
+    assert m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 0, m.MHLA_PATH_FUSED) == 0
     assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) != m.MHLA_PATH_FUSED
     assert m.mhla_plan(0, 1, 64, 16, m.BlockShape.make((8, 8), (4, 4)), 0, 0) < 0
 
@@ -103,7 +103,7 @@ def test_columns_path_host_checks():
     wl = WORKLOADS["hires"]
     bs = m.BlockShape.make(wl.grid, wl.block)
     assert m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) == m.MHLA_PATH_BLOCKED
-    assert m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, m.MHLA_PATH_COLUMNS) == 0
+    assert m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 0, m.MHLA_PATH_COLUMNS) == 0
     for name in WORKLOADS:
         w = WORKLOADS[name]
         b = m.BlockShape.make(w.grid, w.block)
@@ -269,3 +269,110 @@ def test_decode_state_bytes_and_rejects():
                                 None) == m.MHLA_ERR_ALIAS
     assert lib.mhla_decode_step(q, k, v, w, y, None, 1, 1, 16, 4, 8, 0, 0, 1, 0,
                                 None) == m.MHLA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- the contract's signatures
+
+# The boundary calls, with the argument types of the method's statement of
+# the problem: tensors as plain device pointers, sizes as ints, the block
+# shape as a struct, a HIP stream.
+CONTRACT_C = r"""
+#include "mhla.h"
+typedef struct ihipStream_t* hipStream_t;   /* as hip_runtime_api.h defines it */
+int (*f_forward)(const void*, const void*, const void*, const float*, void*, int, int, int, int,
+                 const mhla_block_shape*, int, int, hipStream_t) = mhla_forward;
+int (*f_validate)(int, int, int, int, const mhla_block_shape*, int, int) = mhla_validate;
+size_t (*f_ws)(int, int, int, int, const mhla_block_shape*, int) = mhla_workspace_bytes;
+const char* (*f_err)(int) = mhla_error_string;
+void (*f_release)(void) = mhla_release;
+int (*f_ex)(const void*, const void*, const void*, const float*, void*, int, int, int, int,
+            const mhla_block_shape*, int, int, int, int, hipStream_t) = mhla_forward_ex;
+"""
+
+CONTRACT_CXX = r"""
+#include <hip/hip_runtime_api.h>
+#include <type_traits>
+#include "mhla.h"
+static_assert(std::is_same<mhla_stream_t, hipStream_t>::value, "stream type");
+static_assert(std::is_same<decltype(&mhla_forward),
+    int (*)(const void*, const void*, const void*, const float*, void*, int, int, int, int,
+            const mhla_block_shape*, int, int, hipStream_t)>::value, "mhla_forward");
+static_assert(std::is_same<decltype(&mhla_workspace_bytes),
+    size_t (*)(int, int, int, int, const mhla_block_shape*, int)>::value, "workspace");
+static_assert(std::is_same<decltype(&mhla_validate),
+    int (*)(int, int, int, int, const mhla_block_shape*, int, int)>::value, "validate");
+int main() { return 0; }
+"""
+
+
+def _compile(tmp_path, name, text, cmd):
+    import subprocess
+    src = tmp_path / name
+    src.write_text(text)
+    res = subprocess.run(cmd + [str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_header_signatures_compile_as_c(tmp_path):
+    """A C compiler accepts pointers of the boundary's exact function types to
+    the declared entry points (an incompatible pointer type is an error)."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    _compile(tmp_path, "contract.c", CONTRACT_C,
+             ["gcc", "-std=c11", "-fsyntax-only", "-Werror=incompatible-pointer-types",
+              "-Wall", "-Werror", "-Wno-unused-variable", "-I", os.path.join(ROOT, "include")])
+
+
+def test_header_stream_type_is_hip_stream(tmp_path):
+    """With the HIP runtime header included first, mhla_stream_t is hipStream_t
+    and the boundary's signatures are the declared ones."""
+    import shutil
+    inc = "/opt/rocm/include"
+    if shutil.which("g++") is None or not os.path.exists(os.path.join(inc, "hip")):
+        pytest.skip("no g++ or HIP headers")
+    _compile(tmp_path, "contract.cpp", CONTRACT_CXX,
+             ["g++", "-std=c++17", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I", inc,
+              "-I", os.path.join(ROOT, "include")])
+
+
+def test_workspace_queries():
+    """mhla_workspace_bytes is the AUTO path's need; the _ex form takes option
+    bits and a path."""
+    for name in ("deit_t", "dit_xl2", "hires", "video"):
+        wl = WORKLOADS[name]
+        bs = m.BlockShape.make(wl.grid, wl.block)
+        a = m.mhla_workspace_bytes(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype)
+        b = m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 0, m.MHLA_PATH_AUTO)
+        assert a == b
+        if m.mhla_plan(wl.B, wl.H, wl.N, wl.d, bs, wl.phi, wl.dtype) == m.MHLA_PATH_BLOCKED:
+            assert a > 0
+        else:
+            assert a == 0
+    assert m.mhla_workspace_bytes(0, 1, 64, 16, m.BlockShape.make((8, 8), (4, 4)), 0) == 0
+    wl = WORKLOADS["lm_causal"]
+    bs = m.BlockShape.make(wl.grid, wl.block)
+    assert m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, 8, 0) == 0  # bad flag
+    assert m.mhla_workspace_bytes_ex(wl.B, wl.H, wl.N, wl.d, bs, wl.dtype, wl.flags, 0) > 0
+
+
+def test_profiled_rejects_before_any_launch():
+    lib = m.load_library()
+    bs = m.BlockShape.make((1, 8, 8), (1, 4, 4))
+    buf = (ctypes.c_char * (64 * 16 * 2 * 8 + 64))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    sz = 64 * 16 * 2
+    args = (base, base + sz, base + 2 * sz, base + 3 * sz, base + 5 * sz, 1, 1, 64, 16,
+            ctypes.byref(bs), 0, 1, 0, 0)
+    n = ctypes.c_int(-1)
+    fake = (ctypes.c_void_p * (m.MHLA_MAX_LAUNCHES + 1))(*([1] * (m.MHLA_MAX_LAUNCHES + 1)))
+    # too few event handles, a NULL array, a NULL count, a NULL handle
+    assert lib.mhla_forward_profiled(*args, fake, m.MHLA_MAX_LAUNCHES, ctypes.byref(n), None,
+                                     None) == m.MHLA_ERR_INVALID_ARG
+    assert lib.mhla_forward_profiled(*args, None, 9, ctypes.byref(n), None,
+                                     None) == m.MHLA_ERR_INVALID_ARG
+    assert lib.mhla_forward_profiled(*args, fake, 9, None, None, None) == m.MHLA_ERR_INVALID_ARG
+    fake[3] = None
+    assert lib.mhla_forward_profiled(*args, fake, 9, ctypes.byref(n), None,
+                                     None) == m.MHLA_ERR_INVALID_ARG
+    assert n.value == -1

@@ -1,7 +1,6 @@
 """Host-side logic of bench.py (CPU only): the one-GPU guard, the roofline
-object of a whole call, and the committed HBM byte counts keyed to the
-kernel sources."""
-import hashlib
+objects, the per-kernel work table and the committed HBM byte counts keyed
+to the kernel sources."""
 import json
 import os
 import subprocess
@@ -12,6 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
+from mhla_inputs import WORKLOADS  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
@@ -36,23 +36,46 @@ def test_roofline_of_call_reports_the_binding_fraction(gbs, tfs, bound):
     json.dumps(r)
 
 
-def _source_digest(kernel):
-    h = hashlib.sha256()
-    for name in bench.KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "token_level_head_mhla_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+@pytest.mark.parametrize("nbytes,flops,bound", [(8e9, 1e9, "hbm"), (1e6, 2.5e12, "mfma")])
+def test_roofline_entry(nbytes, flops, bound):
+    r = bench.roofline_entry(nbytes, flops, 1.0)   # 1 ms
+    assert r["bound"] == bound
+    assert r["frac"] == max(r["hbm_frac"], r["flop_frac"])
+    assert r["achieved"] / r["peak"] == pytest.approx(r["frac"], rel=1e-3)
+    f = bench.roofline_entry(1.0, 157.3e9, 1.0, fp32=True)
+    assert f["bound"] == "alu" and f["frac"] == pytest.approx(1.0)
+
+
+def test_kernel_work_adds_up_to_the_algorithmic_flops():
+    """The step kernels' flops sum to the method's flops of a call; the
+    single-kernel paths move exactly the algorithmic bytes; the blocked path's
+    kernels move the summary tables on top of them."""
+    wl = WORKLOADS["video"]
+    names = ["k_summary_mfma", "k_mix_coef", "k_mix_big", "k_readout_mfma"]
+    work = [bench.kernel_work(n, wl, "blocked") for n in names]
+    assert sum(f for _, f in work) == wl.algorithmic_flops()
+    assert sum(b for b, _ in work) > wl.algorithmic_bytes()
+    assert work[2][1] == 2 * wl.M ** 2 * wl.d ** 2 * wl.B * wl.H
+    wl = WORKLOADS["deit_t"]
+    assert bench.kernel_work("k_fused", wl, "fused") == (wl.algorithmic_bytes(),
+                                                         wl.algorithmic_flops())
+    assert bench.kernel_work("unknown", wl, "fused") == (0, 0)
 
 
 def test_measured_traffic_is_tied_to_the_kernel_sources():
-    summary = os.path.join(ROOT, "profiles", "k_fused_deit_t_hbm_bytes.md")
-    text = open(summary).read()
-    value = bench.measured_traffic("k_fused", "deit_t")
-    if "source_sha256_16: %s" % _source_digest("k_fused") in text:
-        # the committed count applies: it is the FETCH + WRITE bytes of the summary
-        assert value is not None and value > 0
-        assert "traffic_bytes_per_launch: %d" % value in text
-    else:
-        assert value is None
-    assert bench.measured_traffic("k_fused", "no_such_workload") is None
-    assert bench.measured_traffic("no_such_kernel", "deit_t") is None
+    for fn in os.listdir(os.path.join(ROOT, "profiles")):
+        if not fn.endswith("_hbm_bytes.md"):
+            continue
+        path_name, rest = fn.split("_", 1)
+        workload = rest[:-len("_hbm_bytes.md")]
+        assert path_name in bench.PATH_SOURCES, fn
+        text = open(os.path.join(ROOT, "profiles", fn)).read()
+        value = bench.measured_traffic(path_name, workload, None)
+        if "source_sha256_16: %s" % bench.sources_digest(path_name) in text:
+            # the committed count applies: it is the FETCH + WRITE bytes of the summary
+            assert value is not None and value > 0
+            assert "traffic_bytes_per_call: %d" % value in text
+        else:
+            assert value is None
+    assert bench.measured_traffic("fused", "no_such_workload", None) is None
+    assert bench.measured_traffic("no_such_path", "deit_t", "k_fused") is None

@@ -17,12 +17,14 @@ MHLA_DTYPE_F32, MHLA_DTYPE_BF16 = 0, 1
 (MHLA_PATH_AUTO, MHLA_PATH_GENERIC, MHLA_PATH_FUSED, MHLA_PATH_PAIRS, MHLA_PATH_BLOCKED,
  MHLA_PATH_COLUMNS) = range(6)
 MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL = 1, 2
+MHLA_MAX_LAUNCHES = 8
 
 EXPORTED_SYMBOLS = (
     "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward",
     "mhla_decode_state_bytes", "mhla_decode_step", "mhla_validate", "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
-    "mhla_error_string", "mhla_last_error", "mhla_release",
+    "mhla_workspace_bytes_ex", "mhla_forward_profiled", "mhla_error_string", "mhla_last_error",
+    "mhla_release",
 )
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,10 @@ def load_library():
     lib.mhla_forward_path.restype = ip
     lib.mhla_forward_ex.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, ip, vp]
     lib.mhla_forward_ex.restype = ip
+    lib.mhla_forward_profiled.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, ip,
+                                          ctypes.POINTER(vp), ip, ctypes.POINTER(ip),
+                                          ctypes.POINTER(ctypes.c_char_p), vp]
+    lib.mhla_forward_profiled.restype = ip
     lib.mhla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip,
                                   ip, vp]
     lib.mhla_backward.restype = ip
@@ -91,8 +97,10 @@ def load_library():
     lib.mhla_plan.restype = ip
     lib.mhla_num_blocks.argtypes = [ip, bsp]
     lib.mhla_num_blocks.restype = ip
-    lib.mhla_workspace_bytes.argtypes = [ip, ip, ip, ip, bsp, ip, ip]
+    lib.mhla_workspace_bytes.argtypes = [ip, ip, ip, ip, bsp, ip]
     lib.mhla_workspace_bytes.restype = ctypes.c_size_t
+    lib.mhla_workspace_bytes_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
+    lib.mhla_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.mhla_error_string.argtypes = [ip]
     lib.mhla_error_string.restype = ctypes.c_char_p
     lib.mhla_last_error.argtypes = []
@@ -153,9 +161,14 @@ def mhla_num_blocks(N, block_shape) -> int:
     return int(load_library().mhla_num_blocks(N, ctypes.byref(_shape(block_shape))))
 
 
-def mhla_workspace_bytes(B, H, N, d, block_shape, dtype, path=MHLA_PATH_AUTO) -> int:
+def mhla_workspace_bytes(B, H, N, d, block_shape, dtype) -> int:
     return int(load_library().mhla_workspace_bytes(B, H, N, d, ctypes.byref(_shape(block_shape)),
-                                                   dtype, path))
+                                                   dtype))
+
+
+def mhla_workspace_bytes_ex(B, H, N, d, block_shape, dtype, flags=0, path=MHLA_PATH_AUTO) -> int:
+    return int(load_library().mhla_workspace_bytes_ex(
+        B, H, N, d, ctypes.byref(_shape(block_shape)), dtype, int(flags), int(path)))
 
 
 def mhla_release() -> None:
@@ -171,7 +184,10 @@ def _dtype_code(t) -> int:
     raise TypeError("Q/K/V must be float32 or bfloat16, got %s" % t.dtype)
 
 
-def _check_tensors(Q, K, V, W, out):
+def _check_tensors(Q, K, V, W, out, block_shape):
+    """Types, devices, shapes and dtypes; Wmix must hold exactly H*M*M floats,
+    since the library reads (and the backward writes) that many and cannot see
+    a buffer's size.  Returns the block shape structure."""
     import torch
     for name, t in (("Q", Q), ("K", K), ("V", V), ("Wmix", W), ("out", out)):
         if not isinstance(t, torch.Tensor):
@@ -186,6 +202,15 @@ def _check_tensors(Q, K, V, W, out):
         raise ValueError("Q, K, V, out must share one dtype")
     if W.dtype != torch.float32:
         raise ValueError("Wmix must be float32")
+    bs = _shape(block_shape)
+    B, H, N, d = Q.shape
+    M = mhla_num_blocks(N, bs)
+    if M < 0:
+        raise MhlaError(-M, mhla_last_error())
+    if W.numel() != H * M * M:
+        raise ValueError("Wmix has %d elements; H*M*M = %d*%d*%d = %d are needed"
+                         % (W.numel(), H, M, M, H * M * M))
+    return bs
 
 
 def _stream_ptr(stream) -> int:
@@ -197,9 +222,8 @@ def _stream_ptr(stream) -> int:
 
 def mhla_forward_path(Q, K, V, Wmix, out, block_shape, phi_kind, path, stream=None):
     """Enqueue the forward on `stream` (default: torch's current stream)."""
-    _check_tensors(Q, K, V, Wmix, out)
+    bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
     B, H, N, d = Q.shape
-    bs = _shape(block_shape)
     rc = load_library().mhla_forward_path(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
         ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(path), _stream_ptr(stream))
@@ -211,9 +235,8 @@ def mhla_forward_path(Q, K, V, Wmix, out, block_shape, phi_kind, path, stream=No
 def mhla_forward_ex(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHLA_PATH_AUTO,
                     stream=None):
     """Enqueue the forward with option bits (MHLA_FLAG_NO_NORM, MHLA_FLAG_CAUSAL)."""
-    _check_tensors(Q, K, V, Wmix, out)
+    bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
     B, H, N, d = Q.shape
-    bs = _shape(block_shape)
     rc = load_library().mhla_forward_ex(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
         ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(flags), int(path),
@@ -226,10 +249,9 @@ def mhla_forward_ex(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHL
 def mhla_backward(Q, K, V, Wmix, dY, dQ, dK, dV, dWmix, block_shape, phi_kind, flags=0,
                   stream=None):
     """Enqueue the backward pass: writes dQ, dK, dV (like Q) and dWmix (like Wmix)."""
-    _check_tensors(Q, K, V, Wmix, dY)
-    _check_tensors(dQ, dK, dV, dWmix, dY)
+    bs = _check_tensors(Q, K, V, Wmix, dY, block_shape)
+    _check_tensors(dQ, dK, dV, dWmix, dY, block_shape)
     B, H, N, d = Q.shape
-    bs = _shape(block_shape)
     rc = load_library().mhla_backward(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), dY.data_ptr(), dQ.data_ptr(),
         dK.data_ptr(), dV.data_ptr(), dWmix.data_ptr(), B, H, N, d, ctypes.byref(bs),
@@ -260,6 +282,9 @@ def mhla_decode_step(q, k, v, Wmix, y, state, M, nb, t, phi_kind, flags=0, strea
     if not (isinstance(state, torch.Tensor) and state.is_cuda and state.is_contiguous()):
         raise ValueError("state must be a contiguous GPU tensor")
     B, H, d = q.shape
+    if Wmix.numel() != H * int(M) * int(M):
+        raise ValueError("Wmix has %d elements; H*M*M = %d are needed"
+                         % (Wmix.numel(), H * int(M) * int(M)))
     if state.numel() * state.element_size() < mhla_decode_state_bytes(B, H, d, M):
         raise ValueError("state is smaller than mhla_decode_state_bytes")
     rc = load_library().mhla_decode_step(
@@ -273,12 +298,55 @@ def mhla_decode_step(q, k, v, Wmix, y, state, M, nb, t, phi_kind, flags=0, strea
 
 def mhla_forward(Q, K, V, Wmix, out, block_shape, phi_kind, stream=None):
     """Enqueue the forward with the library's path choice."""
-    _check_tensors(Q, K, V, Wmix, out)
+    bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
     B, H, N, d = Q.shape
-    bs = _shape(block_shape)
     rc = load_library().mhla_forward(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
         ctypes.byref(bs), int(phi_kind), _dtype_code(Q), _stream_ptr(stream))
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())
     return out
+
+
+class PreparedForward:
+    """A forward call with its arguments marshalled once, for timing loops.
+    call() enqueues mhla_forward_ex; profiled(events) enqueues
+    mhla_forward_profiled with `events` (at least MHLA_MAX_LAUNCHES + 1
+    hipEvent_t handles as ints) and returns the names of the launched
+    kernels."""
+
+    def __init__(self, Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHLA_PATH_AUTO,
+                 stream=None):
+        bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
+        B, H, N, d = Q.shape
+        self._bs = bs
+        self._args = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(),
+                      B, H, N, d, ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(flags),
+                      int(path))
+        self._stream = _stream_ptr(stream)
+        self._names = (ctypes.c_char_p * MHLA_MAX_LAUNCHES)()
+        self._n = ctypes.c_int(0)
+        lib = load_library()
+        self._fwd, self._prof = lib.mhla_forward_ex, lib.mhla_forward_profiled
+        self._keep = (Q, K, V, Wmix, out)
+
+    def call(self):
+        rc = self._fwd(*self._args, self._stream)
+        if rc != MHLA_OK:
+            raise MhlaError(rc, mhla_last_error())
+
+    def profiled(self, events):
+        ev = (ctypes.c_void_p * len(events))(*events)
+        rc = self._prof(*self._args, ev, len(events), ctypes.byref(self._n), self._names,
+                        self._stream)
+        if rc != MHLA_OK:
+            raise MhlaError(rc, mhla_last_error())
+        return [self._names[i].decode() for i in range(min(self._n.value, MHLA_MAX_LAUNCHES))]
+
+
+def mhla_forward_profiled(Q, K, V, Wmix, out, block_shape, phi_kind, flags, path, events,
+                          stream=None):
+    """mhla_forward_ex recording events[0] before and events[k] after launch k;
+    returns the launched kernels' names."""
+    return PreparedForward(Q, K, V, Wmix, out, block_shape, phi_kind, flags, path,
+                           stream).profiled(events)

@@ -858,6 +858,7 @@ void launch_mix_small(long slices, int H, int M, const bf16_t* S, const float* W
     k_mix_small<EP, MODE, 8, OutT><<<grid, 256, 0, st>>>(S, W, St, M, H);
   else
     k_mix_small<EP, MODE, kMixSmallM, OutT><<<grid, 256, 0, st>>>(S, W, St, M, H);
+  launch_mark(st, "k_mix_small");
 }
 
 // wc: mix_coef_bytes(H, M) bytes of scratch for the large-M kernel (which is
@@ -877,14 +878,17 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
       k_mix_coef_t<<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M);
     else
       k_mix_coef<MODE><<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M, tot);
+    launch_mark(st, "k_mix_coef");
     const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 255) / 256));
     k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+    launch_mark(st, "k_mix_big");
     return;
   }
   if (M <= 32) {
     constexpr int NG = (D::EP / 128 + kStreamTiles - 1) / kStreamTiles;
     const unsigned n = (unsigned)(xslices * NG);
     k_mix_stream<D::EP, MODE, 32><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
+    launch_mark(st, "k_mix_stream");
     return;
   }
   const int ib = mix_ib(M);
@@ -893,6 +897,7 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
     k_mix_mfma<D::EP, 64, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
   else
     k_mix_mfma<D::EP, 128, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
+  launch_mark(st, "k_mix_mfma");
 }
 
 template <int DP>
@@ -951,6 +956,7 @@ bf16_t* launch_summary_mix(long slices, int H, int N, int d, const Geo& g, const
     k_summary_mfma<DP, PHI, true><<<grid, 64 * D::NT, 0, st>>>(K, V, S, g, N, d, nullptr);
   else
     k_summary_mfma<DP, PHI><<<grid, 64 * D::NT, 0, st>>>(K, V, S, g, N, d, nullptr);
+  launch_mark(st, "k_summary_mfma");
   launch_mix<DP>(slices, H, g.M, S, W, St, causal ? kMixCausal : kMixPlain, wc, st);
   return St;
 }
@@ -973,6 +979,7 @@ int launch_blocked_t(long slices, int H, int N, int d, const Geo& g, const bf16_
     k_readout_mfma<DP, PHI, true><<<grid, kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
   else
     k_readout_mfma<DP, PHI><<<grid, kBlkThreads, 0, st>>>(Q, St, Y, g, N, d);
+  launch_mark(st, "k_readout_mfma");
   return 0;
 }
 

@@ -170,6 +170,7 @@ int launch_readout_causal(long slices, int H, int N, int d, const Geo& g, const 
     return -1;
   k_readout_causal<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), kBlkThreads, lds, st>>>(
       Q, K, V, W, St, Y, g, H, N, d);
+  launch_mark(st, "k_readout_causal");
   return 0;
 }
 

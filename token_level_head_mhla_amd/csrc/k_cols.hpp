@@ -413,6 +413,7 @@ int launch_cols_t(long slices, int H, int N, int d, const Geo& g, const bf16_t* 
   const long grid = ((slices + 7) / 8) * 8 * NC;
   k_cols<DP, MT, PHI><<<dim3((unsigned)grid), dim3(64 * kColsWaves), lds, st>>>(
       Q, K, V, W, Y, g, H, N, d, slices, NC);
+  launch_mark(st, "k_cols");
   return 0;
 }
 

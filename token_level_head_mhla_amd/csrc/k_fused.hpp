@@ -359,6 +359,7 @@ int launch_fused_t(long slices, int H, int N, int d, const Geo& g, const bf16_t*
   for (int b = 0; b < kFusedMaxM; ++b) fb.b[b] = b < g.M ? g.blockbase(b) : 0;
   k_fused<DP, NBP, MM, PHI><<<dim3((unsigned)slices), dim3(64 * fused_waves(MM)), lds, st>>>(
       Q, K, V, W, Y, g, fb, H, N, d);
+  launch_mark(st, "k_fused");
   return 0;
 }
 

@@ -261,6 +261,7 @@ int launch_pairs_t(long slices, int H, int N, int d, const Geo& g, const bf16_t*
     return -1;
   k_pairs<DK, DO, QB, PHI><<<dim3((unsigned)slices), dim3(kPairsThreads), lds, st>>>(
       Q, K, V, W, Y, g, H, N, d);
+  launch_mark(st, "k_pairs");
   return 0;
 }
 

@@ -88,6 +88,31 @@ template <> struct Elt<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Per-launch event recording (mhla_forward_profiled).  While a recorder is
+// installed for the calling thread, every forward launch site calls
+// launch_mark(stream, name) right after its kernel launch: the next event is
+// recorded on that stream and the kernel's name kept.  With no recorder the
+// call does nothing.
+struct LaunchRecorder {
+  void* const* events;  // hipEvent_t handles; events[0] precedes the first launch
+  int cap;              // launches that have an event (max_events - 1)
+  int n = 0;            // launches seen
+  const char** names;   // may be null
+  bool failed = false;  // a hipEventRecord failed
+};
+inline thread_local LaunchRecorder* g_launch_rec = nullptr;
+
+inline void launch_mark(hipStream_t st, const char* name) {
+  LaunchRecorder* r = g_launch_rec;
+  if (r == nullptr) return;
+  if (r->n < r->cap) {
+    if (hipEventRecord(static_cast<hipEvent_t>(r->events[r->n + 1]), st) != hipSuccess)
+      r->failed = true;
+    if (r->names != nullptr) r->names[r->n] = name;
+  }
+  ++r->n;
+}
+
 // Raises a kernel's dynamic LDS limit to `bytes` once per device (the
 // attribute belongs to the function on each device).  `done` is the caller's
 // per-kernel flag array; threads that race here only repeat the call.
