@@ -68,6 +68,7 @@ CAUSAL_CASES = [
     ((1, 1, 1200), (1, 1, 24), 96, PHI_RELU),   # M = 50, d = 96
     ((1, 1, 8192), (1, 1, 32), 32, PHI_ELU1),   # M = 256: the large-M prefix mixing
     ((1, 1, 4608), (1, 1, 16), 16, PHI_RELU),   # M = 288: a partial query-block tile
+    ((1, 1, 20480), (1, 1, 64), 64, PHI_ELU1),  # M = 320, d = 64 (the video entry width)
 ]
 
 

@@ -158,6 +158,7 @@ BLOCKED_CASES = [
     ((1, 48, 48), (1, 2, 4), 16, PHI_RELU),    # M = 288: a partial query-block tile
     ((4, 32, 32), (1, 4, 4), 64, PHI_ELU1),    # M = 256, d = 64 (the video entry width)
     ((1, 32, 64), (1, 2, 4), 96, PHI_RELU),    # M = 256, d = 96
+    ((1, 1, 6656), (1, 1, 16), 64, PHI_ELU1),  # M = 416: a partial 128-block z chunk
 ]
 
 

@@ -7,8 +7,9 @@
 //                    transpose reads, fp32 accumulation, bf16 result)
 //   k_mix_mfma     : S~_i = sum_b W[i,b] S_b, z~_i = sum_b W[i,b] z_b, one
 //                    GEMM per (batch, head) slice over all d*d + d entries
-//                    (k_mix_small for M <= 16; k_mix_coef + k_mix_big, a
-//                    larger-tile GEMM on bf16 coefficients, for M >= 256)
+//                    (k_mix_small for M <= 16; for M >= 256, k_mix_prep
+//                    (bf16 coefficients and z~) + k_mix_big, a larger-tile
+//                    GEMM over the d*d entries of S)
 //   k_readout_mfma : Y_q = phi(Q_q) S~_i / (phi(Q_q) . z~_i), one wave per
 //                    query block, operands straight from global memory
 //
@@ -341,9 +342,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 
 // ---------------------------------------------------------------------------
 // Mixing for many blocks (M >= kMixBigM, M % 32 == 0; plain, prefix and
-// transposed modes).  k_mix_coef first writes the coefficient matrix of the
-// mode in bf16 (Wc[h][i][b] = coef(i, b)), so that the GEMM streams two bf16
-// operands with unconditional 16-byte loads.  k_mix_big: one workgroup (4
+// transposed modes).  k_mix_prep (plain, prefix) or k_mix_coef_t (transposed)
+// first writes the coefficient matrix of the mode in bf16 (Wc[h][i][b] =
+// coef(i, b)), so that the GEMM streams two bf16 operands with unconditional
+// 16-byte loads.  k_mix_big: one workgroup (4
 // waves) computes 256 query blocks x 128 entries of one slice; wave (we, wi)
 // owns 64 entries x 128 query blocks (32 accumulator tiles), which keeps it
 // within 256 registers, so two workgroups share a CU and one's barrier waits
@@ -362,30 +364,114 @@ __host__ __device__ inline size_t coef_tiled(int M, int h, int i, int b) {
   return (((size_t)h * nit + i / 256) * nk + b / 32) * 8192 + (size_t)(i % 256) * 32 + b % 32;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void k_mix_coef(const float* __restrict__ W,
-                                                  bf16_t* __restrict__ Wc, int M, long total) {
-  // grid = total / 1024 over the padded [H][MI][M] entries (MI = M rounded up
-  // to 256), four consecutive entries per thread (M % 32 == 0)
-  static_assert(MODE != kMixTransposed, "the transposed mode uses k_mix_coef_t");
-  const long e = 4 * ((long)blockIdx.x * 256 + threadIdx.x);
-  if (e >= total) return;
-  const long mi = (long)(M + 255) / 256 * 256;
-  const int h = (int)(e / (mi * M));
-  const long r = e - h * mi * M;
-  const int i = (int)(r / M), b = (int)(r - (r / M) * M);
-  f32x4_t v = zero4();
-  if (i < M) {
-    v = __builtin_nontemporal_load(
-        reinterpret_cast<const f32x4_t*>(W + ((size_t)h * M + i) * M + b));  // read once
-    if constexpr (MODE == kMixCausal) {
+// Coefficients and mixed normalisers of the large-M mixing, plain and
+// prefix modes.  A workgroup owns the 16 query blocks i0 .. i0+15 of head h
+// (rows past M are the zero padding of the coefficient tiles):
+//   - it converts their rows of W to the bf16 coefficients of the mode
+//     (coef(i, b) = W[h][i][b], zero for b >= i in the prefix mode) and
+//     writes them in the tiled layout of coef_tiled;
+//   - for every slice of head h it forms z~_i = sum_b coef(i, b) z_b on MFMA
+//     (the same bf16 coefficients as the GEMM, fp32 accumulation) and stores
+//     it as the z part of row i of S~ (entries DP*DP .. DP*DP + DP - 1).
+// k_mix_big then mixes only the DP*DP entries of S, which are a whole number
+// of its 128-entry tiles.  The key blocks go in steps of 32; wave w takes
+// steps w, w + 4, ...; the z_b rows of 128 key blocks (one step per wave) are
+// staged in LDS and read as transposed B operands; the four waves' partial
+// sums meet in LDS.  grid = H * MI / 16 (MI = M rounded up to 256), block =
+// 256, M % 32 == 0.
+template <int DP, int MODE>
+__global__ __launch_bounds__(256) void k_mix_prep(const float* __restrict__ W,
+                                                  const bf16_t* __restrict__ S,
+                                                  bf16_t* __restrict__ St,
+                                                  bf16_t* __restrict__ Wc, int M, int H,
+                                                  long nslices) {
+  static_assert(MODE == kMixPlain || MODE == kMixCausal, "plain and prefix modes only");
+  constexpr int EP = BlockedDims<DP>::EP;
+  constexpr int NT = DP / 16;        // 16-feature output tiles
+  constexpr int ZR = DP + 8;         // LDS row stride of the staged z rows
+  constexpr int CH = 128;            // key blocks staged per chunk
+  constexpr int ZCH = CH * DP / 8 / 256;  // 16-byte z pieces per thread per chunk
+  __shared__ __attribute__((aligned(16))) bf16_t sz[CH * ZR];
+  __shared__ __attribute__((aligned(16))) float sacc[4][16][DP + 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int nti = (M + 255) / 256 * 16;  // 16-row tiles per head
+  const int h = blockIdx.x / nti;
+  const int i0 = (blockIdx.x - h * nti) * 16;
+  const int i = i0 + s;                  // this lane's row of the A operand
+  const int nk = M / 32;
+  const float* Wr = W + ((size_t)h * M + (i < M ? i : 0)) * M;
+  for (long slice = h; slice < nslices; slice += H) {
+    const bool first = slice == h;       // the coefficient tiles are written once
+    f32x4_t acc[NT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (b + q >= i) v[q] = 0.0f;
+    for (int t = 0; t < NT; ++t) acc[t] = zero4();
+    const bf16_t* Zs = S + (size_t)slice * M * EP + DP * DP;
+    for (int c0 = 0; c0 < M; c0 += CH) {
+      // stage z rows c0 .. c0+CH-1 (zero past M)
+      u32x4_t zr[ZCH];
+#pragma unroll
+      for (int u = 0; u < ZCH; ++u) {
+        const int pc = tid + 256 * u;
+        const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
+        zr[u] = c0 + r < M ? *reinterpret_cast<const u32x4_t*>(Zs + (size_t)(c0 + r) * EP + 8 * f)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+      for (int u = 0; u < ZCH; ++u) {
+        const int pc = tid + 256 * u;
+        const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
+        *reinterpret_cast<u32x4_t*>(sz + r * ZR + 8 * f) = zr[u];
+      }
+      __syncthreads();
+      const int k = c0 / 32 + wave;      // this wave's step of the chunk
+      if (k < nk) {
+        const int b = 32 * k + 8 * grp;  // A: row i, key blocks b .. b+7
+        f32x4_t w0 = zero4(), w1 = zero4();
+        if (i < M) {
+          w0 = *reinterpret_cast<const f32x4_t*>(Wr + b);
+          w1 = *reinterpret_cast<const f32x4_t*>(Wr + b + 4);
+          if constexpr (MODE == kMixCausal) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (b + q >= i) w0[q] = 0.0f;
+              if (b + 4 + q >= i) w1[q] = 0.0f;
+            }
+          }
+        }
+        const u32x4_t a32 = {pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), pack2(w1[0], w1[1]),
+                             pack2(w1[2], w1[3])};
+        if (first) *reinterpret_cast<u32x4_t*>(Wc + coef_tiled(M, h, i, b)) = a32;
+        const u16x8_t a = __builtin_bit_cast(u16x8_t, a32);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = mfma_bf16(a, lds_tr8(sz, ZR, 32 * wave, 16 * t, lane), acc[t]);
+      }
     }
+    // acc[t] lane (s, grp) element r = z~[i0 + 4grp + r][16t + s] (partial)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[wave][4 * grp + r][16 * t + s] = acc[t][r];
+    __syncthreads();
+    for (int e = tid; e < 16 * DP / 2; e += 256) {
+      const int row = e / (DP / 2), c = 2 * (e - row * (DP / 2));
+      if (i0 + row < M) {
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v0 += sacc[w][row][c];
+          v1 += sacc[w][row][c + 1];
+        }
+        *reinterpret_cast<uint32_t*>(St + ((size_t)slice * M + i0 + row) * EP + DP * DP + c) =
+            pack2(v0, v1);
+      }
+    }
+    __syncthreads();  // sacc is rewritten by the next slice
   }
-  *reinterpret_cast<uint2*>(Wc + coef_tiled(M, h, i, b)) =
-      make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
 }
 
 // Mixing for 16 < M <= 32 (MP = 32, M padded): the contraction is a single
@@ -540,7 +626,7 @@ __device__ __forceinline__ void mix_big_groups() {
   }
 }
 
-template <int EP, int MODE>
+template <int EP, int MODE, int NE = EP / 128>
 __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S,
                                                     const bf16_t* __restrict__ Wc,
                                                     bf16_t* __restrict__ St, int M, int H,
@@ -550,10 +636,11 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
   constexpr int SRS = TE + 8;               // S tile row stride (elements), rows = key blocks
   constexpr int WRS = KB + 16;              // W tile row stride, rows = query blocks (measured
                                             // fastest for the 16-byte fragment reads)
-  constexpr int nE = EP / TE;
+  constexpr int nE = NE;                  // entry tiles computed (the first NE of the row)
   constexpr int SCH = KB * TE / 8 / 256;  // 16-byte S chunks per thread per step (2)
   constexpr int WCH = TI * KB / 8 / 256;  // 16-byte W chunks per thread per step (4)
-  static_assert(EP % TE == 0 && SCH * 8 * 256 == KB * TE && WCH * 8 * 256 == TI * KB, "tiles");
+  static_assert(EP % TE == 0 && NE * TE <= EP && SCH * 8 * 256 == KB * TE &&
+                WCH * 8 * 256 == TI * KB, "tiles");
   __shared__ __attribute__((aligned(16))) bf16_t sS[2][KB * SRS];
   __shared__ __attribute__((aligned(16))) bf16_t sW[2][TI * WRS];
   const int tid = threadIdx.x;
@@ -873,14 +960,23 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
   }
   const long xslices = (slices + 7) / 8 * 8;
   if (mix_coef_bytes(H, M) != 0) {
-    const long tot = (long)H * ((M + 255) / 256 * 256) * M;  // padded entries
-    if constexpr (MODE == kMixTransposed)
+    const int nit = (M + 255) / 256;
+    if constexpr (MODE == kMixTransposed) {
+      // the backward's transposed mixing: dz_b rides along as the last entry tile
+      const long tot = (long)H * nit * 256 * M;
       k_mix_coef_t<<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M);
-    else
-      k_mix_coef<MODE><<<dim3((unsigned)(tot / 1024)), 256, 0, st>>>(W, wc, M, tot);
-    launch_mark(st, "k_mix_coef");
-    const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 255) / 256));
-    k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+      launch_mark(st, "k_mix_coef_t");
+      const unsigned nb = (unsigned)(xslices * (D::EP / 128) * nit);
+      k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+    } else {
+      // coefficients and z~ first; the GEMM then covers the DP*DP entries only
+      k_mix_prep<DP, MODE><<<dim3((unsigned)(H * nit * 16)), 256, 0, st>>>(W, S, St, wc, M, H,
+                                                                          slices);
+      launch_mark(st, "k_mix_prep");
+      constexpr int NE = DP * DP / 128;
+      const unsigned nb = (unsigned)(xslices * NE * nit);
+      k_mix_big<D::EP, MODE, NE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
+    }
     launch_mark(st, "k_mix_big");
     return;
   }
