@@ -126,6 +126,26 @@ int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wm
                     const mhla_block_shape* block_shape, int phi_kind, int dtype,
                     int flags, int path, mhla_stream_t stream);
 
+/* mhla_forward_ex for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the call's scratch (the blocked path's S / S~ tables and mixing
+ * coefficients, the generic path's fp32 tables) lives in a fixed array of
+ * MHLA_NOALLOC_SCRATCH_BYTES that the library's code object holds on every
+ * device it runs on, until the process ends; nothing is allocated or freed.
+ * The caller still passes Q, K, V, Wmix and out.  A call whose scratch need
+ * (mhla_workspace_bytes_ex) exceeds the array returns MHLA_ERR_UNSUPPORTED
+ * before any launch; other errors are those of mhla_forward_ex.  Every call
+ * on one device shares that device's array (it keeps the last call's
+ * contents; no call depends on them): calls that overlap in time on one
+ * device -- on different streams or host threads -- race and give undefined
+ * results, so serialise them. */
+#define MHLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int mhla_forward_noalloc(const void* Q, const void* K, const void* V,
+                         const float* Wmix, void* out, int B, int H, int N,
+                         int d, const mhla_block_shape* block_shape,
+                         int phi_kind, int dtype, int flags, int path,
+                         mhla_stream_t stream);
+
 /* Upper bound on the kernel launches of one forward call (any path and
  * options). */
 #define MHLA_MAX_LAUNCHES 8

@@ -23,9 +23,10 @@ EXPORTED_SYMBOLS = (
     "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward",
     "mhla_decode_state_bytes", "mhla_decode_step", "mhla_validate", "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
-    "mhla_workspace_bytes_ex", "mhla_forward_profiled", "mhla_error_string", "mhla_last_error",
-    "mhla_release",
+    "mhla_workspace_bytes_ex", "mhla_forward_profiled", "mhla_forward_noalloc",
+    "mhla_error_string", "mhla_last_error", "mhla_release",
 )
+MHLA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmhla.so")
@@ -79,6 +80,9 @@ def load_library():
                                           ctypes.POINTER(vp), ip, ctypes.POINTER(ip),
                                           ctypes.POINTER(ctypes.c_char_p), vp]
     lib.mhla_forward_profiled.restype = ip
+    lib.mhla_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip, ip, ip,
+                                         vp]
+    lib.mhla_forward_noalloc.restype = ip
     lib.mhla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, bsp, ip, ip,
                                   ip, vp]
     lib.mhla_backward.restype = ip
@@ -238,6 +242,21 @@ def mhla_forward_ex(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0, path=MHL
     bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
     B, H, N, d = Q.shape
     rc = load_library().mhla_forward_ex(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
+        ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(flags), int(path),
+        _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return out
+
+
+def mhla_forward_noalloc(Q, K, V, Wmix, out, block_shape, phi_kind, flags=0,
+                         path=MHLA_PATH_AUTO, stream=None):
+    """mhla_forward_ex on the library's fixed scratch (no device allocation;
+    calls that overlap on one device race)."""
+    bs = _check_tensors(Q, K, V, Wmix, out, block_shape)
+    B, H, N, d = Q.shape
+    rc = load_library().mhla_forward_noalloc(
         Q.data_ptr(), K.data_ptr(), V.data_ptr(), Wmix.data_ptr(), out.data_ptr(), B, H, N, d,
         ctypes.byref(bs), int(phi_kind), _dtype_code(Q), int(flags), int(path),
         _stream_ptr(stream))

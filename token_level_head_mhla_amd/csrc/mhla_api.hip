@@ -147,6 +147,39 @@ int launch_generic(const Problem& p, const T* Q, const T* K, const T* V, const f
   return MHLA_OK;
 }
 
+// Scratch of mhla_forward_noalloc, for callers that cannot allocate device
+// memory: a fixed array in the library's code object, so that each device the
+// library runs on holds its own copy from the first launch until the process
+// ends.  256 MiB holds the workspace of every forward workload the library is
+// measured on (the largest, the video-latent shape, needs 211 MiB); larger
+// calls are rejected.  Host code never uses the array's name as an address:
+// it takes the device address from hipGetSymbolAddress (scratch_address).
+constexpr size_t kNoAllocScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+int scratch_address(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MHLA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MHLA_ERR_UNSUPPORTED, "device %d is beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MHLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MHLA_OK;
+}
+
 // Where a forward call's workspace comes from: the library's cache (one
 // growing buffer per device and stream), or a caller-supplied fixed region
 // (`fixed`, `fixed_bytes`) that is never grown.
@@ -311,6 +344,21 @@ int mhla_forward_ex(const void* Q, const void* K, const void* V, const float* Wm
   if (path < MHLA_PATH_AUTO || path > MHLA_PATH_COLUMNS)
     return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
   return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, flags, path, stream);
+}
+
+int mhla_forward_noalloc(const void* Q, const void* K, const void* V, const float* Wmix,
+                         void* out, int B, int H, int N, int d,
+                         const mhla_block_shape* block_shape, int phi_kind, int dtype, int flags,
+                         int path, mhla_stream_t stream) {
+  g_last_error.clear();
+  if (path < MHLA_PATH_AUTO || path > MHLA_PATH_COLUMNS)
+    return fail(MHLA_ERR_INVALID_ARG, "unknown path %d", path);
+  WsSource src;
+  const int rc = scratch_address(&src.fixed);
+  if (rc != MHLA_OK) return rc;
+  src.fixed_bytes = kNoAllocScratchBytes;
+  return run(Q, K, V, Wmix, out, B, H, N, d, block_shape, phi_kind, dtype, flags, path, stream,
+             nullptr, &src);
 }
 
 int mhla_forward_profiled(const void* Q, const void* K, const void* V, const float* Wmix,
