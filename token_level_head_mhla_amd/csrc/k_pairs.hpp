@@ -34,8 +34,10 @@ constexpr int kPairsMaxQB = 4;  // query blocks per wave (M <= 32)
 // Feature operands of phi(K) phi(Q)^T in steps of 32 (lane group g holds
 // features 32 ks + 8g .. +7).  When DK is not a multiple of 32 the last step
 // (ks == ks_full) covers 16 features and groups 2 and 3 hold zeros, so that
-// every product is a 16x16x32 MFMA.  (A 16x16x16 MFMA for that tail, fed
-// from a 16x16x32 accumulation, gave wrong results in the backward kernels.)
+// every product is a 16x16x32 MFMA.  (A 16x16x16 MFMA for the tail would
+// accumulate onto the result of a 16x16x32 one; on gfx950 such a dependent
+// pair of different shapes reads a wrong accumulator when it issues back to
+// back, and the compiler inserts no wait states between them.)
 //   feat_operand: from global row `tok` (phi applied; features past d and
 //                 tok < 0 give 0)
 //   feat_row:     from an LDS row of phi values (pad columns already 0)
