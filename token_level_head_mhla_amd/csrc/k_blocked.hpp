@@ -791,6 +791,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
     az[ks] = s == 0 ? *reinterpret_cast<const u16x8_t*>(row + DP * DP + 32 * ks + 8 * grp)
                     : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   const int bb = g.blockbase(i);
+  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
+  // per-wave LDS staging area
+  constexpr bool STAGED = DP == 64 || DP == 32;
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[STAGED ? kBlkWaves * 16 * (DP + 8) : 1];
+  bf16_t* stage = stage_all + wave * 16 * (DP + 8);
+  const bool whole_rows = STAGED && d == DP;
   // Query tiles of 16, loaded QP tiles at a time before any of them is used,
   // so that their transfers overlap.
   constexpr int QP = 4;
@@ -829,8 +835,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_mfma(
       for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[u][ks], oz);
       const float den = __shfl(oz[0], s);
       const float rd = out_scale(g, den);
-      store_row_tiles<NT, STREAM>(tq[u] >= 0 ? Y + off + (size_t)tq[u] * d : nullptr, d, o, rd,
-                                  grp);
+      bf16_t* yrow = tq[u] >= 0 ? Y + off + (size_t)tq[u] * d : nullptr;
+      if constexpr (STAGED) {
+        if (whole_rows) {
+          store_rows_staged<NT, STREAM>(yrow, stage, o, rd, threadIdx.x & 63);
+          continue;
+        }
+      }
+      store_row_tiles<NT, STREAM>(yrow, d, o, rd, grp);
     }
   }
 }

@@ -168,4 +168,45 @@ __device__ __forceinline__ void store_row_tiles(bf16_t* row, int limit, const f3
   }
 }
 
+// Stores the accumulator tiles t[0..NT) of 16 output rows -- tile j, lane
+// group g, element r holds row s, column 16j + 4g + r -- scaled by `scale`,
+// as bf16 rows of 16 NT elements (NT = 2 or 4: 64 or 128 bytes), each row
+// written whole by one store instruction.  The wave first writes the tiles
+// to its LDS staging area `stage` (16 x (16 NT + 8) bf16, private to the
+// wave), then reads them back row-contiguous, so that each instruction
+// stores 64 lanes x 16 bytes = 64 / (2 NT) complete rows: no cache line is
+// written in parts (store_row_tiles writes every 128-byte row as two 64-byte
+// halves, which nontemporal stores leave unmerged).  row: this lane's
+// pointer to row s (nullptr: the row is not stored); every lane of the wave
+// calls this.  STREAM: nontemporal stores.
+template <int NT, bool STREAM>
+__device__ __forceinline__ void store_rows_staged(bf16_t* row, bf16_t* stage,
+                                                  const f32x4_t (&t)[NT], float scale, int lane) {
+  static_assert(NT == 2 || NT == 4, "rows of 64 or 128 bytes");
+  constexpr int RS = 16 * NT + 8;  // staging row stride (elements)
+  constexpr int LPR = 2 * NT;      // lanes per row, 16 bytes each
+  constexpr int RPI = 64 / LPR;    // rows per store instruction
+  const int s = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    *reinterpret_cast<uint2*>(stage + s * RS + 16 * j + 4 * grp) =
+        make_uint2(pack2(t[j][0] * scale, t[j][1] * scale), pack2(t[j][2] * scale, t[j][3] * scale));
+  __builtin_amdgcn_wave_barrier();  // LDS operations of one wave run in order
+  const unsigned long long rp = reinterpret_cast<unsigned long long>(row);
+#pragma unroll
+  for (int h = 0; h < 16 / RPI; ++h) {
+    const int r = h * RPI + lane / LPR, c = 8 * (lane % LPR);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * RS + c);
+    const unsigned lo = __shfl((unsigned)rp, r), hi = __shfl((unsigned)(rp >> 32), r);
+    bf16_t* dst = reinterpret_cast<bf16_t*>(((unsigned long long)hi << 32) | lo);
+    if (dst != nullptr) {
+      if constexpr (STREAM)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + c));
+      else
+        *reinterpret_cast<u32x4_t*>(dst + c) = v;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // the next call may rewrite the staging area
+}
+
 }  // namespace mhla
