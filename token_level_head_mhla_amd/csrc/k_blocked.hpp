@@ -349,10 +349,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 // waves) computes 256 query blocks x 128 entries of one slice; wave (we, wi)
 // owns 64 entries x 128 query blocks (32 accumulator tiles), which keeps it
 // within 256 registers, so two workgroups share a CU and one's barrier waits
-// overlap the other's MFMAs.  Key blocks advance 32 per step: the tiles of
-// step k + 2 are fetched into one of two register sets while step k runs, and
-// the tiles of step k + 1 are written to the other LDS buffer between the
-// MFMAs of step k (scheduling groups), with one barrier per step.  In the
+// overlap the other's MFMAs.  Key blocks advance 32 per step through a ring
+// of three LDS stages (72 KB) filled by global-to-LDS loads
+// (global_load_lds_dwordx4, no register round trip): the loads of step k + 2
+// are issued while step k is multiplied, one barrier per step.  In the
 // prefix mode a tile stops at the last key block its rows can use.
 constexpr int kMixBigM = 256;
 
@@ -614,16 +614,98 @@ __global__ __launch_bounds__(256) void k_mix_coef_t(const float* __restrict__ W,
       make_uint2(pack2(tile[c4][r], tile[c4 + 1][r]), pack2(tile[c4 + 2][r], tile[c4 + 3][r]));
 }
 
-template <int A, int AT, int NWR>
-__device__ __forceinline__ void mix_big_groups() {
-  // NWR rounds of (4 MFMAs, 1 LDS write), then the remaining MFMAs
-  if constexpr (A < NWR) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-    mix_big_groups<A + 1, AT, NWR>();
-  } else {
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 * AT - 4 * NWR, 0);
+// The pipelined main loop of k_mix_big.  The three stages are separate
+// restrict-qualified arrays so that the compiler's wait insertion can tell
+// a stage being read from the stages whose loads are still in flight.
+template <int EP>
+__device__ __forceinline__ void mix_big_loop(bf16_t* __restrict__ ring0, bf16_t* __restrict__ ring1,
+                                             bf16_t* __restrict__ ring2,
+                                             const bf16_t* __restrict__ Ss,
+                                             const bf16_t* __restrict__ Wt, int nk, int e0,
+                                             int wave, int lane, f32x4_t (&acc)[4][8]) {
+  constexpr int TI = 256, TE = 128, KB = 32, EW = TE / 2, AT = EW / 16;
+  constexpr int SST = KB * TE;
+  const int s = lane & 15, grp = lane >> 4;
+  const int we = wave & 1, wi = wave >> 1;
+  static_assert(TI * KB == 8192, "coefficient tile");
+  // Step k's tiles into stage `st`: wave w moves S rows 8w .. 8w+7 (two
+  // 1 KB loads of four rows) and W rows 64w .. 64w+63 (four loads of 16
+  // rows); lane L's 16 bytes land at slot L of the load's 1 KB.  Six loads
+  // per thread per step.
+  auto issue = [&](bf16_t* st, int k) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * wave + 4 * u + (lane >> 4);
+      const int f = ((lane & 15) - r) & 15;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(Ss + (size_t)(k * KB + r) * EP + e0 + 8 * f),
+          (__attribute__((address_space(3))) void*)(st + (8 * wave + 4 * u) * TE), 16, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 64 * wave + 16 * u + (lane >> 2);
+      const int f = (lane & 3) ^ ((i >> 1) & 3);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(Wt + (size_t)k * 8192 + i * KB + 8 * f),
+          (__attribute__((address_space(3))) void*)(st + SST + (64 * wave + 16 * u) * KB), 16, 0,
+          0);
+    }
+  };
+  // A = S^T (rows e, contraction b via transpose reads), B = W^T (column i,
+  // the same b: W[i][8grp .. 8grp+7] is one chunk)
+  auto compute = [&](const bf16_t* st) {
+    const bf16_t* sS = st;
+    const bf16_t* sW = st + SST;
+    u16x8_t bw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      bw[c] = *reinterpret_cast<const u16x8_t*>(sW + (128 * wi + 16 * c + s) * KB +
+                                                8 * (grp ^ ((s >> 1) & 3)));
+    // lane (s, grp) of a transpose read supplies row 8grp + s/4 (+4 for the
+    // second read), entries c0 + 4 (s % 4) .. + 3: chunk c0 / 8 + (s % 4) / 2
+    const int r_lo = 8 * grp + (s >> 2), half = 4 * (s & 1);
+#pragma unroll
+    for (int a = 0; a < AT; ++a) {
+      const int f = (EW * we + 16 * a) / 8 + ((s & 3) >> 1);
+      const i16x4_t lo = lds_tr4(sS + r_lo * TE + 8 * ((f + r_lo) & 15) + half);
+      const i16x4_t hi = lds_tr4(sS + (r_lo + 4) * TE + 8 * ((f + r_lo + 4) & 15) + half);
+      const u16x8_t af =
+          __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[a][c] = mfma_bf16(af, bw[c], acc[a][c]);
+    }
+  };
+  // Step k: wait for this thread's loads of step k (the six of step k + 1
+  // may still be in flight), barrier (every wave's step-k tiles are in LDS
+  // and every wave is done reading step k - 1's stage), refill that stage
+  // with step k + 2 (past the end: the last step again, into a stage no one
+  // reads), multiply.  Every step issues six loads, so the wait is always
+  // vmcnt(6).  The barrier is a plain s_barrier after explicit counter
+  // waits: a workgroup fence would also wait for step k + 1's loads.
+  auto step = [&](bf16_t* cur, bf16_t* next2, int k) {
+    __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(next2, k + 2 < nk ? k + 2 : nk - 1);
+    compute(cur);
+  };
+  // stage of step k: k % 3; the main loop is unrolled by three so that
+  // every stage is a fixed array and the body has no branches
+  issue(ring0, 0);
+  issue(ring1, nk > 1 ? 1 : 0);
+  int k = 0;
+  for (; k + 3 <= nk; k += 3) {
+    step(ring0, ring2, k);
+    step(ring1, ring0, k + 1);
+    step(ring2, ring1, k + 2);
   }
+  if (k < nk) step(ring0, ring2, k);
+  if (k + 1 < nk) step(ring1, ring0, k + 1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no load is left in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int EP, int MODE, int NE = EP / 128>
@@ -633,16 +715,22 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
                                                     long nslices) {
   constexpr int TI = 256, TE = 128, KB = 32;
   constexpr int EW = TE / 2, AT = EW / 16;  // entries and A tiles per wave
-  constexpr int SRS = TE + 8;               // S tile row stride (elements), rows = key blocks
-  constexpr int WRS = KB + 16;              // W tile row stride, rows = query blocks (measured
-                                            // fastest for the 16-byte fragment reads)
-  constexpr int nE = NE;                  // entry tiles computed (the first NE of the row)
-  constexpr int SCH = KB * TE / 8 / 256;  // 16-byte S chunks per thread per step (2)
-  constexpr int WCH = TI * KB / 8 / 256;  // 16-byte W chunks per thread per step (4)
-  static_assert(EP % TE == 0 && NE * TE <= EP && SCH * 8 * 256 == KB * TE &&
-                WCH * 8 * 256 == TI * KB, "tiles");
-  __shared__ __attribute__((aligned(16))) bf16_t sS[2][KB * SRS];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[2][TI * WRS];
+  constexpr int nE = NE;                    // entry tiles computed (the first NE of the row)
+  static_assert(EP % TE == 0 && NE * TE <= EP, "tiles");
+  // One stage of the ring: the S tile (KB key blocks x TE entries, rows of
+  // 256 bytes) and the W tile (TI query blocks x KB coefficients, rows of 64
+  // bytes), both unpadded.  The global-to-LDS loads write 64 lanes x 16
+  // bytes contiguously, so the bank spreading is a permutation of the
+  // 16-byte chunks within a row, chosen by the lane that loads them:
+  //   S row r: chunk f at slot (f + r) % 16  (the transpose reads of 4
+  //            consecutive rows then fall on distinct banks, as with a
+  //            16-byte row pad);
+  //   W row i: chunk f at slot f ^ ((i >> 1) & 3)  (the fragment reads of 16
+  //            consecutive rows, one chunk each, spread over all banks).
+  constexpr int SST = KB * TE, WST = TI * KB, STAGE = SST + WST;  // elements
+  __shared__ __attribute__((aligned(16))) bf16_t ring0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring2[STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -665,7 +753,7 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
     const int last = i0 + TI - 1 < M - 1 ? i0 + TI - 1 : M - 1;
     const int need = (last + KB - 1) / KB;
     nk = need < nk ? need : nk;
-    nk = nk > 0 ? nk : 1;  // one all-zero step keeps the pipeline shape
+    nk = nk > 0 ? nk : 1;
   }
 
   f32x4_t acc[AT][8];
@@ -674,80 +762,7 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[a][c] = zero4();
 
-  // Two register sets, indexed by compile-time constants only (the step loop
-  // is unrolled by two), so that they stay in registers.
-  u32x4_t sr0[SCH], wr0[WCH], sr1[SCH], wr1[WCH];
-  auto gload = [&](u32x4_t (&sr)[SCH], u32x4_t (&wr)[WCH], int k) {
-    const int b0 = k * KB;
-#pragma unroll
-    for (int u = 0; u < SCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (TE / 8), f = c % (TE / 8);
-      sr[u] = *reinterpret_cast<const u32x4_t*>(Ss + (size_t)(b0 + r) * EP + e0 + 8 * f);
-    }
-    // chunk c of the step's 16 KB tile is row c / 4, columns 8 (c % 4) ..;
-    // rows past M are zero padding
-#pragma unroll
-    for (int u = 0; u < WCH; ++u)
-      wr[u] = *reinterpret_cast<const u32x4_t*>(Wt + (size_t)k * 8192 + 8 * (tid + 256 * u));
-  };
-  auto lstore = [&](const u32x4_t (&sr)[SCH], const u32x4_t (&wr)[WCH], int buf) {
-#pragma unroll
-    for (int u = 0; u < SCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (TE / 8), f = c % (TE / 8);
-      *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) = sr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < WCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (KB / 8), f = c % (KB / 8);
-      *reinterpret_cast<u32x4_t*>(sW[buf] + r * WRS + 8 * f) = wr[u];
-    }
-  };
-  // A = S^T (rows e, contraction b via transpose reads), B = W^T (column i,
-  // the same b: W[i][8grp .. 8grp+7] is contiguous)
-  auto compute = [&](int buf) {
-    u16x8_t bw[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      bw[c] = *reinterpret_cast<const u16x8_t*>(sW[buf] + (128 * wi + 16 * c + s) * WRS + 8 * grp);
-#pragma unroll
-    for (int a = 0; a < AT; ++a) {
-      const u16x8_t af = lds_tr8(sS[buf], SRS, 0, EW * we + 16 * a, lane);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[a][c] = mfma_bf16(af, bw[c], acc[a][c]);
-    }
-  };
-  auto schedule = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x020, SCH + WCH, 0);  // global loads first
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * AT, 0);  // then the fragment reads
-    mix_big_groups<0, AT, SCH + WCH>();                          // LDS writes among MFMAs
-  };
-
-  // Step k reads LDS buffer k & 1; register set (k + 1) & 1 holds step k + 1
-  // and set k & 1 is refilled with step k + 2.  Loads and stores are
-  // unconditional (steps past the end repeat the last one, which is
-  // harmless), and no path leaves the loop from its middle, so every path
-  // into the loop head has the same loads in flight.
-  gload(sr0, wr0, 0);
-  gload(sr1, wr1, nk > 1 ? 1 : 0);
-  lstore(sr0, wr0, 0);
-  lds_barrier();
-  int k = 0;
-  for (; k + 1 < nk; k += 2) {
-    gload(sr0, wr0, k + 2 < nk ? k + 2 : nk - 1);
-    compute(0);
-    lstore(sr1, wr1, 1);
-    schedule();
-    lds_barrier();
-    gload(sr1, wr1, k + 3 < nk ? k + 3 : nk - 1);
-    compute(1);
-    lstore(sr0, wr0, 0);
-    schedule();
-    lds_barrier();
-  }
-  if (k < nk) compute(0);  // an odd last step, already in buffer 0
+  mix_big_loop<EP>(ring0, ring1, ring2, Ss, Wt, nk, e0, wave, lane, acc);
   // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
 #pragma unroll
   for (int c = 0; c < 8; ++c) {

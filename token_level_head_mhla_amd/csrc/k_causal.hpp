@@ -35,6 +35,12 @@ inline size_t causal_lds(int nb) {
   return 2 * (size_t)causal_nbp(nb) * BlockedDims<DP>::RS * sizeof(bf16_t);
 }
 
+// Static LDS of k_readout_causal: the per-wave output staging (d = 32, 64).
+template <int DP>
+constexpr size_t causal_stage_bytes() {
+  return (DP == 64 || DP == 32) ? (size_t)kBlkWaves * 16 * (DP + 8) * sizeof(bf16_t) : 2;
+}
+
 template <int DP, int PHI>
 __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
@@ -91,6 +97,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
                                : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   lds_barrier();
 
+  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
+  // per-wave LDS staging area
+  constexpr bool STAGED = DP == 64 || DP == 32;
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[causal_stage_bytes<DP>() / 2];
+  bf16_t* stage = stage_all + wave * 16 * (DP + 8);
+  const bool whole_rows = STAGED && d == DP;
   const bf16_t* vbase = sV + 4 * (s & 3);
   const int vj = 4 * grp + (s >> 2);  // key row this lane addresses for the V^T reads
   for (int q0 = 16 * wave; q0 < nb; q0 += 16 * kBlkWaves) {
@@ -141,8 +153,14 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
     }
 
     const float rd = out_scale(g, __shfl(oz[0], s));
-    store_row_tiles<NT, true>(qj < nb ? Y + off + (size_t)(base + qj) * d : nullptr, d, o, rd,
-                              grp);
+    bf16_t* yrow = qj < nb ? Y + off + (size_t)(base + qj) * d : nullptr;
+    if constexpr (STAGED) {
+      if (whole_rows) {
+        store_rows_staged<NT, true>(yrow, stage, o, rd, lane);
+        continue;
+      }
+    }
+    store_row_tiles<NT, true>(yrow, d, o, rd, grp);
   }
 }
 
@@ -164,9 +182,10 @@ int launch_readout_causal(long slices, int H, int N, int d, const Geo& g, const 
                           bf16_t* Y, hipStream_t st) {
   const size_t lds = causal_lds<DP>(g.nb);
   static std::atomic<bool> attr_set[64];
-  if (lds > 64 * 1024 &&
+  // the dynamic part may use what the static staging leaves of the 160 KB
+  if (lds > 64 * 1024 - causal_stage_bytes<DP>() &&
       lds_limit_once(reinterpret_cast<const void*>(&k_readout_causal<DP, PHI>), attr_set,
-                     160 * 1024) != 0)
+                     (int)(160 * 1024 - causal_stage_bytes<DP>())) != 0)
     return -1;
   k_readout_causal<DP, PHI><<<dim3((unsigned)g.M, (unsigned)slices), kBlkThreads, lds, st>>>(
       Q, K, V, W, St, Y, g, H, N, d);
