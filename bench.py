@@ -23,7 +23,11 @@ largest median time.
   python bench.py --copy-mb 256
 
 times a plain device copy of that size instead (the reference kernel for
-scaling the HBM byte counters of a profiler run).
+scaling the HBM byte counters of a profiler run), and
+
+  python bench.py --library-gemm --workload video
+
+times the vendor BLAS on the large-M mixing GEMM's shape.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ import argparse
 import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -58,6 +63,10 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="time a plain device copy of this many MB instead")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor BLAS (torch.bmm, bf16) on the workload's mixing GEMM "
+                         "shape, H x [M x M] @ [M x d*d], instead: a reference for the large-M "
+                         "mixing kernel")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (mhla_backward) instead of the forward")
     ap.add_argument("--decode", action="store_true",
@@ -167,6 +176,41 @@ def roofline_entry(nbytes, flops, ms, fp32=False):
     return r
 
 
+def library_gemm_bench(args):
+    """The mixing step S~ = W S of one head is a plain GEMM of shape
+    [M x M] @ [M x d*d] (bf16 operands, fp32 accumulation); this times the
+    vendor library (torch.bmm -> hipBLASLt / rocBLAS) on it, batched over the
+    heads, as a reference for the large-M mixing kernel."""
+    import torch
+    from mhla_inputs import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    g = torch.Generator(device="cpu").manual_seed(0)
+    S = wl.B * wl.H
+    A = (torch.randn(S, wl.M, wl.M, generator=g) * 0.05).to(torch.bfloat16).cuda().contiguous()
+    Bm = torch.randn(S, wl.M, wl.d * wl.d, generator=g).to(torch.bfloat16).cuda().contiguous()
+    C = torch.empty(S, wl.M, wl.d * wl.d, dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        torch.bmm(A, Bm, out=C)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.bmm(A, Bm, out=C)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = statistics.median(ts)
+    flops = 2.0 * S * wl.M * wl.M * wl.d * wl.d
+    print(json.dumps({"library_gemm": "torch.bmm bf16", "workload": wl.name,
+                      "shape": [S, wl.M, wl.M, wl.d * wl.d], "median_us": round(ms * 1e3, 2),
+                      "TFLOPs": round(flops / (ms / 1e3) / 1e12, 1),
+                      "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
+    return 0
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -177,6 +221,8 @@ def main():
         return 2
     if args.copy_mb:
         return copy_bench(args)
+    if args.library_gemm:
+        return library_gemm_bench(args)
     if args.backward:
         return backward_bench(args)
     if args.decode:
