@@ -377,7 +377,8 @@ __host__ __device__ inline size_t coef_tiled(int M, int h, int i, int b) {
 // of its 128-entry tiles.  The key blocks go in steps of 32; wave w takes
 // steps w, w + 4, ...; the z_b rows of 128 key blocks (one step per wave) are
 // staged in LDS and read as transposed B operands; the four waves' partial
-// sums meet in LDS.  grid = H * MI / 16 (MI = M rounded up to 256), block =
+// sums meet in LDS.  grid = H8 * MI / 16 (H8 = H rounded up to 8, MI = M
+// rounded up to 256; the workgroups of one head share an XCD), block =
 // 256, M % 32 == 0.
 template <int DP, int MODE>
 __global__ __launch_bounds__(256) void k_mix_prep(const float* __restrict__ W,
@@ -398,8 +399,12 @@ __global__ __launch_bounds__(256) void k_mix_prep(const float* __restrict__ W,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = lane & 15, grp = lane >> 4;
   const int nti = (M + 255) / 256 * 16;  // 16-row tiles per head
-  const int h = blockIdx.x / nti;
-  const int i0 = (blockIdx.x - h * nti) * 16;
+  // XCD-aware: the nti workgroups of a head share blockIdx.x % 8, so that
+  // one L2 holds the head's z rows, which every one of them reads
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int h = xcd + 8 * (j / nti);
+  if (h >= H) return;  // padding of the grid to whole groups of 8 heads (no barrier yet)
+  const int i0 = (j - (j / nti) * nti) * 16;
   const int i = i0 + s;                  // this lane's row of the A operand
   const int nk = M / 32;
   const float* Wr = W + ((size_t)h * M + (i < M ? i : 0)) * M;
@@ -997,8 +1002,8 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
       k_mix_big<D::EP, MODE><<<dim3(nb), 256, 0, st>>>(S, wc, St, M, H, slices);
     } else {
       // coefficients and z~ first; the GEMM then covers the DP*DP entries only
-      k_mix_prep<DP, MODE><<<dim3((unsigned)(H * nit * 16)), 256, 0, st>>>(W, S, St, wc, M, H,
-                                                                          slices);
+      const unsigned np = (unsigned)((H + 7) / 8 * 8 * nit * 16);
+      k_mix_prep<DP, MODE><<<dim3(np), 256, 0, st>>>(W, S, St, wc, M, H, slices);
       launch_mark(st, "k_mix_prep");
       constexpr int NE = DP * DP / 128;
       const unsigned nb = (unsigned)(xslices * NE * nit);
