@@ -52,8 +52,12 @@ def _check(wl, flags=0, label=""):
     ref = oracle.np_backward(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, G, wl.grid, wl.block,
                              wl.phi, norm=not (flags & FLAG_NO_NORM), dw_abs=True)
     errs = [slice_error(got[i], ref[i]) for i in range(3)] + [_head_error(got[3], ref[3], ref[4])]
+    # reported beside the gate: dW's error relative to max|dW| per head (for
+    # M = 1 with the normaliser dW is exactly 0 and this reads as the raw error)
+    dw_rel_max = _head_error(got[3], ref[3], ref[3])
     print("PARITY backward %s %s %s d=%d phi=%d M=%d flags=%d errs dQ %.2e dK %.2e dV %.2e dW %.2e"
-          % (label, wl.grid, wl.block, wl.d, wl.phi, wl.M, flags, *errs))
+          " (dW / max|dW| %.2e)"
+          % (label, wl.grid, wl.block, wl.d, wl.phi, wl.M, flags, *errs, dw_rel_max))
     for g in got:
         assert np.all(np.isfinite(g))
     for e in errs:
@@ -63,7 +67,7 @@ def _check(wl, flags=0, label=""):
 BACKWARD_CASES = [
     # (B, H, grid, block, d, phi)
     (2, 3, (1, 14, 14), (1, 7, 7), 64, PHI_ELU1),    # DeiT-like, ragged 49-token blocks
-    (2, 2, (1, 16, 16), (1, 4, 4), 72, PHI_RELU),    # DiT-like, d = 72 padded to 96
+    (2, 2, (1, 16, 16), (1, 4, 4), 72, PHI_RELU),    # DiT-like, 16-token blocks: token-pair backward
     (1, 2, (1, 32, 32), (1, 8, 8), 64, PHI_RELU),    # M = 16
     (2, 2, (1, 40, 52), (1, 4, 4), 32, PHI_ELU1),    # M = 130: partial dW tiles
     (2, 2, (1, 8, 8), (1, 8, 8), 16, PHI_ELU1),      # M = 1, d = 16 padded to 32
@@ -72,6 +76,10 @@ BACKWARD_CASES = [
     (1, 2, (1, 32, 32), (1, 2, 2), 32, PHI_ELU1),    # M = 256: large-M mixing, both directions
     (2, 2, (1, 48, 48), (1, 2, 4), 64, PHI_RELU),    # M = 288: partial 128-row dW tiles, d = 64
     (2, 2, (1, 20, 16), (1, 4, 4), 64, PHI_ELU1),    # M = 20: streamed mixing, both directions
+    (2, 2, (1, 32, 32), (1, 4, 8), 96, PHI_ELU1),    # 32-token blocks, d = 96, M = 32: dW in 8 parts
+    (1, 2, (1, 32, 64), (1, 4, 8), 72, PHI_RELU),    # d = 72 padded to 96, M = 64, B = 1, 8 parts
+    (1, 32, (1, 60, 128), (1, 4, 8), 32, PHI_ELU1),  # M = 240, B = 1, 32 slices: one part, dW
+                                                     # written directly, partial 64-row tiles
 ]
 
 

@@ -434,8 +434,9 @@ inline int dw_split(long slices, int M) {
 inline bool backward_supports(int dtype, int d, int M, long slices) {
   if (!blocked_supports(dtype, d, M, slices)) return false;
   // the precise mixing GEMM runs 64 query blocks per workgroup on a 1-D grid,
-  // and the dW tile grid is ceil(M/16)^2 (M < 256) or ceil(M/128)^2 workgroups
-  // along x
+  // and the dW tile grid along x is ceil(M/16)^2 (M <= 16), ceil(M/64)^2 times
+  // the contraction parts (16 < M < 256) or ceil(M/128)^2 (M >= 256), all at
+  // most ceil(M/16)^2
   const long n = (slices + 7) / 8 * 8 * (long)(blocked_ws_elems(d) / kMixEB) * ((M + 63) / 64);
   return n * kBlkThreads < (1L << 31) && (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
 }
