@@ -80,6 +80,7 @@ BACKWARD_CASES = [
     (1, 2, (1, 32, 64), (1, 4, 8), 72, PHI_RELU),    # d = 72 padded to 96, M = 64, B = 1, 8 parts
     (1, 32, (1, 60, 128), (1, 4, 8), 32, PHI_ELU1),  # M = 240, B = 1, 32 slices: one part, dW
                                                      # written directly, partial 64-row tiles
+    (2, 2, (1, 32, 64), (1, 2, 4), 96, PHI_RELU),    # M = 256, d = 96: large-M mixing at DP = 96
 ]
 
 

@@ -443,7 +443,8 @@ inline bool backward_supports(int dtype, int d, int M, long slices) {
 
 // Workspace: S, S~, dS~, dS ([slices][M][EP] bf16 each), the precise S~
 // ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden and rq ([slices][N]
-// fp32 each), P ([slices][M][M] fp32), the mixing's coefficient scratch.
+// fp32 each), P ([slices][M][M] fp32), the mixing's coefficient scratch (two
+// sets for the precise large-M mixing).
 inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   const size_t rows = (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
   const size_t al = 256;
@@ -451,7 +452,7 @@ inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   return 4 * up(rows) + 2 * up(rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
          2 * up((size_t)slices * N * sizeof(float)) +
          up((size_t)dw_split(slices, M) * slices * M * M * sizeof(float)) +
-         mix_coef_bytes(H, M);
+         mix_coef2_bytes(H, M);
 }
 
 template <int DP, int PHI>
@@ -522,7 +523,7 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
                                                                     pstride);
   }
   // 6. dQ, against the precise S~
-  launch_mix_f32<DP>(slices, H, M, S, W, St32, st);
+  launch_mix_f32<DP>(slices, H, M, S, W, St32, wc, st);
   k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
       Q, St32, dY, rq, dden, dQ, g, N, d);
   // 7. dK

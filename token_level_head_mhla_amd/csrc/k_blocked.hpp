@@ -781,6 +781,170 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
 }
 
 // ---------------------------------------------------------------------------
+// The precise large-M mixing (the backward's fp32 S~ for dQ): St = W S with
+// W = hi + lo split into two bf16 coefficient sets, both in the tiled layout
+// of coef_tiled (lo at Wc + lo_off), fp32 accumulation and fp32 output, over
+// all EP entries of a row (the z column included).  k_mix_coef2 writes the two
+// sets; k_mix_big_f32 is k_mix_big's ring with a 128 x 128 workgroup tile
+// (wave (we, wi): 64 entries x 64 query blocks, each fragment pair feeding
+// one MFMA per coefficient part), so that a stage (S tile, hi tile, lo tile:
+// 24 KB) matches the plain kernel's and two workgroups share a CU.
+
+// W -> hi = bf16(w), lo = bf16(w - hi), tiled; rows past M are zero.  grid =
+// H * MI * M / 1024 (MI = M rounded up to 256), block = 256: one thread per
+// four consecutive key blocks of one row.
+__global__ __launch_bounds__(256) void k_mix_coef2(const float* __restrict__ W,
+                                                   bf16_t* __restrict__ Wc, long lo_off, int M) {
+  const int MI = (M + 255) / 256 * 256;
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const int mq = M / 4;
+  const long row = t / mq;  // h * MI + i
+  const int b = 4 * (int)(t - row * mq);
+  const int h = (int)(row / MI), i = (int)(row - (long)h * MI);
+  f32x4_t w = zero4();
+  if (i < M) w = *reinterpret_cast<const f32x4_t*>(W + ((size_t)h * M + i) * M + b);
+  const uint2 hi = make_uint2(pack2(w[0], w[1]), pack2(w[2], w[3]));
+  const uint2 lo = make_uint2(pack2(w[0] - lo_f32(hi.x), w[1] - hi_f32(hi.x)),
+                              pack2(w[2] - lo_f32(hi.y), w[3] - hi_f32(hi.y)));
+  const size_t o = coef_tiled(M, h, i, b);
+  *reinterpret_cast<uint2*>(Wc + o) = hi;
+  *reinterpret_cast<uint2*>(Wc + lo_off + o) = lo;
+}
+
+template <int EP>
+__device__ __forceinline__ void mix_big_f32_loop(bf16_t* __restrict__ ring0,
+                                                 bf16_t* __restrict__ ring1,
+                                                 bf16_t* __restrict__ ring2,
+                                                 const bf16_t* __restrict__ Ss,
+                                                 const bf16_t* __restrict__ Wh,
+                                                 const bf16_t* __restrict__ Wl, int nk, int e0,
+                                                 int wave, int lane, f32x4_t (&acc)[4][4]) {
+  constexpr int TI = 128, TE = 128, KB = 32, EW = 64, IW = 64, AT = 4, CT = 4;
+  constexpr int SST = KB * TE, WST = TI * KB;  // elements of the S tile and of one W tile
+  const int s = lane & 15, grp = lane >> 4;
+  const int we = wave & 1, wi = wave >> 1;
+  // Step k's tiles into stage `st` (S rows 8w .. 8w+7, hi and lo rows
+  // 32w .. 32w+31; lane L's 16 bytes land at slot L of each 1 KB load, with
+  // the chunk permutations of k_mix_big).  Six loads per thread per step.
+  auto issue = [&](bf16_t* st, int k) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * wave + 4 * u + (lane >> 4);
+      const int f = ((lane & 15) - r) & 15;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(Ss + (size_t)(k * KB + r) * EP + e0 + 8 * f),
+          (__attribute__((address_space(3))) void*)(st + (8 * wave + 4 * u) * TE), 16, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 32 * wave + 16 * u + (lane >> 2);
+      const int f = (lane & 3) ^ ((i >> 1) & 3);
+      const size_t src = (size_t)k * 8192 + i * KB + 8 * f;
+      bf16_t* dst = st + SST + (32 * wave + 16 * u) * KB;
+      __builtin_amdgcn_global_load_lds((const void*)(Wh + src),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Wl + src),
+                                       (__attribute__((address_space(3))) void*)(dst + WST), 16,
+                                       0, 0);
+    }
+  };
+  auto compute = [&](const bf16_t* st) {
+    const bf16_t* sS = st;
+    const bf16_t* sH = st + SST;
+    const bf16_t* sL = st + SST + WST;
+    u16x8_t bh[CT], bl[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int o = (IW * wi + 16 * c + s) * KB + 8 * (grp ^ ((s >> 1) & 3));
+      bh[c] = *reinterpret_cast<const u16x8_t*>(sH + o);
+      bl[c] = *reinterpret_cast<const u16x8_t*>(sL + o);
+    }
+    const int r_lo = 8 * grp + (s >> 2), half = 4 * (s & 1);
+#pragma unroll
+    for (int a = 0; a < AT; ++a) {
+      const int f = (EW * we + 16 * a) / 8 + ((s & 3) >> 1);
+      const i16x4_t lo = lds_tr4(sS + r_lo * TE + 8 * ((f + r_lo) & 15) + half);
+      const i16x4_t hi = lds_tr4(sS + (r_lo + 4) * TE + 8 * ((f + r_lo + 4) & 15) + half);
+      const u16x8_t af =
+          __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[a][c] = mfma_bf16(af, bh[c], acc[a][c]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[a][c] = mfma_bf16(af, bl[c], acc[a][c]);
+    }
+  };
+  // the step and ring of mix_big_loop
+  auto step = [&](bf16_t* cur, bf16_t* next2, int k) {
+    __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(next2, k + 2 < nk ? k + 2 : nk - 1);
+    compute(cur);
+  };
+  issue(ring0, 0);
+  issue(ring1, nk > 1 ? 1 : 0);
+  int k = 0;
+  for (; k + 3 <= nk; k += 3) {
+    step(ring0, ring2, k);
+    step(ring1, ring0, k + 1);
+    step(ring2, ring1, k + 2);
+  }
+  if (k < nk) step(ring0, ring2, k);
+  if (k + 1 < nk) step(ring1, ring0, k + 1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no load is left in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// grid = 8 * ceil(slices / 8) * (EP / 128) * ceil(M / 128), XCD-aware like
+// k_mix_big; block = 256; M >= kMixBigM, M % 32 == 0.
+template <int EP>
+__global__ __launch_bounds__(256, 2) void k_mix_big_f32(const bf16_t* __restrict__ S,
+                                                        const bf16_t* __restrict__ Wc, long lo_off,
+                                                        float* __restrict__ St, int M, int H,
+                                                        long nslices) {
+  constexpr int TI = 128, TE = 128, KB = 32;
+  constexpr int STAGE = KB * TE + 2 * TI * KB;  // elements: S, hi, lo tiles (24 KB)
+  __shared__ __attribute__((aligned(16))) bf16_t ring0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring2[STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int we = wave & 1, wi = wave >> 1;
+  const int nE = EP / TE, nI = (M + TI - 1) / TI;
+  const int per = nE * nI;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const long slice = (long)(j / per) * 8 + xcd;
+  if (slice >= nslices) return;  // before any barrier
+  const int rem = j - (j / per) * per;
+  const int e0 = (rem / nI) * TE, i0 = (rem - (rem / nI) * nI) * TI;
+  const int h = (int)(slice % H);
+  const bf16_t* Ss = S + (size_t)slice * M * EP;
+  // rows i0 .. i0+127 are one contiguous half of a 256-row coefficient tile
+  const bf16_t* Wh = Wc + coef_tiled(M, h, i0, 0);
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = zero4();
+  mix_big_f32_loop<EP>(ring0, ring1, ring2, Ss, Wh, Wh + lo_off, M / KB, e0, wave, lane, acc);
+  // acc[a][c] lane (s, grp) element r = S~[i0 + 64wi + 16c + s][e0 + 64we + 16a + 4grp + r]
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = i0 + 64 * wi + 16 * c + s;
+    if (i < M) {
+      float* row = St + ((size_t)slice * M + i) * EP + e0 + 64 * we + 4 * grp;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) *reinterpret_cast<f32x4_t*>(row + 16 * a) = acc[a][c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Readout.  grid = (ceil(M / 4), slices), block = 256; wave w reads out query
 // block 4*blockIdx.x + w, 16 queries per step.  Y^T = S~_i^T phi(Q)^T with the
 // contraction split as features 32ks + 8grp .. +7 on both operands; the z~
@@ -896,6 +1060,9 @@ inline size_t mix_coef_bytes(int H, int M) {
   const size_t mi = (size_t)(M + 255) / 256 * 256;  // query-block rows, zero-padded
   return ((size_t)H * mi * M * sizeof(bf16_t) + 255) / 256 * 256;
 }
+
+// Two coefficient sets (hi and lo parts) of the precise large-M mixing.
+inline size_t mix_coef2_bytes(int H, int M) { return 2 * mix_coef_bytes(H, M); }
 
 // Workspace: S and S~, [slices][M][EP] bf16 each, then the mixing's bf16
 // coefficients (large M only; tiled, see coef_tiled).
@@ -1036,20 +1203,34 @@ void launch_mix(long slices, int H, int M, const bf16_t* S, const float* W, bf16
   else launch_mix_m<DP, kMixPlain>(slices, H, M, S, W, St, wc, st);
 }
 
-// The precise variant (fp32 S~, coefficients split in two bf16 parts), with
-// 64 query blocks per workgroup so that both coefficient tiles fit in LDS.
+// The precise variant (fp32 S~, coefficients split in two bf16 parts): for
+// large M the ring kernel k_mix_big_f32, whose two coefficient sets take
+// mix_coef2_bytes(H, M) of scratch at wc; otherwise k_mix_mfma with 64 query
+// blocks per workgroup, so that both coefficient tiles fit in LDS.
 template <int DP>
 void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, float* St,
-                    hipStream_t st) {
+                    bf16_t* wc, hipStream_t st) {
   using D = BlockedDims<DP>;
   if (M <= kMixSmallM) {
     launch_mix_small<D::EP, kMixPlain, float>(slices, H, M, S, W, St, st);
     return;
   }
   const long xslices = (slices + 7) / 8 * 8;
+  if (mix_coef_bytes(H, M) != 0) {
+    // large M: two tiled bf16 coefficient sets in wc (mix_coef2_bytes)
+    const long lo_off = (long)(mix_coef_bytes(H, M) / sizeof(bf16_t));
+    const int mi = (M + 255) / 256 * 256;
+    k_mix_coef2<<<dim3((unsigned)((long)H * mi * M / 1024)), 256, 0, st>>>(W, wc, lo_off, M);
+    launch_mark(st, "k_mix_coef2");
+    const unsigned nb = (unsigned)(xslices * (D::EP / 128) * ((M + 127) / 128));
+    k_mix_big_f32<D::EP><<<dim3(nb), 256, 0, st>>>(S, wc, lo_off, St, M, H, slices);
+    launch_mark(st, "k_mix_big_f32");
+    return;
+  }
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + 63) / 64));
   k_mix_mfma<D::EP, 64, kMixPlain, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
                                                                            slices);
+  launch_mark(st, "k_mix_mfma");
 }
 
 // MI355X's last-level cache (the 256 MB Infinity Cache).  When a blocked call
