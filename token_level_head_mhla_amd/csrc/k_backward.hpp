@@ -15,7 +15,9 @@
 //
 // Treating z as one more value column ([S | z], [V | 1], [dn | dden]) makes
 // every step one of the forward's building blocks:
-//   1. S, S~          summary kernel and mixing GEMM, as in the forward
+//   1. S, S~          summary kernel, then the mixing GEMM in its precise
+//                     form (W as two bf16 parts, S~ in fp32); the same S~
+//                     serves steps 2 and 6
 //   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
 //   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
 //   4. dS, dz         mixing GEMM with W transposed
@@ -46,10 +48,12 @@ __device__ __forceinline__ float dphi_apply(float x) {
 // block 4*blockIdx.x + w, 16 queries per step, exactly like the readout
 // (Y^T tiles and the z~ row for the denominator), then forms dn and dden.
 // Writes dN [slices, N, d] bf16, and dden and the per-token factor rq (1/den,
-// or 1 with the normaliser off) as [slices, N] fp32.
-template <int DP, int PHI>
+// or 1 with the normaliser off) as [slices, N] fp32.  TT = float reads the
+// precise fp32 S~ (rounded to bf16 operands as it is loaded), so that the
+// backward needs only one mixing of S.
+template <int DP, int PHI, typename TT = bf16_t>
 __global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ St, const bf16_t* __restrict__ G,
+    const bf16_t* __restrict__ Q, const TT* __restrict__ St, const bf16_t* __restrict__ G,
     bf16_t* __restrict__ dN, float* __restrict__ dden, float* __restrict__ rq, Geo g, int N,
     int d) {
   using D = BlockedDims<DP>;
@@ -61,17 +65,26 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
   const int i = blockIdx.x * kBlkWaves + wave;
   if (i >= g.M) return;  // no barrier in this kernel
   const size_t off = (size_t)slice * N * d;
-  const bf16_t* row = St + ((size_t)slice * g.M + i) * EP;
+  const TT* row = St + ((size_t)slice * g.M + i) * EP;
+  // eight consecutive entries of the row as one bf16 operand
+  auto ld8 = [&](const TT* p) -> u16x8_t {
+    if constexpr (sizeof(TT) == 4) {
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(p);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(p + 4);
+      return __builtin_bit_cast(u16x8_t, u32x4_t{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]),
+                                                 pack2(x1[0], x1[1]), pack2(x1[2], x1[3])});
+    } else {
+      return *reinterpret_cast<const u16x8_t*>(p);
+    }
+  };
   u16x8_t af[NT][DS], az[DS];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks)
-      af[ct][ks] = *reinterpret_cast<const u16x8_t*>(row + (16 * ct + s) * DP + 32 * ks + 8 * grp);
+    for (int ks = 0; ks < DS; ++ks) af[ct][ks] = ld8(row + (16 * ct + s) * DP + 32 * ks + 8 * grp);
 #pragma unroll
   for (int ks = 0; ks < DS; ++ks)
-    az[ks] = s == 0 ? *reinterpret_cast<const u16x8_t*>(row + DP * DP + 32 * ks + 8 * grp)
-                    : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    az[ks] = s == 0 ? ld8(row + DP * DP + 32 * ks + 8 * grp) : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   const int bb = g.blockbase(i);
   for (int q0 = 0; q0 < g.nb; q0 += 16) {
     const int j = q0 + s;
@@ -441,7 +454,7 @@ inline bool backward_supports(int dtype, int d, int M, long slices) {
   return n * kBlkThreads < (1L << 31) && (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
 }
 
-// Workspace: S, S~, dS~, dS ([slices][M][EP] bf16 each), the precise S~
+// Workspace: S, dS~, dS ([slices][M][EP] bf16 each), the precise S~
 // ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden and rq ([slices][N]
 // fp32 each), P ([slices][M][M] fp32), the mixing's coefficient scratch (two
 // sets for the precise large-M mixing).
@@ -449,7 +462,7 @@ inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   const size_t rows = (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
   const size_t al = 256;
   auto up = [&](size_t x) { return (x + al - 1) / al * al; };
-  return 4 * up(rows) + 2 * up(rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
+  return 3 * up(rows) + up(2 * rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
          2 * up((size_t)slices * N * sizeof(float)) +
          up((size_t)dw_split(slices, M) * slices * M * M * sizeof(float)) +
          mix_coef2_bytes(H, M);
@@ -466,8 +479,7 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   const size_t rows = (size_t)slices * M * D::EP;
   char* p = static_cast<char*>(ws);
   bf16_t* S = reinterpret_cast<bf16_t*>(p);
-  bf16_t* St = S + rows;  // launch_summary_mix places S~ right after S
-  p += 2 * up(rows * sizeof(bf16_t));
+  p += up(rows * sizeof(bf16_t));
   bf16_t* dSt = reinterpret_cast<bf16_t*>(p);
   p += up(rows * sizeof(bf16_t));
   bf16_t* dS = reinterpret_cast<bf16_t*>(p);
@@ -485,18 +497,16 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   const size_t pstride = (size_t)slices * M * M;
   p += up((size_t)nsp * pstride * sizeof(float));
   bf16_t* wc = reinterpret_cast<bf16_t*>(p);
-  static_assert(sizeof(bf16_t) == 2, "bf16");
-  if (2 * up(rows * sizeof(bf16_t)) != 2 * rows * sizeof(bf16_t)) {
-    // S~ must directly follow S (launch_summary_mix's layout): rows*2 bytes is
-    // a multiple of 256 because EP is a multiple of 128
-    return -1;
-  }
   const unsigned nsl = (unsigned)slices;
-  // 1. forward state
-  launch_summary_mix<DP, PHI>(slices, H, N, d, g, K, V, W, S, wc, 0, st);
+  // 1. forward state: S, and the precise S~ (fp32, W in two bf16 parts),
+  //    which serves both the recomputed readout of step 2 and dQ in step 6
+  k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(K, V, S, g, N, d,
+                                                                           nullptr);
+  launch_mix_f32<DP>(slices, H, M, S, W, St32, wc, st);
   // 2. dn, dden
   const unsigned nbw = (unsigned)((M + kBlkWaves - 1) / kBlkWaves);
-  k_bwd_dn<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St, dY, dN, dden, rq, g, N, d);
+  k_bwd_dn<DP, PHI, float><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St32, dY, dN, dden, rq, g,
+                                                                   N, d);
   // 3. dS~ = phi(Q)^T dN per query block, dz~ weighted by dden
   k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(Q, dN, dSt, g, N, d,
                                                                            dden);
@@ -523,7 +533,6 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
                                                                     pstride);
   }
   // 6. dQ, against the precise S~
-  launch_mix_f32<DP>(slices, H, M, S, W, St32, wc, st);
   k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
       Q, St32, dY, rq, dden, dQ, g, N, d);
   // 7. dK
