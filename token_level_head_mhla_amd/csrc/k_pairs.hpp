@@ -110,26 +110,58 @@ __global__ __launch_bounds__(kPairsThreads) void k_pairs(
   int* sB = reinterpret_cast<int*>(sW + M * M);  // first token of every block
 
   // ---- stage: zero pad columns and row N, then phi(K), V, ones column ------
+  // The K and V loads of a batch of kStageU 16-byte chunks per thread are all
+  // issued (clamped in range) before the LDS is zero-filled, so that they are
+  // in flight together; the chunks are written once the fill is done.
+  constexpr int kStageU = 6;
+  const int F8 = d >> 3;
+  const int items = N * F8;
+  const float inv8 = 1.0f / (float)F8, invnb = 1.0f / (float)nb;
+  u32x4_t kst[kStageU], vst[kStageU];
+  int dst[kStageU];
+  auto stage_load = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int it = base + u * kPairsThreads + tid;
+      const int itc = it < items ? it : items - 1;
+      const int row = (int)(((float)itc + 0.5f) * inv8);
+      const int f = itc - row * F8;
+      const int b = (int)(((float)row + 0.5f) * invnb);
+      const size_t src = off + (size_t)(g.blockbase(b) + g.tokoff(row - b * nb)) * d + 8 * f;
+      kst[u] = *reinterpret_cast<const u32x4_t*>(K + src);
+      vst[u] = *reinterpret_cast<const u32x4_t*>(V + src);
+      dst[u] = it < items ? (row << 8) | f : -1;  // f < 16, row <= 512
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      if (dst[u] >= 0) {
+        const int row = dst[u] >> 8, f = dst[u] & 255;
+        *reinterpret_cast<u32x4_t*>(sK + prow(row, RSK) + 8 * f) = phi8<PHI>(kst[u]);
+        *reinterpret_cast<u32x4_t*>(sV + prow(row, RSV) + 8 * f) = vst[u];
+      }
+    }
+  };
+  // W (M * M <= 1024 entries: two per thread) is requested first, so that
+  // waiting for it does not wait for the K / V loads behind it
+  static_assert(2 * kPairsThreads >= 32 * 32, "W entries per thread");
+  const float* Wh = W + (size_t)h * M * M;
+  const float wv0 = tid < M * M ? Wh[tid] : 0.0f;
+  const float wv1 = tid + kPairsThreads < M * M ? Wh[tid + kPairsThreads] : 0.0f;
+  stage_load(0);
   for (int e = tid; e < (int)((L::k_bytes(N) + L::v_bytes(N)) / 16); e += kPairsThreads)
     reinterpret_cast<u32x4_t*>(smem)[e] = u32x4_t{0u, 0u, 0u, 0u};
-  for (int e = tid; e < M * M; e += kPairsThreads) sW[e] = W[(size_t)h * M * M + e];
+  if (tid < M * M) sW[tid] = wv0;
+  if (tid + kPairsThreads < M * M) sW[tid + kPairsThreads] = wv1;
   for (int b = tid; b < M; b += kPairsThreads) sB[b] = g.blockbase(b);
   lds_barrier();
-  {
-    const int F8 = d >> 3;
-    const float inv8 = 1.0f / (float)F8, invnb = 1.0f / (float)nb;
-    for (int it = tid; it < N * F8; it += kPairsThreads) {
-      const int row = (int)(((float)it + 0.5f) * inv8);
-      const int f = it - row * F8;
-      const int b = (int)(((float)row + 0.5f) * invnb);
-      const size_t src = off + (size_t)(sB[b] + g.tokoff(row - b * nb)) * d + 8 * f;
-      const u32x4_t kr = *reinterpret_cast<const u32x4_t*>(K + src);
-      const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(V + src);
-      *reinterpret_cast<u32x4_t*>(sK + prow(row, RSK) + 8 * f) = phi8<PHI>(kr);
-      *reinterpret_cast<u32x4_t*>(sV + prow(row, RSV) + 8 * f) = vr;
-    }
-    for (int t = tid; t < N; t += kPairsThreads) sV[prow(t, RSV) + d] = 0x3f80;  // bf16 1.0
+  stage_store();
+  for (int base = kStageU * kPairsThreads; base < items; base += kStageU * kPairsThreads) {
+    stage_load(base);
+    stage_store();
   }
+  for (int t = tid; t < N; t += kPairsThreads) sV[prow(t, RSV) + d] = 0x3f80;  // bf16 1.0
   lds_barrier();
 
   // ---- this wave's query blocks: phi(Q) operands straight from global -------
