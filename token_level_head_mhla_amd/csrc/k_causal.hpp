@@ -66,17 +66,30 @@ __global__ __launch_bounds__(kBlkThreads) void k_readout_causal(
   const int F8 = d >> 3;
 
   // ---- stage phi(K) and V of the chunk; rows >= nb and features >= d are 0 --
-  for (int it = tid; it < NBP * F8P; it += kBlkThreads) {
-    const int j = it / F8P, f = it - (it / F8P) * F8P;
-    u32x4_t kr = u32x4_t{0u, 0u, 0u, 0u}, vr = u32x4_t{0u, 0u, 0u, 0u};
-    const bool real = j < nb && f < F8;
-    if (real) {
-      const size_t src = off + (size_t)(base + j) * d + 8 * f;
-      kr = *reinterpret_cast<const u32x4_t*>(K + src);
-      vr = *reinterpret_cast<const u32x4_t*>(V + src);
+  // The loads of kStageU chunks per thread are issued together (clamped in
+  // range, so that every load is issued), then written.
+  constexpr int kStageU = 2;
+  for (int it0 = 0; it0 < NBP * F8P; it0 += kStageU * kBlkThreads) {
+    u32x4_t kr[kStageU], vr[kStageU];
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int it = it0 + u * kBlkThreads + tid;
+      const int j = it / F8P, f = it - (it / F8P) * F8P;
+      const size_t src = off + (size_t)(base + min(j, nb - 1)) * d + 8 * min(f, F8 - 1);
+      kr[u] = *reinterpret_cast<const u32x4_t*>(K + src);
+      vr[u] = *reinterpret_cast<const u32x4_t*>(V + src);
     }
-    *reinterpret_cast<u32x4_t*>(sK + j * RS + 8 * f) = real ? phi8<PHI>(kr) : kr;
-    *reinterpret_cast<u32x4_t*>(sV + j * RS + 8 * f) = vr;
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int it = it0 + u * kBlkThreads + tid;
+      const int j = it / F8P, f = it - (it / F8P) * F8P;
+      if (it < NBP * F8P) {
+        const bool real = j < nb && f < F8;
+        const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(sK + j * RS + 8 * f) = real ? phi8<PHI>(kr[u]) : zero;
+        *reinterpret_cast<u32x4_t*>(sV + j * RS + 8 * f) = real ? vr[u] : zero;
+      }
+    }
   }
 
   // ---- prefix mixture S^<_i (transposed rows) and z^<_i from the workspace ----
