@@ -518,16 +518,20 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
   const bf16_t* Ss = S + (size_t)slice * M * EP;
   const float* Wh = W + (size_t)h * M * M;
 
-  // coefficients coef(i, b) as bf16, [i][b]; zero for i, b >= M
-  for (int e = tid; e < MP * MP; e += kBlkThreads) {
-    const int i = e / MP, b = e - (e / MP) * MP;
-    float w = 0.0f;
-    if (i < M && b < M) {
-      if constexpr (MODE == kMixTransposed) w = Wh[(size_t)b * M + i];
-      else w = Wh[(size_t)i * M + b];
-      if constexpr (MODE == kMixCausal) w = b < i ? w : 0.0f;
-    }
-    sW[i * WRS + b] = f32_to_bf16(w);
+  // coefficients coef(i, b) as bf16, [i][b]; zero for i, b >= M.  All of a
+  // thread's W loads are issued first, then the first S tile's (sload(0)
+  // below), so that the coefficient wait does not cover the tile.
+  constexpr int WPT = MP * MP / kBlkThreads;  // coefficients per thread
+  static_assert(WPT * kBlkThreads == MP * MP, "coefficients per thread");
+  // (loads unconditional at clamped indices; the mode's zeros are applied
+  // when the coefficients are written)
+  float wv[WPT];
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    const int e = tid + q * kBlkThreads;
+    const int i = min(e / MP, M - 1), b = min(e - (e / MP) * MP, M - 1);
+    if constexpr (MODE == kMixTransposed) wv[q] = Wh[(size_t)b * M + i];
+    else wv[q] = Wh[(size_t)i * M + b];
   }
   // S chunk u of a tile: key-block row r (clamped in bounds; its coefficients
   // are zero past M), 16-byte piece f
@@ -550,6 +554,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
     }
   };
   sload(0);
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    const int e = tid + q * kBlkThreads;
+    const int i = e / MP, b = e - (e / MP) * MP;
+    const bool keep = i < M && b < M && (MODE != kMixCausal || b < i);
+    sW[i * WRS + b] = f32_to_bf16(keep ? wv[q] : 0.0f);
+  }
   lstore(0);
   lds_barrier();
   for (int t = 0; t < nt; ++t) {
