@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
 // S~ is stored in fp32, so that the only rounding left is that of S.
 enum { kMixPlain = 0, kMixCausal = 1, kMixTransposed = 2 };
 
-template <int EP, int IB, int MODE, typename OutT = bf16_t>
+template <int EP, int IB, int MODE, typename OutT = bf16_t, bool WVEC = true>
 __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restrict__ S,
                                                           const float* __restrict__ W,
                                                           OutT* __restrict__ St, int M, int H,
@@ -212,7 +212,8 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   const int h = (int)(slice % H);
   const bf16_t* Ss = S + (size_t)slice * M * EP;
   const float* Wh = W + (size_t)h * M * M;
-  const bool wvec = (M & 3) == 0 && MODE != kMixTransposed;
+  // WVEC (M % 4 == 0, not transposed): W rows are read as 16-byte vectors
+  static_assert(!WVEC || MODE != kMixTransposed, "vector W loads read rows");
 
   f32x4_t acc[AT][BT];
 #pragma unroll
@@ -222,50 +223,55 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
 
   u32x4_t sr[SCH], sr1[SCH];
   f32x4_t wr[WCH], wr1[WCH];
+  // Loads are unconditional, at clamped rows and columns, so that every load
+  // of a step is in flight before the first wait; the zeros (key blocks past
+  // M, query blocks past M, the prefix mask) are applied when the tiles are
+  // written to LDS.
 #define MHLA_MIX_GLOAD(b0, sr, wr)                                                        \
   _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
     const int c = tid + kBlkThreads * u;                                                  \
     const int r = c / (EB / 8), f = c % (EB / 8);                                         \
-    sr[u] = (b0) + r < M                                                                  \
-                ? *reinterpret_cast<const u32x4_t*>(Ss + (size_t)((b0) + r) * EP + e0 + 8 * f) \
-                : u32x4_t{0u, 0u, 0u, 0u};                                                \
+    sr[u] = *reinterpret_cast<const u32x4_t*>(Ss + (size_t)min((b0) + r, M - 1) * EP + e0 + \
+                                              8 * f);                                     \
+  }                                                                                       \
+  _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (KB / 4), f = c % (KB / 4);                                         \
+    const int ic = min(i0 + r, M - 1), bc = (b0) + 4 * f;                                 \
+    f32x4_t v;                                                                            \
+    if constexpr (WVEC) {                                                                 \
+      v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)ic * M + min(bc, M - 4));        \
+    } else if constexpr (MODE == kMixTransposed) {                                        \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q)                                       \
+        v[q] = Wh[(size_t)min(bc + q, M - 1) * M + ic];                                   \
+    } else {                                                                              \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q)                                       \
+        v[q] = Wh[(size_t)ic * M + min(bc + q, M - 1)];                                   \
+    }                                                                                     \
+    wr[u] = v;                                                                            \
+  }
+#define MHLA_MIX_LSTORE(buf, sr, wr, b0)                                                  \
+  _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
+    const int c = tid + kBlkThreads * u;                                                  \
+    const int r = c / (EB / 8), f = c % (EB / 8);                                         \
+    *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) =                              \
+        (b0) + r < M ? sr[u] : u32x4_t{0u, 0u, 0u, 0u};                                    \
   }                                                                                       \
   _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
     const int c = tid + kBlkThreads * u;                                                  \
     const int r = c / (KB / 4), f = c % (KB / 4);                                         \
     const int i = i0 + r, bc = (b0) + 4 * f;                                              \
-    f32x4_t v = zero4();                                                                  \
-    if (i < M) {                                                                          \
-      if (wvec && bc + 3 < M) {                                                           \
-        v = *reinterpret_cast<const f32x4_t*>(Wh + (size_t)i * M + bc);                   \
-      } else if constexpr (MODE == kMixTransposed) {                                      \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M)                     \
-          v[q] = Wh[(size_t)(bc + q) * M + i];                                            \
-      } else {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q < M)                     \
-          v[q] = Wh[(size_t)i * M + bc + q];                                              \
-      }                                                                                   \
-      if constexpr (MODE == kMixCausal) {                                                 \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) if (bc + q >= i) v[q] = 0.0f;       \
-      }                                                                                   \
+    f32x4_t w = wr[u];                                                                    \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                       \
+      const bool keep = i < M && bc + q < M && (MODE != kMixCausal || bc + q < i);        \
+      w[q] = keep ? w[q] : 0.0f;                                                          \
     }                                                                                     \
-    wr[u] = v;                                                                            \
-  }
-#define MHLA_MIX_LSTORE(buf, sr, wr)                                                      \
-  _Pragma("unroll") for (int u = 0; u < SCH; ++u) {                                       \
-    const int c = tid + kBlkThreads * u;                                                  \
-    const int r = c / (EB / 8), f = c % (EB / 8);                                         \
-    *reinterpret_cast<u32x4_t*>(sS[buf] + r * SRS + 8 * f) = sr[u];                       \
-  }                                                                                       \
-  _Pragma("unroll") for (int u = 0; u < WCH; ++u) {                                       \
-    const int c = tid + kBlkThreads * u;                                                  \
-    const int r = c / (KB / 4), f = c % (KB / 4);                                         \
-    const uint2 hi_ = make_uint2(pack2(wr[u][0], wr[u][1]), pack2(wr[u][2], wr[u][3]));  \
+    const uint2 hi_ = make_uint2(pack2(w[0], w[1]), pack2(w[2], w[3]));                   \
     *reinterpret_cast<uint2*>(sW[buf][0] + r * WRS + 4 * f) = hi_;                        \
     if constexpr (PREC) {                                                                 \
       *reinterpret_cast<uint2*>(sW[buf][WSPLIT - 1] + r * WRS + 4 * f) =                  \
-          make_uint2(pack2(wr[u][0] - lo_f32(hi_.x), wr[u][1] - hi_f32(hi_.x)),           \
-                     pack2(wr[u][2] - lo_f32(hi_.y), wr[u][3] - hi_f32(hi_.y)));          \
+          make_uint2(pack2(w[0] - lo_f32(hi_.x), w[1] - hi_f32(hi_.x)),                   \
+                     pack2(w[2] - lo_f32(hi_.y), w[3] - hi_f32(hi_.y)));                  \
     }                                                                                     \
   }
 
@@ -299,20 +305,20 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
     // first when nk = 1; loads stay unconditional so the waits are exact)
     MHLA_MIX_GLOAD(0, sr, wr)
     MHLA_MIX_GLOAD((nk - 1) * KB, sr1, wr1)
-    MHLA_MIX_LSTORE(0, sr, wr)
-    MHLA_MIX_LSTORE(1, sr1, wr1)
+    MHLA_MIX_LSTORE(0, sr, wr, 0)
+    MHLA_MIX_LSTORE(1, sr1, wr1, (nk - 1) * KB)
     lds_barrier();
     compute(0);
     if (nk == 2) compute(1);
   } else {
     MHLA_MIX_GLOAD(0, sr, wr)
-    MHLA_MIX_LSTORE(0, sr, wr)
+    MHLA_MIX_LSTORE(0, sr, wr, 0)
     lds_barrier();
     for (int k = 0; k < nk; ++k) {
       const int buf = k & 1;
       if (k + 1 < nk) { MHLA_MIX_GLOAD((k + 1) * KB, sr, wr) }
       compute(buf);
-      if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1, sr, wr) }
+      if (k + 1 < nk) { MHLA_MIX_LSTORE(buf ^ 1, sr, wr, (k + 1) * KB) }
       lds_barrier();
     }
   }
@@ -1199,10 +1205,19 @@ void launch_mix_m(long slices, int H, int M, const bf16_t* S, const float* W, bf
   }
   const int ib = mix_ib(M);
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + ib - 1) / ib));
-  if (ib == 64)
-    k_mix_mfma<D::EP, 64, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
+  constexpr bool kVec = MODE != kMixTransposed;  // with M % 4 == 0
+  if (ib == 64 && (M & 3) == 0)
+    k_mix_mfma<D::EP, 64, MODE, bf16_t, kVec><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
+                                                                               slices);
+  else if (ib == 64)
+    k_mix_mfma<D::EP, 64, MODE, bf16_t, false><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
+                                                                                slices);
+  else if ((M & 3) == 0)
+    k_mix_mfma<D::EP, 128, MODE, bf16_t, kVec><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
+                                                                                slices);
   else
-    k_mix_mfma<D::EP, 128, MODE><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H, slices);
+    k_mix_mfma<D::EP, 128, MODE, bf16_t, false><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M,
+                                                                                 H, slices);
   launch_mark(st, "k_mix_mfma");
 }
 
@@ -1239,8 +1254,12 @@ void launch_mix_f32(long slices, int H, int M, const bf16_t* S, const float* W, 
     return;
   }
   const unsigned n = (unsigned)(xslices * (D::EP / kMixEB) * ((M + 63) / 64));
-  k_mix_mfma<D::EP, 64, kMixPlain, float><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M, H,
-                                                                           slices);
+  if ((M & 3) == 0)
+    k_mix_mfma<D::EP, 64, kMixPlain, float, true><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M,
+                                                                                 H, slices);
+  else
+    k_mix_mfma<D::EP, 64, kMixPlain, float, false><<<dim3(n), kBlkThreads, 0, st>>>(S, W, St, M,
+                                                                                  H, slices);
   launch_mark(st, "k_mix_mfma");
 }
 
