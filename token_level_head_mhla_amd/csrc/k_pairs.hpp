@@ -41,14 +41,17 @@ constexpr int kPairsMaxQB = 4;  // query blocks per wave (M <= 32)
 //   feat_operand: from global row `tok` (phi applied; features past d and
 //                 tok < 0 give 0)
 //   feat_row:     from an LDS row of phi values (pad columns already 0)
+// The load is unconditional (token and feature clamped in range) and masked
+// afterwards: a load under a branch makes the compiler wait for it at the
+// join, which would issue a wave's operand loads one round trip at a time.
 template <int PHI>
 __device__ __forceinline__ u16x8_t feat_operand(const bf16_t* base, int tok, int d, int ks,
                                                 int ks_full, int grp) {
   const int k0 = 32 * ks + 8 * grp;
   const bool ok = tok >= 0 && k0 < d && (ks < ks_full || grp < 2);
-  u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-  if (ok) v = phi8<PHI>(*reinterpret_cast<const u32x4_t*>(base + (size_t)tok * d + k0));
-  return __builtin_bit_cast(u16x8_t, v);
+  const u32x4_t v =
+      *reinterpret_cast<const u32x4_t*>(base + (size_t)(tok > 0 ? tok : 0) * d + min(k0, d - 8));
+  return __builtin_bit_cast(u16x8_t, ok ? phi8<PHI>(v) : u32x4_t{0u, 0u, 0u, 0u});
 }
 
 __device__ __forceinline__ u16x8_t feat_row(const bf16_t* lds, int row, int rs, int ks,

@@ -136,6 +136,16 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
 #pragma unroll
     for (int ks = 0; ks < KSF; ++ks) qf[u][ks] = feat_operand<PHI>(Q + off, qtok[u], d, ks, KS, grp);
   }
+  // G of this lane's query and value columns 16c + 4grp .. +3, requested now
+  // (unconditional, clamped; masked where it is used) so that it is in flight
+  // during pass 1
+  uint2 gx[QB][CT];
+#pragma unroll
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      gx[u][c] = *reinterpret_cast<const uint2*>(G + off + (size_t)(qtok[u] > 0 ? qtok[u] : 0) * d +
+                                                 min(16 * c + 4 * grp, d - 4));
 
   // key member s of a block: row of this lane for the row-operand reads; key
   // member 4grp + s/4: row supplied to the transpose reads
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_q(
       const int c0 = 16 * c + 4 * grp;
       f32x4_t gv = zero4();
       if (qtok[u] >= 0 && c0 < d) {
-        const uint2 x = *reinterpret_cast<const uint2*>(G + off + (size_t)qtok[u] * d + c0);
+        const uint2 x = gx[u][c];
         gv = f32x4_t{lo_f32(x.x), hi_f32(x.x), lo_f32(x.y), hi_f32(x.y)};
       }
 #pragma unroll
@@ -394,11 +404,13 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
     // V in the acc8 order of the value columns; columns past d are 0
 #pragma unroll
     for (int m = 0; m < CS; ++m) {
+      // unconditional loads at clamped addresses, masked after
       const int c0 = 32 * m + 4 * grp, c1 = c0 + 16;
-      uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-      if (real && c0 < d) lo = *reinterpret_cast<const uint2*>(V + off + (size_t)ktok[u] * d + c0);
-      if (real && c1 < d) hi = *reinterpret_cast<const uint2*>(V + off + (size_t)ktok[u] * d + c1);
-      vf[u][m] = from_u2x2(lo, hi);
+      const bf16_t* vrow = V + off + (size_t)(real ? ktok[u] : 0) * d;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + min(c0, d - 4));
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + min(c1, d - 4));
+      const uint2 z = make_uint2(0u, 0u);
+      vf[u][m] = from_u2x2(real && c0 < d ? lo : z, real && c1 < d ? hi : z);
     }
   }
 
