@@ -91,6 +91,13 @@ def test_backward_shapes(B, H, grid, block, d, phi, norm):
     _check(wl, 0 if norm else FLAG_NO_NORM)
 
 
+def test_backward_mixing_many_slices():
+    """M = 256, 64 slices, d = 32: the transposed large-M mixing runs 72 tiles
+    per XCD, a second, ragged round of workgroups."""
+    wl = custom_workload(1, 64, 32, (1, 1, 1024), (1, 1, 4), PHI_ELU1, DTYPE_BF16, index=461)
+    _check(wl, 0)
+
+
 PAIRS_BACKWARD_CASES = [
     # (B, H, grid, block, d, phi): blocks of at most 16 tokens take the
     # token-pair backward (two kernels, no d x d state)

@@ -173,6 +173,30 @@ def test_blocked_shapes(grid, block, d, phi):
     assert err <= TOL[DTYPE_BF16]
 
 
+# M >= 256 with many slices: the large-M mixing runs several rounds of
+# workgroups on each XCD (one 256-query-block x 128-entry tile each; an XCD
+# takes ceil(B * H / 8) * (d * d / 128) * ceil(M / 256) of them, 64 at a time
+# on 256 CUs), including a ragged last round and partial query tiles.
+# (B, H, grid, block, d, phi)
+MANY_SLICE_CASES = [
+    (5, 8, (1, 1, 1152), (1, 1, 4), 32, PHI_RELU),   # M = 288: 80 tiles per XCD
+    (12, 8, (1, 1, 1280), (1, 1, 4), 32, PHI_ELU1),  # M = 320: 192 tiles per XCD
+    (25, 8, (1, 1, 1024), (1, 1, 4), 32, PHI_ELU1),  # M = 256: 200 tiles per XCD
+    (9, 8, (1, 1, 1664), (1, 1, 4), 32, PHI_RELU),   # M = 416: 144 tiles per XCD
+]
+
+
+@pytest.mark.parametrize("B,H,grid,block,d,phi", MANY_SLICE_CASES)
+def test_blocked_many_slices(B, H, grid, block, d, phi):
+    wl = custom_workload(B, H, d, grid, block, phi, DTYPE_BF16, index=hash((B, grid, d)) % 997)
+    inp = make_inputs(wl)
+    y = to_f64(run(inp, m.MHLA_PATH_BLOCKED))
+    assert np.all(np.isfinite(y))
+    err = slice_error(y, _oracle_full(inp))
+    print("PARITY blocked B=%d H=%d %s d=%d M=%d err=%.3e" % (B, H, grid, d, wl.M, err))
+    assert err <= TOL[DTYPE_BF16]
+
+
 PAIRS_CASES = [
     # (grid, block, d, phi): blocks of at most 16 tokens, the token-pair order
     ((1, 16, 16), (1, 4, 4), 72, PHI_ELU1),    # DiT-like, d = 72 (16-wide tail step)

@@ -785,15 +785,44 @@ __global__ __launch_bounds__(256, 2) void k_mix_big(const bf16_t* __restrict__ S
     for (int c = 0; c < 8; ++c) acc[a][c] = zero4();
 
   mix_big_loop<EP>(ring0, ring1, ring2, Ss, Wt, nk, e0, wave, lane, acc);
-  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
+  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]:
+  // consecutive lanes hold different rows.  The stores go through LDS, 16
+  // rows at a time in a wave-private 16 x 72 area of the (now idle) ring:
+  // v_permlane16_swap pairs lane groups g, g ^ 1 so that each lane holds 8
+  // consecutive entries of its row (at column b(g) = 0, 16, 8, 24 for
+  // g = 0..3, and + 32 from the second tile pair), the lane writes them, and
+  // reads back 8 entries of row L / 8 (and L / 8 + 8) at column 8 (L % 8).
+  // Each store instruction then writes eight whole 128-byte rows (this
+  // wave's 64 entries of a row: one aligned line, as EP is a multiple of 64)
+  // with consecutive lanes on consecutive bytes; storing straight from the
+  // accumulators (each lane 16 bytes of a different row) took 5 us longer
+  // on the video shape.
+  __syncthreads();  // every wave is done reading the ring
+  constexpr int RS = 72;  // staging row stride (elements)
+  static_assert(4 * 16 * RS <= STAGE, "staging fits a stage");
+  bf16_t* sw = ring0 + wave * 16 * RS;
+  const int bcol = (grp & 1) ? 12 + 4 * grp : 4 * grp;
+  const int rr = lane >> 3, ch = lane & 7;
+  bf16_t* ob = St + ((size_t)slice * M + i0 + 128 * wi + rr) * EP + e0 + EW * we + 8 * ch;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const int i = i0 + 128 * wi + 16 * c + s;
-    f32x4_t t[AT];
 #pragma unroll
-    for (int a = 0; a < AT; ++a) t[a] = acc[a][c];
-    store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 + EW * we : nullptr, EW, t,
-                        1.0f, grp);
+    for (int j = 0; j < 2; ++j) {
+      const f32x4_t& x = acc[2 * j][c];
+      const f32x4_t& y = acc[2 * j + 1][c];
+      const auto p0 =
+          __builtin_amdgcn_permlane16_swap(pack2(x[0], x[1]), pack2(y[0], y[1]), false, false);
+      const auto p1 =
+          __builtin_amdgcn_permlane16_swap(pack2(x[2], x[3]), pack2(y[2], y[3]), false, false);
+      *reinterpret_cast<u32x4_t*>(sw + s * RS + bcol + 32 * j) = u32x4_t{p0[0], p1[0], p0[1], p1[1]};
+    }
+    __builtin_amdgcn_wave_barrier();  // LDS operations of one wave run in order
+    const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sw + rr * RS + 8 * ch);
+    const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(sw + (rr + 8) * RS + 8 * ch);
+    __builtin_amdgcn_wave_barrier();
+    const int ib = i0 + 128 * wi + 16 * c + rr;
+    if (ib < M) *reinterpret_cast<u32x4_t*>(ob + (size_t)(16 * c) * EP) = v0;
+    if (ib + 8 < M) *reinterpret_cast<u32x4_t*>(ob + (size_t)(16 * c + 8) * EP) = v1;
   }
 }
 
