@@ -66,6 +66,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
   if (i >= g.M) return;  // no barrier in this kernel
   const size_t off = (size_t)slice * N * d;
   const TT* row = St + ((size_t)slice * g.M + i) * EP;
+  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
+  // per-wave LDS staging area (consecutive lanes on consecutive bytes)
+  constexpr bool STAGED = DP == 64 || DP == 32;
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[STAGED ? kBlkWaves * 16 * (DP + 8) : 1];
+  bf16_t* stage = stage_all + (STAGED ? wave * 16 * (DP + 8) : 0);
+  const bool whole_rows = STAGED && d == DP;
   // eight consecutive entries of the row as one bf16 operand
   auto ld8 = [&](const TT* p) -> u16x8_t {
     if constexpr (sizeof(TT) == 4) {
@@ -128,7 +134,13 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
       f32x4_t gt[NT];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) gt[ct] = f32x4_t{gv[ct][0], gv[ct][1], gv[ct][2], gv[ct][3]};
-      store_row_tiles<NT>(tq >= 0 ? dN + off + (size_t)tq * d : nullptr, d, gt, scale, grp);
+      bf16_t* nrow = tq >= 0 ? dN + off + (size_t)tq * d : nullptr;
+      if constexpr (STAGED) {
+        if (whole_rows) store_rows_staged<NT, false>(nrow, stage, gt, scale, lane);
+        else store_row_tiles<NT>(nrow, d, gt, scale, grp);
+      } else {
+        store_row_tiles<NT>(nrow, d, gt, scale, grp);
+      }
     }
     if (tq >= 0) {
       if (grp == 0) {
@@ -162,10 +174,16 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
   constexpr int NP = SPLIT ? 2 : 1;
   __shared__ __attribute__((aligned(16))) bf16_t sT[NP][DP * RS];  // rows c, entries f
   __shared__ __attribute__((aligned(16))) float sz[DP];             // the z row
+  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
+  // per-wave LDS staging area (consecutive lanes on consecutive bytes)
+  constexpr bool STAGED = DP == 64 || DP == 32;
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[STAGED ? kBlkWaves * 16 * (DP + 8) : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = lane & 15, grp = lane >> 4;
+  bf16_t* stage = stage_all + (STAGED ? wave * 16 * (DP + 8) : 0);
+  const bool whole_rows = STAGED && d == DP;
   const long slice = blockIdx.y;
   const int blk = blockIdx.x;
   const size_t off = (size_t)slice * N * d;
@@ -229,6 +247,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
 #pragma unroll
     for (int kc = 0; kc < DS; ++kc) bm[kc] = (tq >= 0 && 32 * kc + 8 * grp < d) ? bu[kc] : zero8;
     const float usm = tq >= 0 ? us : 1.0f, uem = tq >= 0 ? ue : 0.0f;
+    f32x4_t o[NT];
 #pragma unroll
     for (int ft = 0; ft < NT; ++ft) {
       f32x4_t acc = zero4();
@@ -238,18 +257,19 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
         for (int kc = 0; kc < DS; ++kc)
           acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), bm[kc], acc);
       // acc lane (s, grp) element r = sum_c T[f][c] u[token t0 + s][c], f = 16ft + 4grp + r
-      const int f = 16 * ft + 4 * grp;
-      if (tq >= 0 && f < d) {
-        const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y),
-                            hi_f32(xv[ft].y)};
-        float o[4];
+      const int f = min(16 * ft + 4 * grp, DP - 4);
+      const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y), hi_f32(xv[ft].y)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          o[r] = (acc[r] * usm + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
-        *reinterpret_cast<uint2*>(dX + off + (size_t)tq * d + f) =
-            make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+      for (int r = 0; r < 4; ++r) o[ft][r] = (acc[r] * usm + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
+    }
+    bf16_t* xrow = tq >= 0 ? dX + off + (size_t)tq * d : nullptr;
+    if constexpr (STAGED) {
+      if (whole_rows) {
+        store_rows_staged<NT, false>(xrow, stage, o, 1.0f, lane);
+        continue;
       }
     }
+    store_row_tiles<NT>(xrow, d, o, 1.0f, grp);
   }
 }
 

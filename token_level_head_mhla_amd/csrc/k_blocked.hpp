@@ -978,15 +978,33 @@ __global__ __launch_bounds__(256, 2) void k_mix_big_f32(const bf16_t* __restrict
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = zero4();
   mix_big_f32_loop<EP>(ring0, ring1, ring2, Ss, Wh, Wh + lo_off, M / KB, e0, wave, lane, acc);
-  // acc[a][c] lane (s, grp) element r = S~[i0 + 64wi + 16c + s][e0 + 64we + 16a + 4grp + r]
+  // acc[a][c] lane (s, grp) element r = S~[i0 + 64wi + 16c + s][e0 + 64we + 16a + 4grp + r]:
+  // consecutive lanes hold different rows.  As in k_mix_big, the stores go
+  // through LDS, 16 rows at a time in a wave-private 16 x 68 fp32 area of the
+  // (now idle) ring, and are read back as 16 bytes of row 4h + L / 16 at
+  // column 4 (L % 16): each store instruction writes four whole 256-byte rows
+  // (this wave's 64 entries) with consecutive lanes on consecutive bytes.
+  __syncthreads();  // every wave is done reading the ring
+  constexpr int RS = 68;  // staging row stride (floats)
+  static_assert(4 * 16 * RS * 4 <= STAGE * 2, "staging fits a stage");
+  float* sw = reinterpret_cast<float*>(ring0) + wave * 16 * RS;
+  const int rq = lane >> 4, cq = 4 * (lane & 15);
+  float* ob = St + ((size_t)slice * M + i0 + 64 * wi + rq) * EP + e0 + 64 * we + cq;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int i = i0 + 64 * wi + 16 * c + s;
-    if (i < M) {
-      float* row = St + ((size_t)slice * M + i) * EP + e0 + 64 * we + 4 * grp;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) *reinterpret_cast<f32x4_t*>(row + 16 * a) = acc[a][c];
-    }
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<f32x4_t*>(sw + s * RS + 16 * a + 4 * grp) = acc[a][c];
+    __builtin_amdgcn_wave_barrier();  // LDS operations of one wave run in order
+    f32x4_t v[4];
+#pragma unroll
+    for (int hq = 0; hq < 4; ++hq)
+      v[hq] = *reinterpret_cast<const f32x4_t*>(sw + (4 * hq + rq) * RS + cq);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int hq = 0; hq < 4; ++hq)
+      if (i0 + 64 * wi + 16 * c + 4 * hq + rq < M)
+        *reinterpret_cast<f32x4_t*>(ob + (size_t)(16 * c + 4 * hq) * EP) = v[hq];
   }
 }
 
