@@ -21,10 +21,12 @@
 //   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
 //   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
 //   4. dS, dz         mixing GEMM with W transposed
-//   5. dW             k_dw_partial16 (M <= 16) or k_dw_partial (per slice,
-//                     the rows of dS~ against the rows of S over all d*d + d
-//                     entries, in up to 8 parts) and k_dw_reduce (sum over
-//                     the parts and the batch, fixed order: deterministic)
+//   5. dW             k_dw_partial16 (M <= 16), k_dw_partial (16 < M < 256)
+//                     or k_dw_big (M >= 256): per slice, the rows of dS~
+//                     against the rows of S over all d*d + d entries (for
+//                     16 < M < 256 in up to 8 parts), and k_dw_reduce (sum
+//                     over the parts and the batch, fixed order:
+//                     deterministic)
 //   6. dQ             k_bwd_dphi: S~ staged in LDS and read transposed,
 //                     times G (exact bf16) on MFMA, scaled by 1/den per token
 //                     in fp32, plus z~ dden in fp32, times phi'(Q)
@@ -326,15 +328,16 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial16(const bf16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Step 5, M > 16.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
+// Step 5, 16 < M < 256.  P[slice][i][b] = sum_{e < DP*DP + DP} A[slice][i][e] B[slice][b][e]
 // over the workspace rows (A = dS~, B = S).  grid = (ceil(M/T)^2 * nsplit,
-// slices), block = 256: a T x T output tile per workgroup (T = 128 for
-// M >= 256, else 64), a (T/2) x (T/2) quarter per wave.  Both operands are
+// slices), block = 256: a T x T output tile per workgroup (T = 64; the
+// kernel also takes T = 128), a (T/2) x (T/2) quarter per wave.  Both operands are
 // contiguous in e, so the MFMA fragments are 16-byte row reads of an LDS tile
 // (no transpose); 32-entry steps pass through a double-buffered tile, loaded
 // one step ahead.  Each operand row is read once per T output columns (the
 // 16 x 16-tile kernel above reads it once per 16: 6.5 GB through L2 and
-// 712 us on the video shape, against 122 us here).  For 16 < M < 256 the
+// 712 us on the video shape, against 122 us here with T = 128, which
+// k_dw_big has since replaced for M >= 256).  For 16 < M < 256 the
 // contraction is split into nsplit parts (dw_split) that write separate
 // partial sums, so that the few 64 x 64 tiles still give enough workgroups
 // (4096-token image backward: 0.242 against 0.249 ms with the 16 x 16
@@ -429,6 +432,143 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
     }
 }
 
+// Step 5, M >= 256: the same P[slice][i][b] = sum_e A[slice][i][e] B[slice][b][e]
+// as k_dw_partial, on large-M mixing's pattern.  A workgroup (4 waves) computes
+// a 256 (i) x 128 (b) tile, a wave 128 x 64 (32 accumulator tiles, 32 MFMAs per
+// step).  Entries advance 32 per step through a ring of three 24 KB LDS stages
+// filled by global-to-LDS loads (global_load_lds_dwordx4) two steps ahead,
+// one barrier per step: no register staging and no LDS store instructions.
+// Both operands are rows of 64 bytes per step (32 entries), kept unpadded
+// with 16-byte chunk f of row r at slot f ^ ((r / 2) % 4), so that the
+// fragment reads (16 rows, one chunk each) spread over all banks; the lane
+// that loads a slot fetches the chunk that belongs there.  Rows past M are
+// clamped in bounds and never stored.  grid = 8 ceil(slices / 8) *
+// ceil(M / 256) * ceil(M / 128) (the workgroups of one slice share an XCD and
+// its L2), block = 256.  Same-box harness on the video backward's shape
+// (24 slices, M = 512): 77.4-79.1 us against 110-114 us for k_dw_partial with
+// 128 x 128 tiles, bit-identical output.
+template <int EP>
+__device__ __forceinline__ void dw_big_loop(bf16_t* __restrict__ ring0, bf16_t* __restrict__ ring1,
+                                            bf16_t* __restrict__ ring2,
+                                            const bf16_t* __restrict__ Ab,
+                                            const bf16_t* __restrict__ Bb, int M, int i0, int b0,
+                                            int nk, int wave, int lane, f32x4_t (&acc)[8][4]) {
+  constexpr int TI = 256, TB = 128, KB = 32;
+  const int s = lane & 15, grp = lane >> 4;
+  const int wi = wave >> 1, wb = wave & 1;
+  // Wave w loads A rows 64w .. 64w+63 (four loads of 16 rows) and B rows
+  // 32w .. 32w+31 (two loads): lane L's 16 bytes land at slot L of the 1 KB,
+  // row L / 4, slot L % 4, holding chunk (L % 4) ^ ((row / 2) % 4).
+  const bf16_t* ap[4];
+  const bf16_t* bp[2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 64 * wave + 16 * u + (lane >> 2);
+    ap[u] = Ab + (size_t)(i0 + r < M ? i0 + r : M - 1) * EP + 8 * ((lane & 3) ^ ((r >> 1) & 3));
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 32 * wave + 16 * u + (lane >> 2);
+    bp[u] = Bb + (size_t)(b0 + r < M ? b0 + r : M - 1) * EP + 8 * ((lane & 3) ^ ((r >> 1) & 3));
+  }
+  auto issue = [&](bf16_t* st, int k) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(ap[u] + 32 * k),
+          (__attribute__((address_space(3))) void*)(st + (64 * wave + 16 * u) * KB), 16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(bp[u] + 32 * k),
+          (__attribute__((address_space(3))) void*)(st + (TI + 32 * wave + 16 * u) * KB), 16, 0, 0);
+  };
+  // A fragment t: row 128wi + 16t + s, entries 8grp .. +7; B fragment u: row
+  // TI + 64wb + 16u + s, the same entries
+  auto compute = [&](const bf16_t* st) {
+    const int sw = 8 * (grp ^ ((s >> 1) & 3));
+    u16x8_t bf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      bf[u] = *reinterpret_cast<const u16x8_t*>(st + (TI + 64 * wb + 16 * u + s) * KB + sw);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u16x8_t af = *reinterpret_cast<const u16x8_t*>(st + (128 * wi + 16 * t + s) * KB + sw);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][u] = mfma_bf16(af, bf[u], acc[t][u]);
+    }
+  };
+  // as in mix_big_loop: wait for this thread's six loads of step k (the six
+  // of step k + 1 may stay in flight), barrier, refill the stage read in
+  // step k - 1 with step k + 2 (past the end: the last step again, into a
+  // stage no one reads), multiply
+  auto step = [&](bf16_t* cur, bf16_t* next2, int k) {
+    __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(next2, k + 2 < nk ? k + 2 : nk - 1);
+    compute(cur);
+  };
+  issue(ring0, 0);
+  issue(ring1, nk > 1 ? 1 : 0);
+  int k = 0;
+  for (; k + 3 <= nk; k += 3) {
+    step(ring0, ring2, k);
+    step(ring1, ring0, k + 1);
+    step(ring2, ring1, k + 2);
+  }
+  if (k < nk) step(ring0, ring2, k);
+  if (k + 1 < nk) step(ring1, ring0, k + 1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no load is left in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int DP>
+__global__ __launch_bounds__(256, 2) void k_dw_big(const bf16_t* __restrict__ A,
+                                                  const bf16_t* __restrict__ Bm,
+                                                  float* __restrict__ P, int M, long nslices) {
+  using D = BlockedDims<DP>;
+  constexpr int EP = D::EP, E = DP * DP + DP, NSTEP = E / 32, TI = 256, TB = 128;
+  static_assert(E % 32 == 0, "contraction steps");
+  constexpr int STAGE = (TI + TB) * 32;  // elements (24 KB)
+  __shared__ __attribute__((aligned(16))) bf16_t ring0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t ring2[STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  const int wi = wave >> 1, wb = wave & 1;
+  const int nti = (M + TI - 1) / TI, ntb = (M + TB - 1) / TB, per = nti * ntb;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const long slice = (long)(j / per) * 8 + xcd;
+  if (slice >= nslices) return;  // before any barrier
+  const int rem = j - (j / per) * per;
+  const int i0 = TI * (rem / ntb), b0 = TB * (rem % ntb);
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
+  dw_big_loop<EP>(ring0, ring1, ring2, A + (size_t)slice * M * EP, Bm + (size_t)slice * M * EP, M,
+                  i0, b0, NSTEP, wave, lane, acc);
+  // acc[t][u] lane (s, grp) element r = P[i0 + 128wi + 16t + 4grp + r][b0 + 64wb + 16u + s]
+  float* Ps = P + (size_t)slice * M * M;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bc = b0 + 64 * wb + 16 * u + s;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 128 * wi + 16 * t + 4 * grp + r;
+        if (i < M && bc < M) Ps[(size_t)i * M + bc] = acc[t][u][r];
+      }
+    }
+}
+
 // dW[h][i][b] = sum over the parts of the contraction and over the batch of
 // P[part][batch * H + h][i][b], in a fixed order (parts outer, batch inner).
 __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
@@ -467,11 +607,13 @@ inline int dw_split(long slices, int M) {
 inline bool backward_supports(int dtype, int d, int M, long slices) {
   if (!blocked_supports(dtype, d, M, slices)) return false;
   // the precise mixing GEMM runs 64 query blocks per workgroup on a 1-D grid,
-  // and the dW tile grid along x is ceil(M/16)^2 (M <= 16), ceil(M/64)^2 times
-  // the contraction parts (16 < M < 256) or ceil(M/128)^2 (M >= 256), all at
-  // most ceil(M/16)^2
+  // and the dW tile grid along x is ceil(M/16)^2 (M <= 16) or ceil(M/64)^2
+  // times the contraction parts (16 < M < 256), both at most ceil(M/16)^2; for
+  // M >= 256 the dW grid is 1-D (k_dw_big)
   const long n = (slices + 7) / 8 * 8 * (long)(blocked_ws_elems(d) / kMixEB) * ((M + 63) / 64);
-  return n * kBlkThreads < (1L << 31) && (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
+  const long ndw = (slices + 7) / 8 * 8 * (long)((M + 255) / 256) * ((M + 127) / 128);
+  return n * kBlkThreads < (1L << 31) && ndw < (1L << 31) &&
+         (long)((M + 15) / 16) * ((M + 15) / 16) < (1L << 31);
 }
 
 // Workspace: S, dS~, dS ([slices][M][EP] bf16 each), the precise S~
@@ -536,9 +678,8 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   const bool direct = B == 1 && nsp == 1;
   float* Pd = direct ? dW : P;
   if (M >= 256) {
-    const unsigned nt = (unsigned)((M + 127) / 128);
-    k_dw_partial<DP, 128><<<dim3(nt * nt, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M, 1,
-                                                                      pstride);
+    const unsigned nb = (unsigned)((slices + 7) / 8 * 8 * ((M + 255) / 256) * ((M + 127) / 128));
+    k_dw_big<DP><<<dim3(nb), 256, 0, st>>>(dSt, S, Pd, M, slices);
   } else if (M > 16) {
     const unsigned nt = (unsigned)((M + 63) / 64);
     k_dw_partial<DP, 64><<<dim3(nt * nt * nsp, nsl), kBlkThreads, 0, st>>>(dSt, S, Pd, M, nsp,
