@@ -570,7 +570,11 @@ __global__ __launch_bounds__(256, 2) void k_dw_big(const bf16_t* __restrict__ A,
 }
 
 // dW[h][i][b] = sum over the parts of the contraction and over the batch of
-// P[part][batch * H + h][i][b], in a fixed order (parts outer, batch inner).
+// P[part][batch * H + h][i][b], in a fixed order: term q (part q / B, batch
+// item q % B) goes to partial sum q % 8, and the eight partial sums meet in a
+// fixed tree.  The terms are fetched eight at a time, with no branch among
+// the eight loads (indices past the last term are clamped and masked), so
+// that eight loads are in flight per thread.
 __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
                                                    float* __restrict__ dW, int B, int H, int M,
                                                    int nsplit, size_t pstride) {
@@ -578,17 +582,27 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ P,
   const long MM = (long)M * M;
   if (e >= (long)H * MM) return;
   const long h = e / MM, ib = e - h * MM;
-  // eight partial sums in a fixed order (batch items b, b+8, ...), so that
-  // eight loads are in flight at a time
+  const int n = nsplit * B;
+  // term q0's address, advanced by one batch item (db) or, after the last
+  // batch item, to the first of the next part (dsp)
+  const float* first = P + h * MM + ib;
+  const float* ptr = first;
+  const long db = (long)H * MM, dsp = (long)pstride - (long)(B - 1) * db;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* Ps = P + (size_t)sp * pstride;
-    int b = 0;
-    for (; b + 8 <= B; b += 8) {
+  int b = 0;  // batch item of term q0
+  for (int q0 = 0; q0 < n; q0 += 8) {
+    float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += Ps[((long)(b + u) * H + h) * MM + ib];
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = q0 + u < n;
+      v[u] = *(ok ? ptr : first);
+      v[u] = ok ? v[u] : 0.0f;
+      const bool wrap = b + 1 == B;
+      ptr += wrap ? dsp : db;
+      b = wrap ? 0 : b + 1;
     }
-    for (int u = 0; b + u < B; ++u) acc[u] += Ps[((long)(b + u) * H + h) * MM + ib];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += v[u];
   }
   dW[e] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
