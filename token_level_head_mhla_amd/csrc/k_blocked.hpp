@@ -324,24 +324,47 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_mfma(const bf16_t* __restri
   }
 #undef MHLA_MIX_GLOAD
 #undef MHLA_MIX_LSTORE
-  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]
+  // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 16a + 4grp + r]:
+  // consecutive lanes hold different rows.  The stores go through the S
+  // tiles' LDS (idle after the barrier below), 16 rows at a time in a
+  // wave-private area, so that each store instruction writes whole rows of
+  // the wave's EW entries with consecutive lanes on consecutive bytes.
+  lds_barrier();  // every wave is done reading the tiles
+  if constexpr (PREC) {
+    constexpr int RSF = EW + 4;    // staging row stride (floats)
+    constexpr int LPR = EW / 4;    // lanes per row, 16 bytes each
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    static_assert(kBlkWaves * 16 * RSF * 4 <= 2 * KB * SRS * 2, "staging fits the S tiles");
+    float* sw = reinterpret_cast<float*>(&sS[0][0]) + wave * 16 * RSF;
+    const int rr = lane / LPR, cq = 4 * (lane % LPR);
+    OutT* ob = St + ((size_t)slice * M + i0 + IW * wi + rr) * EP + e0 + EW * we + cq;
 #pragma unroll
-  for (int c = 0; c < BT; ++c) {
-    const int i = i0 + IW * wi + 16 * c + s;
-    if (i < M) {
-      OutT* row = St + ((size_t)slice * M + i) * EP + e0 + EW * we;
-      if constexpr (PREC) {
+    for (int c = 0; c < BT; ++c) {
 #pragma unroll
-        for (int a = 0; a < AT; ++a) *reinterpret_cast<f32x4_t*>(row + 16 * a + 4 * grp) = acc[a][c];
-      }
+      for (int a = 0; a < AT; ++a)
+        *reinterpret_cast<f32x4_t*>(sw + s * RSF + 16 * a + 4 * grp) = acc[a][c];
+      __builtin_amdgcn_wave_barrier();  // LDS operations of one wave run in order
+      f32x4_t v[16 / RPI];
+#pragma unroll
+      for (int hq = 0; hq < 16 / RPI; ++hq)
+        v[hq] = *reinterpret_cast<const f32x4_t*>(sw + (RPI * hq + rr) * RSF + cq);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int hq = 0; hq < 16 / RPI; ++hq)
+        if (i0 + IW * wi + 16 * c + RPI * hq + rr < M)
+          *reinterpret_cast<f32x4_t*>(ob + (size_t)(16 * c + RPI * hq) * EP) = v[hq];
     }
-    if constexpr (!PREC) {
-      // every lane joins the exchange of the 16-byte stores
+  } else {
+    static_assert(kBlkWaves * 16 * (16 * AT + 8) <= 2 * KB * SRS, "staging fits the S tiles");
+    bf16_t* stage = &sS[0][0] + wave * 16 * (16 * AT + 8);
+#pragma unroll
+    for (int c = 0; c < BT; ++c) {
+      const int i = i0 + IW * wi + 16 * c + s;
       f32x4_t t[AT];
 #pragma unroll
       for (int a = 0; a < AT; ++a) t[a] = acc[a][c];
-      store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 + EW * we : nullptr, EW, t,
-                          1.0f, grp);
+      store_rows_staged<AT, false>(i < M ? St + ((size_t)slice * M + i) * EP + e0 + EW * we : nullptr,
+                                   stage, t, 1.0f, lane);
     }
   }
 }
