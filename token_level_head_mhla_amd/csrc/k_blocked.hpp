@@ -534,9 +534,11 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
   constexpr int NG = (nE + kStreamTiles - 1) / kStreamTiles;  // tile groups per slice
   __shared__ __attribute__((aligned(16))) bf16_t sS[2][MP * SRS];
   __shared__ __attribute__((aligned(16))) bf16_t sW[MP * WRS];
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[kBlkWaves * 16 * (16 * AT + 8)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  bf16_t* stage = stage_all + wave * 16 * (16 * AT + 8);
   const int s = lane & 15, grp = lane >> 4;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const long slice = (long)(j / NG) * 8 + xcd;
@@ -615,7 +617,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
 #pragma unroll
         for (int c = 0; c < BT; ++c) acc[a][c] = mfma_bf16(af[a], bw[c], acc[a][c]);
     }
-    // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 32 wave + 16a + 4grp + r]
+    // acc[a][c] lane (s, grp) element r = S~[i = 16c + s][e = 32 wave + 16a + 4grp + r];
+    // stored through the wave's LDS staging area, so that each store
+    // instruction writes whole 64-byte row pieces with consecutive lanes on
+    // consecutive bytes
     const int e0 = (t0 + t) * TE + 32 * wave;
 #pragma unroll
     for (int c = 0; c < BT; ++c) {
@@ -623,8 +628,8 @@ __global__ __launch_bounds__(kBlkThreads) void k_mix_stream(const bf16_t* __rest
       f32x4_t tt[AT];
 #pragma unroll
       for (int a = 0; a < AT; ++a) tt[a] = acc[a][c];
-      store_row_tiles<AT>(i < M ? St + ((size_t)slice * M + i) * EP + e0 : nullptr, 32, tt, 1.0f,
-                          grp);
+      store_rows_staged<AT, false>(i < M ? St + ((size_t)slice * M + i) * EP + e0 : nullptr,
+                                   stage, tt, 1.0f, lane);
     }
     lstore(buf ^ 1);
     lds_barrier();
