@@ -16,9 +16,12 @@
 // Treating z as one more value column ([S | z], [V | 1], [dn | dden]) makes
 // every step one of the forward's building blocks:
 //   1. S, S~          summary kernel, then the mixing GEMM in its precise
-//                     form (W as two bf16 parts, S~ in fp32); the same S~
-//                     serves steps 2 and 6
-//   2. dn, dden       k_bwd_dn: the readout recomputed, then the two formulas
+//                     form (W as two bf16 parts, S~ in fp32)
+//   2. dn, dden, dQ   k_bwd_q, one pass over the query blocks: the readout
+//                     recomputed, the two formulas, then dphi(Q) from S~
+//                     staged in LDS (hi + lo bf16, read transposed) times G
+//                     (exact bf16) on MFMA, scaled by 1/den per token in
+//                     fp32, plus z~ dden in fp32, times phi'(Q)
 //   3. dS~, dz~       summary kernel with (phi(Q), dN) and dden as z weights
 //   4. dS, dz         mixing GEMM with W transposed
 //   5. dW             k_dw_partial16 (M <= 16), k_dw_partial (16 < M < 256)
@@ -27,11 +30,9 @@
 //                     16 < M < 256 in up to 8 parts), and k_dw_reduce (sum
 //                     over the parts and the batch, fixed order:
 //                     deterministic)
-//   6. dQ             k_bwd_dphi: S~ staged in LDS and read transposed,
-//                     times G (exact bf16) on MFMA, scaled by 1/den per token
-//                     in fp32, plus z~ dden in fp32, times phi'(Q)
-//   7. dK             k_bwd_dphi with dS and V, plus dz, times phi'(K)
-//   8. dV             the readout kernel with K for Q, dS for S~ and no
+//   6. dK             k_bwd_dphi: dS staged in LDS and read transposed,
+//                     times V on MFMA, plus dz, times phi'(K)
+//   7. dV             the readout kernel with K for Q, dS for S~ and no
 //                     normaliser: dV^T = dS^T phi(K)^T.
 #pragma once
 
@@ -46,136 +47,22 @@ __device__ __forceinline__ float dphi_apply(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Step 2.  grid = (ceil(M / 4), slices), block = 256: wave w handles query
-// block 4*blockIdx.x + w, 16 queries per step, exactly like the readout
-// (Y^T tiles and the z~ row for the denominator), then forms dn and dden.
-// Writes dN [slices, N, d] bf16, and dden and the per-token factor rq (1/den,
-// or 1 with the normaliser off) as [slices, N] fp32.  TT = float reads the
-// precise fp32 S~ (rounded to bf16 operands as it is loaded), so that the
-// backward needs only one mixing of S.
-template <int DP, int PHI, typename TT = bf16_t>
-__global__ __launch_bounds__(kBlkThreads) void k_bwd_dn(
-    const bf16_t* __restrict__ Q, const TT* __restrict__ St, const bf16_t* __restrict__ G,
-    bf16_t* __restrict__ dN, float* __restrict__ dden, float* __restrict__ rq, Geo g, int N,
-    int d) {
-  using D = BlockedDims<DP>;
-  constexpr int NT = D::NT, DS = D::DS, EP = D::EP;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s = lane & 15, grp = lane >> 4;
-  const long slice = blockIdx.y;
-  const int i = blockIdx.x * kBlkWaves + wave;
-  if (i >= g.M) return;  // no barrier in this kernel
-  const size_t off = (size_t)slice * N * d;
-  const TT* row = St + ((size_t)slice * g.M + i) * EP;
-  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
-  // per-wave LDS staging area (consecutive lanes on consecutive bytes)
-  constexpr bool STAGED = DP == 64 || DP == 32;
-  __shared__ __attribute__((aligned(16))) bf16_t stage_all[STAGED ? kBlkWaves * 16 * (DP + 8) : 1];
-  bf16_t* stage = stage_all + (STAGED ? wave * 16 * (DP + 8) : 0);
-  const bool whole_rows = STAGED && d == DP;
-  // eight consecutive entries of the row as one bf16 operand
-  auto ld8 = [&](const TT* p) -> u16x8_t {
-    if constexpr (sizeof(TT) == 4) {
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(p);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(p + 4);
-      return __builtin_bit_cast(u16x8_t, u32x4_t{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]),
-                                                 pack2(x1[0], x1[1]), pack2(x1[2], x1[3])});
-    } else {
-      return *reinterpret_cast<const u16x8_t*>(p);
-    }
-  };
-  u16x8_t af[NT][DS], az[DS];
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks) af[ct][ks] = ld8(row + (16 * ct + s) * DP + 32 * ks + 8 * grp);
-#pragma unroll
-  for (int ks = 0; ks < DS; ++ks)
-    az[ks] = s == 0 ? ld8(row + DP * DP + 32 * ks + 8 * grp) : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  const int bb = g.blockbase(i);
-  for (int q0 = 0; q0 < g.nb; q0 += 16) {
-    const int j = q0 + s;
-    const int tq = j < g.nb ? bb + g.tokoff(j) : -1;
-    u16x8_t bq[DS];
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
-      const int k0 = 32 * ks + 8 * grp;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (tq >= 0 && k0 < d) v = *reinterpret_cast<const u32x4_t*>(Q + off + (size_t)tq * d + k0);
-      bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(v));
-    }
-    f32x4_t o[NT], oz = zero4();
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      o[ct] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < DS; ++ks) o[ct] = mfma_bf16(af[ct][ks], bq[ks], o[ct]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < DS; ++ks) oz = mfma_bf16(az[ks], bq[ks], oz);
-    const float rd = out_scale(g, __shfl(oz[0], s));
-    // G^T in the accumulator layout: lane (s, grp) holds G[q0+s][16ct+4grp .. +3]
-    float gv[NT][4];
-    float dot = 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int c = 16 * ct + 4 * grp;
-      uint2 u = make_uint2(0u, 0u);
-      if (tq >= 0 && c < d) u = *reinterpret_cast<const uint2*>(G + off + (size_t)tq * d + c);
-      gv[ct][0] = lo_f32(u.x); gv[ct][1] = hi_f32(u.x);
-      gv[ct][2] = lo_f32(u.y); gv[ct][3] = hi_f32(u.y);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dot += gv[ct][r] * (o[ct][r] * rd);
-    }
-    // sum over the four lanes of query s (groups 0..3)
-    dot += __shfl_xor(dot, 16);
-    dot += __shfl_xor(dot, 32);
-    const float scale = g.norm ? rd : 1.0f;
-    {
-      f32x4_t gt[NT];
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) gt[ct] = f32x4_t{gv[ct][0], gv[ct][1], gv[ct][2], gv[ct][3]};
-      bf16_t* nrow = tq >= 0 ? dN + off + (size_t)tq * d : nullptr;
-      if constexpr (STAGED) {
-        if (whole_rows) store_rows_staged<NT, false>(nrow, stage, gt, scale, lane);
-        else store_row_tiles<NT>(nrow, d, gt, scale, grp);
-      } else {
-        store_row_tiles<NT>(nrow, d, gt, scale, grp);
-      }
-    }
-    if (tq >= 0) {
-      if (grp == 0) {
-        dden[(size_t)slice * N + tq] = g.norm ? -dot * rd : 0.0f;
-        rq[(size_t)slice * N + tq] = scale;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Steps 6 and 7.  dphi(x_t)[f] = us_t sum_c T_blk[f][c] u_t[c] + t_blk[f] e_t,
-// where
-//   T, t = S~, z~ (query blocks), u = G, us = 1/den, e = dden   for dQ, and
-//   T, t = dS, dz (key blocks),   u = V, us = 1,     e = 1      for dK,
-// then dX = dphi * phi'(X).  grid = (M, slices), block = 256: one workgroup
-// per block.  The block's workspace row (rows c = value column, entries f;
-// row DP = the z vector) is staged in LDS and read transposed as the A
-// operand (A[f][c]); wave w takes the block's 16-token tiles w, w + 4, ...;
-// the B operand u^T is read straight from global memory.  u stays exact
-// bf16; the per-token factor and the z term are applied in fp32.
-template <int DP, int PHI, typename TT>
-__global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
-    const bf16_t* __restrict__ X, const TT* __restrict__ T, const bf16_t* __restrict__ U,
-    const float* __restrict__ uscale, const float* __restrict__ uext, bf16_t* __restrict__ dX,
-    Geo g, int N, int d) {
+// Step 6.  dphi(k_t)[f] = sum_c dS_blk[f][c] v_t[c] + dz_blk[f], then
+// dK = dphi * phi'(K).  grid = (M, slices), block = 256: one workgroup per key
+// block.  The block's dS row (rows c = value column, entries f; row DP = dz)
+// is staged in LDS and read transposed as the A operand (A[f][c]); wave w
+// takes the block's 16-token tiles w, w + 4, ...; the B operand V^T is read
+// straight from global memory, and the dz term is added in fp32.
+template <int DP, int PHI>
+__global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(const bf16_t* __restrict__ X,
+                                                          const bf16_t* __restrict__ T,
+                                                          const bf16_t* __restrict__ U,
+                                                          bf16_t* __restrict__ dX, Geo g, int N,
+                                                          int d) {
   using D = BlockedDims<DP>;
   constexpr int NT = D::NT, DS = D::DS, EP = D::EP, RS = D::RS;
-  // fp32 state (the precise S~ of dQ) enters as two bf16 parts, hi + lo
-  constexpr bool SPLIT = sizeof(TT) == 4;
-  constexpr int NP = SPLIT ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) bf16_t sT[NP][DP * RS];  // rows c, entries f
-  __shared__ __attribute__((aligned(16))) float sz[DP];             // the z row
+  __shared__ __attribute__((aligned(16))) bf16_t sT[DP * RS];  // rows c, entries f
+  __shared__ __attribute__((aligned(16))) float sz[DP];         // the z row
   // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
   // per-wave LDS staging area (consecutive lanes on consecutive bytes)
   constexpr bool STAGED = DP == 64 || DP == 32;
@@ -189,17 +76,16 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
   const long slice = blockIdx.y;
   const int blk = blockIdx.x;
   const size_t off = (size_t)slice * N * d;
-  const TT* row = T + ((size_t)slice * g.M + blk) * EP;
+  const bf16_t* row = T + ((size_t)slice * g.M + blk) * EP;
   constexpr int F8P = DP / 8;
   const int bb = g.blockbase(blk);
   // Loads of one 16-token tile: the u^T operand (lane (s, grp), step kc holds
-  // u[token][32kc + 8grp .. +7]), x at this lane's output features and the
-  // per-token factors.  Rows and features are clamped in bounds, so every
-  // load is issued; pad tokens and features are masked when used.
+  // u[token][32kc + 8grp .. +7]) and x at this lane's output features.  Rows
+  // and features are clamped in bounds, so every load is issued; pad tokens
+  // and features are masked when used.
   int tq;
   u16x8_t bu[DS];
   uint2 xv[NT];
-  float us, ue;
   auto load_tile = [&](int t0) {
     const int j = t0 + s;
     tq = j < g.nb ? bb + g.tokoff(j) : -1;
@@ -212,8 +98,6 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
     for (int ft = 0; ft < NT; ++ft)
       xv[ft] = *reinterpret_cast<const uint2*>(X + off + (size_t)tc * d +
                                                min(16 * ft + 4 * grp, d - 4));
-    us = uscale != nullptr ? uscale[(size_t)slice * N + tc] : 1.0f;
-    ue = uext != nullptr ? uext[(size_t)slice * N + tc] : 1.0f;
   };
   // the wave's first tile is requested before the state is staged, so that
   // both transfers are in flight together
@@ -221,26 +105,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
   if (first < g.nb) load_tile(first);
   for (int it = tid; it < DP * F8P; it += kBlkThreads) {
     const int c = it / F8P, f = it - (it / F8P) * F8P;
-    if constexpr (SPLIT) {
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f + 4);
-      const u32x4_t hi = u32x4_t{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]),
-                                 pack2(x1[2], x1[3])};
-      const u32x4_t lo = u32x4_t{pack2(x0[0] - lo_f32(hi[0]), x0[1] - hi_f32(hi[0])),
-                                 pack2(x0[2] - lo_f32(hi[1]), x0[3] - hi_f32(hi[1])),
-                                 pack2(x1[0] - lo_f32(hi[2]), x1[1] - hi_f32(hi[2])),
-                                 pack2(x1[2] - lo_f32(hi[3]), x1[3] - hi_f32(hi[3]))};
-      *reinterpret_cast<u32x4_t*>(sT[0] + c * RS + 8 * f) = hi;
-      *reinterpret_cast<u32x4_t*>(sT[NP - 1] + c * RS + 8 * f) = lo;
-    } else {
-      *reinterpret_cast<u32x4_t*>(sT[0] + c * RS + 8 * f) =
-          *reinterpret_cast<const u32x4_t*>(row + c * DP + 8 * f);
-    }
+    *reinterpret_cast<u32x4_t*>(sT + c * RS + 8 * f) =
+        *reinterpret_cast<const u32x4_t*>(row + c * DP + 8 * f);
   }
-  for (int f = tid; f < DP; f += kBlkThreads) {
-    if constexpr (SPLIT) sz[f] = row[DP * DP + f];
-    else sz[f] = bf16_to_f32(row[DP * DP + f]);
-  }
+  for (int f = tid; f < DP; f += kBlkThreads) sz[f] = bf16_to_f32(row[DP * DP + f]);
   lds_barrier();
   for (int t0 = first; t0 < g.nb; t0 += 16 * kBlkWaves) {
     if (t0 != first) load_tile(t0);
@@ -248,21 +116,19 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
     u16x8_t bm[DS];
 #pragma unroll
     for (int kc = 0; kc < DS; ++kc) bm[kc] = (tq >= 0 && 32 * kc + 8 * grp < d) ? bu[kc] : zero8;
-    const float usm = tq >= 0 ? us : 1.0f, uem = tq >= 0 ? ue : 0.0f;
+    const float uem = tq >= 0 ? 1.0f : 0.0f;
     f32x4_t o[NT];
 #pragma unroll
     for (int ft = 0; ft < NT; ++ft) {
       f32x4_t acc = zero4();
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int kc = 0; kc < DS; ++kc)
-          acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), bm[kc], acc);
+      for (int kc = 0; kc < DS; ++kc)
+        acc = mfma_bf16(lds_tr8(sT, RS, 32 * kc, 16 * ft, lane), bm[kc], acc);
       // acc lane (s, grp) element r = sum_c T[f][c] u[token t0 + s][c], f = 16ft + 4grp + r
-      const int f = min(16 * ft + 4 * grp, DP - 4);
+      const int f = 16 * ft + 4 * grp;
       const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y), hi_f32(xv[ft].y)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[ft][r] = (acc[r] * usm + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
+      for (int r = 0; r < 4; ++r) o[ft][r] = (acc[r] + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
     }
     bf16_t* xrow = tq >= 0 ? dX + off + (size_t)tq * d : nullptr;
     if constexpr (STAGED) {
@@ -272,6 +138,183 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(
       }
     }
     store_row_tiles<NT>(xrow, d, o, 1.0f, grp);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 2 and 6 in one pass over the query blocks (they read the same S~ rows,
+// Q and G): per 16-token tile of block i,
+//   o^T = S~_i^T phi(Q)^T and den = phi(q).z~_i with S~, z~ rounded to bf16
+//       (the recomputed readout),
+//   dden = -(G . o) / den^2 (0 without the normaliser), dN = G / den (G
+//       without it), stored through LDS as whole rows,
+//   dphi(q)[f] = (1/den) sum_c S~[f][c] G[c] + z~[f] dden, with S~ as two
+//       bf16 parts (hi + lo) and the per-token factors in fp32, times phi'(q),
+//       stored as dQ.
+// So the fp32 S~ rows, Q and G are read once instead of twice, and the
+// per-token factor 1/den never goes through memory.  grid = (M, slices),
+// block = 256: one workgroup per query block, the block's S~ row staged in
+// LDS as hi and lo parts (rows c = value column, entries f); wave w takes the
+// 16-token tiles w, w + 4, ...  Loads are unconditional (token and feature
+// clamped in range) and masked where used.
+template <int DP, int PHI>
+__global__ __launch_bounds__(kBlkThreads) void k_bwd_q(
+    const bf16_t* __restrict__ Q, const float* __restrict__ St, const bf16_t* __restrict__ G,
+    bf16_t* __restrict__ dN, float* __restrict__ dden, bf16_t* __restrict__ dQ, Geo g, int N,
+    int d) {
+  using D = BlockedDims<DP>;
+  constexpr int NT = D::NT, DS = D::DS, EP = D::EP, RS = D::RS;
+  __shared__ __attribute__((aligned(16))) bf16_t sT[2][DP * RS];  // hi, lo: rows c, entries f
+  __shared__ __attribute__((aligned(16))) float sz[DP];            // z~ (fp32)
+  __shared__ __attribute__((aligned(16))) bf16_t szb[DP];          // z~ rounded to bf16
+  // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
+  // per-wave LDS staging area (consecutive lanes on consecutive bytes)
+  constexpr bool STAGED = DP == 64 || DP == 32;
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[STAGED ? kBlkWaves * 16 * (DP + 8) : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = lane & 15, grp = lane >> 4;
+  bf16_t* stage = stage_all + (STAGED ? wave * 16 * (DP + 8) : 0);
+  const bool whole_rows = STAGED && d == DP;
+  const long slice = blockIdx.y;
+  const int blk = blockIdx.x;
+  const size_t off = (size_t)slice * N * d;
+  const float* row = St + ((size_t)slice * g.M + blk) * EP;
+  constexpr int F8P = DP / 8;
+  const int bb = g.blockbase(blk);
+  // Loads of one 16-token tile, all issued before any is used: phi(Q) and G
+  // as B operands (features 32k + 8grp .. +7 of token s), G in the
+  // accumulator layout (features 16ct + 4grp .. +3) and Q at the same
+  // features.  The wave's first tile is requested before the state is
+  // staged, so that both transfers are in flight together.
+  int tq;
+  u32x4_t qv[DS];
+  u16x8_t gb[DS];
+  uint2 gu[NT], xv[NT];
+  auto load_tile = [&](int t0) {
+    const int j = t0 + s;
+    tq = j < g.nb ? bb + g.tokoff(j) : -1;
+    const int tc = bb + g.tokoff(min(j, g.nb - 1));
+    const bf16_t* qr = Q + off + (size_t)tc * d;
+    const bf16_t* gr = G + off + (size_t)tc * d;
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      qv[ks] = *reinterpret_cast<const u32x4_t*>(qr + min(32 * ks + 8 * grp, d - 8));
+      gb[ks] = *reinterpret_cast<const u16x8_t*>(gr + min(32 * ks + 8 * grp, d - 8));
+    }
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      gu[ct] = *reinterpret_cast<const uint2*>(gr + min(16 * ct + 4 * grp, d - 4));
+      xv[ct] = *reinterpret_cast<const uint2*>(qr + min(16 * ct + 4 * grp, d - 4));
+    }
+  };
+  const int first = 16 * wave;
+  if (first < g.nb) load_tile(first);
+  for (int it = tid; it < DP * F8P; it += kBlkThreads) {
+    const int c = it / F8P, f = it - (it / F8P) * F8P;
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f);
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(row + c * DP + 8 * f + 4);
+    const u32x4_t hi = u32x4_t{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]),
+                               pack2(x1[2], x1[3])};
+    const u32x4_t lo = u32x4_t{pack2(x0[0] - lo_f32(hi[0]), x0[1] - hi_f32(hi[0])),
+                               pack2(x0[2] - lo_f32(hi[1]), x0[3] - hi_f32(hi[1])),
+                               pack2(x1[0] - lo_f32(hi[2]), x1[1] - hi_f32(hi[2])),
+                               pack2(x1[2] - lo_f32(hi[3]), x1[3] - hi_f32(hi[3]))};
+    *reinterpret_cast<u32x4_t*>(sT[0] + c * RS + 8 * f) = hi;
+    *reinterpret_cast<u32x4_t*>(sT[1] + c * RS + 8 * f) = lo;
+  }
+  for (int f = 2 * tid; f < DP; f += 2 * kBlkThreads) {
+    const float z0 = row[DP * DP + f], z1 = row[DP * DP + f + 1];
+    sz[f] = z0;
+    sz[f + 1] = z1;
+    *reinterpret_cast<uint32_t*>(szb + f) = pack2(z0, z1);
+  }
+  lds_barrier();
+  const u16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t0 = first; t0 < g.nb; t0 += 16 * kBlkWaves) {
+    if (t0 != first) load_tile(t0);
+    u16x8_t bq[DS];
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const bool ok = tq >= 0 && 32 * ks + 8 * grp < d;
+      bq[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(ok ? qv[ks] : u32x4_t{0u, 0u, 0u, 0u}));
+      gb[ks] = ok ? gb[ks] : zero8;
+    }
+    // the recomputed readout: o^T (rows c = value column, column = token s)
+    f32x4_t o[NT], oz = zero4();
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      o[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks)
+        o[ct] = mfma_bf16(*reinterpret_cast<const u16x8_t*>(sT[0] + (16 * ct + s) * RS + 32 * ks +
+                                                           8 * grp),
+                          bq[ks], o[ct]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const u16x8_t az = s == 0 ? *reinterpret_cast<const u16x8_t*>(szb + 32 * ks + 8 * grp)
+                                : zero8;
+      oz = mfma_bf16(az, bq[ks], oz);
+    }
+    const float rd = out_scale(g, __shfl(oz[0], s));
+    // G^T in the accumulator layout: lane (s, grp) holds G[t0+s][16ct+4grp .. +3]
+    float gv[NT][4];
+    float dot = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const bool ok = tq >= 0 && 16 * ct + 4 * grp < d;
+      const uint2 u = ok ? gu[ct] : make_uint2(0u, 0u);
+      gv[ct][0] = lo_f32(u.x); gv[ct][1] = hi_f32(u.x);
+      gv[ct][2] = lo_f32(u.y); gv[ct][3] = hi_f32(u.y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dot += gv[ct][r] * (o[ct][r] * rd);
+    }
+    // sum over the four lanes of token s (groups 0..3)
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float scale = g.norm ? rd : 1.0f;
+    const float dd = g.norm ? -dot * rd : 0.0f;
+    {
+      f32x4_t gt[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) gt[ct] = f32x4_t{gv[ct][0], gv[ct][1], gv[ct][2], gv[ct][3]};
+      bf16_t* nrow = tq >= 0 ? dN + off + (size_t)tq * d : nullptr;
+      if constexpr (STAGED) {
+        if (whole_rows) store_rows_staged<NT, false>(nrow, stage, gt, scale, lane);
+        else store_row_tiles<NT>(nrow, d, gt, scale, grp);
+      } else {
+        store_row_tiles<NT>(nrow, d, gt, scale, grp);
+      }
+    }
+    if (tq >= 0 && grp == 0) dden[(size_t)slice * N + tq] = dd;
+    // dQ against the precise S~ (hi + lo), the per-token factors in fp32
+    const float usm = tq >= 0 ? scale : 1.0f, uem = tq >= 0 ? dd : 0.0f;
+    f32x4_t oq[NT];
+#pragma unroll
+    for (int ft = 0; ft < NT; ++ft) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int kc = 0; kc < DS; ++kc)
+          acc = mfma_bf16(lds_tr8(sT[p], RS, 32 * kc, 16 * ft, lane), gb[kc], acc);
+      // acc lane (s, grp) element r = sum_c S~[f][c] G[token t0 + s][c], f = 16ft + 4grp + r
+      const int f = 16 * ft + 4 * grp;
+      const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y), hi_f32(xv[ft].y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        oq[ft][r] = (acc[r] * usm + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
+    }
+    bf16_t* xrow = tq >= 0 ? dQ + off + (size_t)tq * d : nullptr;
+    if constexpr (STAGED) {
+      if (whole_rows) {
+        store_rows_staged<NT, false>(xrow, stage, oq, 1.0f, lane);
+        continue;
+      }
+    }
+    store_row_tiles<NT>(xrow, d, oq, 1.0f, grp);
   }
 }
 
@@ -631,15 +674,15 @@ inline bool backward_supports(int dtype, int d, int M, long slices) {
 }
 
 // Workspace: S, dS~, dS ([slices][M][EP] bf16 each), the precise S~
-// ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden and rq ([slices][N]
-// fp32 each), P ([slices][M][M] fp32), the mixing's coefficient scratch (two
-// sets for the precise large-M mixing).
+// ([slices][M][EP] fp32), dN ([slices][N][d] bf16), dden ([slices][N] fp32),
+// P ([slices][M][M] fp32), the mixing's coefficient scratch (two sets for the
+// precise large-M mixing).
 inline size_t backward_workspace(long slices, int H, int M, int N, int d) {
   const size_t rows = (size_t)slices * M * blocked_ws_elems(d) * sizeof(bf16_t);
   const size_t al = 256;
   auto up = [&](size_t x) { return (x + al - 1) / al * al; };
   return 3 * up(rows) + up(2 * rows) + up((size_t)slices * N * d * sizeof(bf16_t)) +
-         2 * up((size_t)slices * N * sizeof(float)) +
+         up((size_t)slices * N * sizeof(float)) +
          up((size_t)dw_split(slices, M) * slices * M * M * sizeof(float)) +
          mix_coef2_bytes(H, M);
 }
@@ -666,8 +709,6 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   p += up((size_t)slices * N * d * sizeof(bf16_t));
   float* dden = reinterpret_cast<float*>(p);
   p += up((size_t)slices * N * sizeof(float));
-  float* rq = reinterpret_cast<float*>(p);
-  p += up((size_t)slices * N * sizeof(float));
   float* P = reinterpret_cast<float*>(p);
   const int nsp = dw_split(slices, M);
   const size_t pstride = (size_t)slices * M * M;
@@ -675,13 +716,13 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
   bf16_t* wc = reinterpret_cast<bf16_t*>(p);
   const unsigned nsl = (unsigned)slices;
   // 1. forward state: S, and the precise S~ (fp32, W in two bf16 parts),
-  //    which serves both the recomputed readout of step 2 and dQ in step 6
+  //    which serves both the recomputed readout and dQ in step 2
   k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(K, V, S, g, N, d,
                                                                            nullptr);
   launch_mix_f32<DP>(slices, H, M, S, W, St32, wc, st);
-  // 2. dn, dden
+  // 2. dn, dden and dQ in one pass over the query blocks
   const unsigned nbw = (unsigned)((M + kBlkWaves - 1) / kBlkWaves);
-  k_bwd_dn<DP, PHI, float><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(Q, St32, dY, dN, dden, rq, g,
+  k_bwd_q<DP, PHI><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(Q, St32, dY, dN, dden, dQ, g,
                                                                    N, d);
   // 3. dS~ = phi(Q)^T dN per query block, dz~ weighted by dden
   k_summary_mfma<DP, PHI><<<dim3((unsigned)M, nsl), 64 * D::NT, 0, st>>>(Q, dN, dSt, g, N, d,
@@ -707,13 +748,9 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
     k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M, nsp,
                                                                     pstride);
   }
-  // 6. dQ, against the precise S~
-  k_bwd_dphi<DP, PHI, float><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
-      Q, St32, dY, rq, dden, dQ, g, N, d);
-  // 7. dK
-  k_bwd_dphi<DP, PHI, bf16_t><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(
-      K, dS, V, nullptr, nullptr, dK, g, N, d);
-  // 8. dV = readout of phi(K) against dS without the normaliser
+  // 6. dK
+  k_bwd_dphi<DP, PHI><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(K, dS, V, dK, g, N, d);
+  // 7. dV = readout of phi(K) against dS without the normaliser
   Geo g0 = g;
   g0.norm = 0;
   k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, dS, dV, g0, N, d);
