@@ -30,10 +30,10 @@
 //                     16 < M < 256 in up to 8 parts), and k_dw_reduce (sum
 //                     over the parts and the batch, fixed order:
 //                     deterministic)
-//   6. dK             k_bwd_dphi: dS staged in LDS and read transposed,
-//                     times V on MFMA, plus dz, times phi'(K)
-//   7. dV             the readout kernel with K for Q, dS for S~ and no
-//                     normaliser: dV^T = dS^T phi(K)^T.
+//   6. dK, dV         k_bwd_kv, one pass over the key blocks: dS staged in
+//                     LDS; dV^T = dS^T phi(K)^T (the readout with K for Q, dS
+//                     for S~ and no normaliser), and dphi(K) from dS read
+//                     transposed times V on MFMA, plus dz, times phi'(K).
 #pragma once
 
 #include "k_blocked.hpp"
@@ -47,22 +47,28 @@ __device__ __forceinline__ float dphi_apply(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Step 6.  dphi(k_t)[f] = sum_c dS_blk[f][c] v_t[c] + dz_blk[f], then
-// dK = dphi * phi'(K).  grid = (M, slices), block = 256: one workgroup per key
-// block.  The block's dS row (rows c = value column, entries f; row DP = dz)
-// is staged in LDS and read transposed as the A operand (A[f][c]); wave w
-// takes the block's 16-token tiles w, w + 4, ...; the B operand V^T is read
-// straight from global memory, and the dz term is added in fp32.
+// Steps 6 and 7 in one pass over the key blocks (they read the same dS rows
+// and K): per 16-token tile of key block b,
+//   dV^T = dS_b^T phi(K)^T (the readout of phi(K) against dS, without the
+//       normaliser), and
+//   dphi(k)[f] = sum_c dS_b[f][c] v[c] + dz_b[f], times phi'(k) -> dK.
+// grid = (M, slices), block = 256: one workgroup per key block.  The block's
+// dS row (rows c = value column, entries f; row DP = dz) is staged in LDS: its
+// rows are the A operand of dV, and read transposed (A[f][c]) that of dK;
+// wave w takes the block's 16-token tiles w, w + 4, ...  phi(K), V and K at
+// the output features come straight from global memory (the wave's first
+// tile requested before the state is staged); the dz term is added in fp32.
 template <int DP, int PHI>
-__global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(const bf16_t* __restrict__ X,
-                                                          const bf16_t* __restrict__ T,
-                                                          const bf16_t* __restrict__ U,
-                                                          bf16_t* __restrict__ dX, Geo g, int N,
-                                                          int d) {
+__global__ __launch_bounds__(kBlkThreads) void k_bwd_kv(const bf16_t* __restrict__ K,
+                                                        const bf16_t* __restrict__ V,
+                                                        const bf16_t* __restrict__ dS,
+                                                        bf16_t* __restrict__ dK,
+                                                        bf16_t* __restrict__ dV, Geo g, int N,
+                                                        int d) {
   using D = BlockedDims<DP>;
   constexpr int NT = D::NT, DS = D::DS, EP = D::EP, RS = D::RS;
   __shared__ __attribute__((aligned(16))) bf16_t sT[DP * RS];  // rows c, entries f
-  __shared__ __attribute__((aligned(16))) float sz[DP];         // the z row
+  __shared__ __attribute__((aligned(16))) float sz[DP];         // dz
   // rows of 128 or 64 bytes (d == DP = 64 or 32) are stored whole, through a
   // per-wave LDS staging area (consecutive lanes on consecutive bytes)
   constexpr bool STAGED = DP == 64 || DP == 32;
@@ -76,31 +82,32 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(const bf16_t* __restri
   const long slice = blockIdx.y;
   const int blk = blockIdx.x;
   const size_t off = (size_t)slice * N * d;
-  const bf16_t* row = T + ((size_t)slice * g.M + blk) * EP;
+  const bf16_t* row = dS + ((size_t)slice * g.M + blk) * EP;
   constexpr int F8P = DP / 8;
   const int bb = g.blockbase(blk);
-  // Loads of one 16-token tile: the u^T operand (lane (s, grp), step kc holds
-  // u[token][32kc + 8grp .. +7]) and x at this lane's output features.  Rows
-  // and features are clamped in bounds, so every load is issued; pad tokens
-  // and features are masked when used.
+  // Loads of one 16-token tile: K and V as B operands (features
+  // 32k + 8grp .. +7 of token s) and K at this lane's output features
+  // (16ft + 4grp .. +3).  Rows and features are clamped in bounds, so every
+  // load is issued; pad tokens and features are masked when used.
   int tq;
-  u16x8_t bu[DS];
+  u32x4_t kb[DS];
+  u16x8_t vb[DS];
   uint2 xv[NT];
   auto load_tile = [&](int t0) {
     const int j = t0 + s;
     tq = j < g.nb ? bb + g.tokoff(j) : -1;
     const int tc = bb + g.tokoff(min(j, g.nb - 1));
+    const bf16_t* kr = K + off + (size_t)tc * d;
+    const bf16_t* vr = V + off + (size_t)tc * d;
 #pragma unroll
-    for (int kc = 0; kc < DS; ++kc)
-      bu[kc] = *reinterpret_cast<const u16x8_t*>(U + off + (size_t)tc * d +
-                                                 min(32 * kc + 8 * grp, d - 8));
+    for (int ks = 0; ks < DS; ++ks) {
+      kb[ks] = *reinterpret_cast<const u32x4_t*>(kr + min(32 * ks + 8 * grp, d - 8));
+      vb[ks] = *reinterpret_cast<const u16x8_t*>(vr + min(32 * ks + 8 * grp, d - 8));
+    }
 #pragma unroll
     for (int ft = 0; ft < NT; ++ft)
-      xv[ft] = *reinterpret_cast<const uint2*>(X + off + (size_t)tc * d +
-                                               min(16 * ft + 4 * grp, d - 4));
+      xv[ft] = *reinterpret_cast<const uint2*>(kr + min(16 * ft + 4 * grp, d - 4));
   };
-  // the wave's first tile is requested before the state is staged, so that
-  // both transfers are in flight together
   const int first = 16 * wave;
   if (first < g.nb) load_tile(first);
   for (int it = tid; it < DP * F8P; it += kBlkThreads) {
@@ -110,34 +117,56 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_dphi(const bf16_t* __restri
   }
   for (int f = tid; f < DP; f += kBlkThreads) sz[f] = bf16_to_f32(row[DP * DP + f]);
   lds_barrier();
+  const u16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int t0 = first; t0 < g.nb; t0 += 16 * kBlkWaves) {
     if (t0 != first) load_tile(t0);
-    const u16x8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    u16x8_t bm[DS];
+    u16x8_t bk[DS], bm[DS];
 #pragma unroll
-    for (int kc = 0; kc < DS; ++kc) bm[kc] = (tq >= 0 && 32 * kc + 8 * grp < d) ? bu[kc] : zero8;
-    const float uem = tq >= 0 ? 1.0f : 0.0f;
+    for (int ks = 0; ks < DS; ++ks) {
+      const bool ok = tq >= 0 && 32 * ks + 8 * grp < d;
+      bk[ks] = __builtin_bit_cast(u16x8_t, phi8<PHI>(ok ? kb[ks] : u32x4_t{0u, 0u, 0u, 0u}));
+      bm[ks] = ok ? vb[ks] : zero8;
+    }
+    // dV^T: rows c = value column, column = token s
     f32x4_t o[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      o[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks)
+        o[ct] = mfma_bf16(*reinterpret_cast<const u16x8_t*>(sT + (16 * ct + s) * RS + 32 * ks +
+                                                           8 * grp),
+                          bk[ks], o[ct]);
+    }
+    bf16_t* vrow = tq >= 0 ? dV + off + (size_t)tq * d : nullptr;
+    if constexpr (STAGED) {
+      if (whole_rows) store_rows_staged<NT, false>(vrow, stage, o, 1.0f, lane);
+      else store_row_tiles<NT>(vrow, d, o, 1.0f, grp);
+    } else {
+      store_row_tiles<NT>(vrow, d, o, 1.0f, grp);
+    }
+    // dK
+    const float uem = tq >= 0 ? 1.0f : 0.0f;
+    f32x4_t dk[NT];
 #pragma unroll
     for (int ft = 0; ft < NT; ++ft) {
       f32x4_t acc = zero4();
 #pragma unroll
       for (int kc = 0; kc < DS; ++kc)
         acc = mfma_bf16(lds_tr8(sT, RS, 32 * kc, 16 * ft, lane), bm[kc], acc);
-      // acc lane (s, grp) element r = sum_c T[f][c] u[token t0 + s][c], f = 16ft + 4grp + r
+      // acc lane (s, grp) element r = sum_c dS[f][c] v[token t0 + s][c], f = 16ft + 4grp + r
       const int f = 16 * ft + 4 * grp;
       const float x[4] = {lo_f32(xv[ft].x), hi_f32(xv[ft].x), lo_f32(xv[ft].y), hi_f32(xv[ft].y)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[ft][r] = (acc[r] + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
+      for (int r = 0; r < 4; ++r) dk[ft][r] = (acc[r] + sz[f + r] * uem) * dphi_apply<PHI>(x[r]);
     }
-    bf16_t* xrow = tq >= 0 ? dX + off + (size_t)tq * d : nullptr;
+    bf16_t* krow = tq >= 0 ? dK + off + (size_t)tq * d : nullptr;
     if constexpr (STAGED) {
-      if (whole_rows) {
-        store_rows_staged<NT, false>(xrow, stage, o, 1.0f, lane);
-        continue;
-      }
+      if (whole_rows) store_rows_staged<NT, false>(krow, stage, dk, 1.0f, lane);
+      else store_row_tiles<NT>(krow, d, dk, 1.0f, grp);
+    } else {
+      store_row_tiles<NT>(krow, d, dk, 1.0f, grp);
     }
-    store_row_tiles<NT>(xrow, d, o, 1.0f, grp);
   }
 }
 
@@ -748,12 +777,8 @@ int launch_backward_t(long slices, int B, int H, int N, int d, const Geo& g, con
     k_dw_reduce<<<dim3((unsigned)((nw + 255) / 256)), 256, 0, st>>>(P, dW, B, H, M, nsp,
                                                                     pstride);
   }
-  // 6. dK
-  k_bwd_dphi<DP, PHI><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(K, dS, V, dK, g, N, d);
-  // 7. dV = readout of phi(K) against dS without the normaliser
-  Geo g0 = g;
-  g0.norm = 0;
-  k_readout_mfma<DP, PHI><<<dim3(nbw, nsl), kBlkThreads, 0, st>>>(K, dS, dV, g0, N, d);
+  // 6. dK and dV in one pass over the key blocks
+  k_bwd_kv<DP, PHI><<<dim3((unsigned)M, nsl), kBlkThreads, 0, st>>>(K, V, dS, dK, dV, g, N, d);
   return 0;
 }
 
