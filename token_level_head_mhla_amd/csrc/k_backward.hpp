@@ -507,75 +507,88 @@ __global__ __launch_bounds__(kBlkThreads) void k_dw_partial(const bf16_t* __rest
 // Step 5, M >= 256: the same P[slice][i][b] = sum_e A[slice][i][e] B[slice][b][e]
 // as k_dw_partial, on large-M mixing's pattern.  A workgroup (4 waves) computes
 // a 256 (i) x 128 (b) tile, a wave 128 x 64 (32 accumulator tiles, 32 MFMAs per
-// step).  Entries advance 32 per step through a ring of three 24 KB LDS stages
-// filled by global-to-LDS loads (global_load_lds_dwordx4) two steps ahead,
-// one barrier per step: no register staging and no LDS store instructions.
-// Both operands are rows of 64 bytes per step (32 entries), kept unpadded
-// with 16-byte chunk f of row r at slot f ^ ((r / 2) % 4), so that the
+// 32 entries).  Entries advance KB per step through a ring of three LDS
+// stages filled by global-to-LDS loads (global_load_lds_dwordx4) two steps
+// ahead, one barrier per step: no register staging and no LDS store
+// instructions.  KB = 64 where the contraction length allows (d = 64): each
+// step then reads whole 128-byte pieces of the operand rows, which lie 8 KB
+// and more apart, so that every visit to a row is one DRAM access; pieces of
+// 64 bytes cost a second access per line when the rows come from HBM.  The
+// stages (48 KB each) then hold one workgroup per CU; with KB = 32 (24 KB
+// stages) two.  Rows are kept unpadded with 16-byte chunk f of row r at slot
+// f ^ ((r / (8 / CPR)) % CPR), CPR = KB / 8 chunks per row, so that the
 // fragment reads (16 rows, one chunk each) spread over all banks; the lane
 // that loads a slot fetches the chunk that belongs there.  Rows past M are
 // clamped in bounds and never stored.  grid = 8 ceil(slices / 8) *
 // ceil(M / 256) * ceil(M / 128) (the workgroups of one slice share an XCD and
-// its L2), block = 256.  Same-box harness on the video backward's shape
-// (24 slices, M = 512): 77.4-79.1 us against 110-114 us for k_dw_partial with
-// 128 x 128 tiles, bit-identical output.
-template <int EP>
-__device__ __forceinline__ void dw_big_loop(bf16_t* __restrict__ ring0, bf16_t* __restrict__ ring1,
-                                            bf16_t* __restrict__ ring2,
+// its L2), block = 256.
+template <int EP, int KB>
+__device__ __forceinline__ void dw_big_loop(bf16_t* __restrict__ ring,
                                             const bf16_t* __restrict__ Ab,
                                             const bf16_t* __restrict__ Bb, int M, int i0, int b0,
                                             int nk, int wave, int lane, f32x4_t (&acc)[8][4]) {
-  constexpr int TI = 256, TB = 128, KB = 32;
+  constexpr int TI = 256, TB = 128, STAGE = (TI + TB) * KB;
+  constexpr int CPR = KB / 8, RPL = 64 / CPR;  // chunks per row, rows per load
+  constexpr int LA = TI / 4 / RPL, LB = TB / 4 / RPL, NL = LA + LB;
+  // wait for this thread's loads of step k; those of step k + 1 may stay in flight
+  constexpr int WAIT = (NL & 15) | 0x70 | ((NL >> 4) << 14);  // vmcnt(NL) lgkmcnt(0)
   const int s = lane & 15, grp = lane >> 4;
   const int wi = wave >> 1, wb = wave & 1;
-  // Wave w loads A rows 64w .. 64w+63 (four loads of 16 rows) and B rows
-  // 32w .. 32w+31 (two loads): lane L's 16 bytes land at slot L of the 1 KB,
-  // row L / 4, slot L % 4, holding chunk (L % 4) ^ ((row / 2) % 4).
-  const bf16_t* ap[4];
-  const bf16_t* bp[2];
+  // Wave w loads A rows 64w .. 64w+63 and B rows 32w .. 32w+31, RPL rows per
+  // load: lane L's 16 bytes land at slot L of the 1 KB, row L / CPR, slot
+  // L % CPR, holding the chunk that belongs there.
+  const bf16_t* ap[LA];
+  const bf16_t* bp[LB];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 64 * wave + 16 * u + (lane >> 2);
-    ap[u] = Ab + (size_t)(i0 + r < M ? i0 + r : M - 1) * EP + 8 * ((lane & 3) ^ ((r >> 1) & 3));
+  for (int u = 0; u < LA; ++u) {
+    const int r = TI / 4 * wave + RPL * u + lane / CPR;
+    ap[u] = Ab + (size_t)(i0 + r < M ? i0 + r : M - 1) * EP +
+            8 * ((lane % CPR) ^ ((r / (8 / CPR)) % CPR));
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 32 * wave + 16 * u + (lane >> 2);
-    bp[u] = Bb + (size_t)(b0 + r < M ? b0 + r : M - 1) * EP + 8 * ((lane & 3) ^ ((r >> 1) & 3));
+  for (int u = 0; u < LB; ++u) {
+    const int r = TB / 4 * wave + RPL * u + lane / CPR;
+    bp[u] = Bb + (size_t)(b0 + r < M ? b0 + r : M - 1) * EP +
+            8 * ((lane % CPR) ^ ((r / (8 / CPR)) % CPR));
   }
   auto issue = [&](bf16_t* st, int k) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < LA; ++u)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(ap[u] + 32 * k),
-          (__attribute__((address_space(3))) void*)(st + (64 * wave + 16 * u) * KB), 16, 0, 0);
+          (const void*)(ap[u] + KB * k),
+          (__attribute__((address_space(3))) void*)(st + (TI / 4 * wave + RPL * u) * KB), 16, 0,
+          0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < LB; ++u)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(bp[u] + 32 * k),
-          (__attribute__((address_space(3))) void*)(st + (TI + 32 * wave + 16 * u) * KB), 16, 0, 0);
+          (const void*)(bp[u] + KB * k),
+          (__attribute__((address_space(3))) void*)(st + (TI + TB / 4 * wave + RPL * u) * KB), 16,
+          0, 0);
   };
-  // A fragment t: row 128wi + 16t + s, entries 8grp .. +7; B fragment u: row
-  // TI + 64wb + 16u + s, the same entries
+  // per 32 entries h: A fragment t: row 128wi + 16t + s, entries 32h + 8grp
+  // .. +7; B fragment u: row TI + 64wb + 16u + s, the same entries
   auto compute = [&](const bf16_t* st) {
-    const int sw = 8 * (grp ^ ((s >> 1) & 3));
-    u16x8_t bf[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      bf[u] = *reinterpret_cast<const u16x8_t*>(st + (TI + 64 * wb + 16 * u + s) * KB + sw);
+    for (int h = 0; h < KB / 32; ++h) {
+      const int sw = 8 * ((4 * h + grp) ^ ((s / (8 / CPR)) % CPR));
+      u16x8_t bf[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u16x8_t af = *reinterpret_cast<const u16x8_t*>(st + (128 * wi + 16 * t + s) * KB + sw);
+      for (int u = 0; u < 4; ++u)
+        bf[u] = *reinterpret_cast<const u16x8_t*>(st + (TI + 64 * wb + 16 * u + s) * KB + sw);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][u] = mfma_bf16(af, bf[u], acc[t][u]);
+      for (int t = 0; t < 8; ++t) {
+        const u16x8_t af =
+            *reinterpret_cast<const u16x8_t*>(st + (128 * wi + 16 * t + s) * KB + sw);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[t][u] = mfma_bf16(af, bf[u], acc[t][u]);
+      }
     }
   };
-  // as in mix_big_loop: wait for this thread's six loads of step k (the six
-  // of step k + 1 may stay in flight), barrier, refill the stage read in
-  // step k - 1 with step k + 2 (past the end: the last step again, into a
-  // stage no one reads), multiply
+  // as in mix_big_loop: wait for step k's loads, barrier, refill the stage
+  // read in step k - 1 with step k + 2 (past the end: the last step again,
+  // into a stage no one reads), multiply
   auto step = [&](bf16_t* cur, bf16_t* next2, int k) {
-    __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(WAIT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -584,6 +597,9 @@ __device__ __forceinline__ void dw_big_loop(bf16_t* __restrict__ ring0, bf16_t* 
     issue(next2, k + 2 < nk ? k + 2 : nk - 1);
     compute(cur);
   };
+  bf16_t* const ring0 = ring;
+  bf16_t* const ring1 = ring + STAGE;
+  bf16_t* const ring2 = ring + 2 * STAGE;
   issue(ring0, 0);
   issue(ring1, nk > 1 ? 1 : 0);
   int k = 0;
@@ -598,17 +614,21 @@ __device__ __forceinline__ void dw_big_loop(bf16_t* __restrict__ ring0, bf16_t* 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// entries per step of k_dw_big: 64 where d^2 + d allows it
 template <int DP>
-__global__ __launch_bounds__(256, 2) void k_dw_big(const bf16_t* __restrict__ A,
-                                                  const bf16_t* __restrict__ Bm,
-                                                  float* __restrict__ P, int M, long nslices) {
+constexpr int dw_big_kb() {
+  return (DP * DP + DP) % 64 == 0 ? 64 : 32;
+}
+
+template <int DP>
+__global__ __launch_bounds__(256, dw_big_kb<DP>() == 64 ? 1 : 2) void k_dw_big(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, float* __restrict__ P, int M,
+    long nslices) {
   using D = BlockedDims<DP>;
-  constexpr int EP = D::EP, E = DP * DP + DP, NSTEP = E / 32, TI = 256, TB = 128;
-  static_assert(E % 32 == 0, "contraction steps");
-  constexpr int STAGE = (TI + TB) * 32;  // elements (24 KB)
-  __shared__ __attribute__((aligned(16))) bf16_t ring0[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t ring1[STAGE];
-  __shared__ __attribute__((aligned(16))) bf16_t ring2[STAGE];
+  constexpr int EP = D::EP, E = DP * DP + DP, KB = dw_big_kb<DP>(), NSTEP = E / KB;
+  constexpr int TI = 256, TB = 128;
+  static_assert(E % KB == 0, "contraction steps");
+  __shared__ __attribute__((aligned(16))) bf16_t ring[3 * (TI + TB) * KB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = lane & 15, grp = lane >> 4;
@@ -624,8 +644,8 @@ __global__ __launch_bounds__(256, 2) void k_dw_big(const bf16_t* __restrict__ A,
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
-  dw_big_loop<EP>(ring0, ring1, ring2, A + (size_t)slice * M * EP, Bm + (size_t)slice * M * EP, M,
-                  i0, b0, NSTEP, wave, lane, acc);
+  dw_big_loop<EP, KB>(ring, A + (size_t)slice * M * EP, Bm + (size_t)slice * M * EP, M, i0, b0,
+                      NSTEP, wave, lane, acc);
   // acc[t][u] lane (s, grp) element r = P[i0 + 128wi + 16t + 4grp + r][b0 + 64wb + 16u + s]
   float* Ps = P + (size_t)slice * M * M;
 #pragma unroll
