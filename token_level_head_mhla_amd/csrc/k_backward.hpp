@@ -58,8 +58,9 @@ __device__ __forceinline__ float dphi_apply(float x) {
 // wave w takes the block's 16-token tiles w, w + 4, ...  phi(K), V and K at
 // the output features come straight from global memory (the wave's first
 // tile requested before the state is staged); the dz term is added in fp32.
+// d = 64: held to 80 VGPRs for six workgroups per CU, as for k_bwd_q.
 template <int DP, int PHI>
-__global__ __launch_bounds__(kBlkThreads) void k_bwd_kv(const bf16_t* __restrict__ K,
+__global__ __launch_bounds__(kBlkThreads, DP == 64 ? 6 : 1) void k_bwd_kv(const bf16_t* __restrict__ K,
                                                         const bf16_t* __restrict__ V,
                                                         const bf16_t* __restrict__ dS,
                                                         bf16_t* __restrict__ dK,
@@ -186,8 +187,11 @@ __global__ __launch_bounds__(kBlkThreads) void k_bwd_kv(const bf16_t* __restrict
 // LDS as hi and lo parts (rows c = value column, entries f); wave w takes the
 // 16-token tiles w, w + 4, ...  Loads are unconditional (token and feature
 // clamped in range) and masked where used.
+// d = 64: the compiler is held to 96 VGPRs (91 used, no spills), so that five
+// workgroups share a CU (LDS allows five): the kernel is bound by its memory
+// streams, and a fifth workgroup keeps more of them in flight.
 template <int DP, int PHI>
-__global__ __launch_bounds__(kBlkThreads) void k_bwd_q(
+__global__ __launch_bounds__(kBlkThreads, DP == 64 ? 5 : 1) void k_bwd_q(
     const bf16_t* __restrict__ Q, const float* __restrict__ St, const bf16_t* __restrict__ G,
     bf16_t* __restrict__ dN, float* __restrict__ dden, bf16_t* __restrict__ dQ, Geo g, int N,
     int d) {
