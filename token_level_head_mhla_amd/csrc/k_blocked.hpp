@@ -46,15 +46,17 @@ inline int blocked_dp(int d) { return (d + 31) / 32 * 32; }
 // and one wave per 16-column tile ct of the value dimension.  The block's
 // tokens are staged in LDS (phi applied to K) 64 at a time; wave ct forms
 // S[:, 16ct .. 16ct+15] from transpose-read operands, and wave 0 also forms
-// z_b (a ones B operand).  Small LDS and register footprints keep ~24 waves
-// per CU, which hides the load latency of this bandwidth-bound kernel.
+// z_b (a ones B operand).  For d = 64 the compiler is held to 80 VGPRs (76
+// used, no spills) so that six workgroups (24 waves) share a CU, next to 20 KB
+// of LDS each: the more blocks are in flight, the better this bandwidth-bound
+// kernel hides its load latency (at 104 VGPRs only four fitted).
 //
 // zw == nullptr gives z_b = sum_j phi(K_j); otherwise z_b = sum_j zw[j] phi(K_j)
 // with zw a per-token fp32 weight ([slices, N]); the backward pass uses this
 // for dz~_i = sum_q dden_q phi(Q_q).  STREAM = true reads K and V with the
 // nontemporal hint (see blocked_stream).
 template <int DP, int PHI, bool STREAM = false>
-__global__ __launch_bounds__(64 * (DP / 16)) void k_summary_mfma(
+__global__ __launch_bounds__(64 * (DP / 16), DP == 64 ? 6 : 1) void k_summary_mfma(
     const bf16_t* __restrict__ K, const bf16_t* __restrict__ V, bf16_t* __restrict__ S, Geo g,
     int N, int d, const float* __restrict__ zw) {
   using D = BlockedDims<DP>;
