@@ -408,9 +408,11 @@ __host__ __device__ inline size_t coef_tiled(int M, int h, int i, int b) {
 // of its 128-entry tiles.  The key blocks go in steps of 32; wave w takes
 // steps w, w + 4, ...; the z_b rows of 128 key blocks (one step per wave) are
 // staged in LDS and read as transposed B operands; the four waves' partial
-// sums meet in LDS.  grid = H8 * MI / 16 (H8 = H rounded up to 8, MI = M
-// rounded up to 256; the workgroups of one head share an XCD), block =
-// 256, M % 32 == 0.
+// sums meet in LDS.  Each chunk's z rows and W pieces are requested while the
+// previous chunk is multiplied (a workgroup used to wait for two round trips
+// per chunk: the z rows, then, after staging them, the W pieces).  grid =
+// H8 * MI / 16 (H8 = H rounded up to 8, MI = M rounded up to 256; the
+// workgroups of one head share an XCD), block = 256, M % 32 == 0.
 template <int DP, int MODE>
 __global__ __launch_bounds__(256) void k_mix_prep(const float* __restrict__ W,
                                                   const bf16_t* __restrict__ S,
@@ -437,76 +439,100 @@ __global__ __launch_bounds__(256) void k_mix_prep(const float* __restrict__ W,
   if (h >= H) return;  // padding of the grid to whole groups of 8 heads (no barrier yet)
   const int i0 = (j - (j / nti) * nti) * 16;
   const int i = i0 + s;                  // this lane's row of the A operand
-  const int nk = M / 32;
+  const int nk = M / 32, nch = (M + CH - 1) / CH;
   const float* Wr = W + ((size_t)h * M + (i < M ? i : 0)) * M;
-  for (long slice = h; slice < nslices; slice += H) {
-    const bool first = slice == h;       // the coefficient tiles are written once
-    f32x4_t acc[NT];
+  // The work is a sequence of (slice, chunk) pairs: slices h, h + H, ...,
+  // chunks of CH key blocks.  The z rows and W pieces of the next pair are
+  // requested as soon as the current pair is staged, so that they arrive
+  // while it is multiplied.
+  u32x4_t zr[ZCH];
+  f32x4_t w0, w1;
+  auto fetch = [&](long sl, int c0) {
+    const bf16_t* Zs = S + (size_t)sl * M * EP + DP * DP;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = zero4();
-    const bf16_t* Zs = S + (size_t)slice * M * EP + DP * DP;
-    for (int c0 = 0; c0 < M; c0 += CH) {
-      // stage z rows c0 .. c0+CH-1 (zero past M)
-      u32x4_t zr[ZCH];
+    for (int u = 0; u < ZCH; ++u) {
+      const int pc = tid + 256 * u;
+      const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
+      zr[u] = c0 + r < M ? *reinterpret_cast<const u32x4_t*>(Zs + (size_t)(c0 + r) * EP + 8 * f)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const int b = c0 + 32 * wave + 8 * grp;  // A: row i, key blocks b .. b+7
+    w0 = w1 = zero4();
+    if (c0 / 32 + wave < nk && i < M) {
+      w0 = *reinterpret_cast<const f32x4_t*>(Wr + b);
+      w1 = *reinterpret_cast<const f32x4_t*>(Wr + b + 4);
+    }
+  };
+  f32x4_t acc[NT];
 #pragma unroll
-      for (int u = 0; u < ZCH; ++u) {
-        const int pc = tid + 256 * u;
-        const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
-        zr[u] = c0 + r < M ? *reinterpret_cast<const u32x4_t*>(Zs + (size_t)(c0 + r) * EP + 8 * f)
-                           : u32x4_t{0u, 0u, 0u, 0u};
+  for (int t = 0; t < NT; ++t) acc[t] = zero4();
+  long slice = h;
+  int c = 0;
+  fetch(slice, 0);
+  for (;;) {
+    const int c0 = c * CH;
+    const int k = c0 / 32 + wave;        // this wave's step of the chunk
+    const int b = 32 * k + 8 * grp;
+    lds_barrier();  // the previous chunk's reads of sz are done
+#pragma unroll
+    for (int u = 0; u < ZCH; ++u) {
+      const int pc = tid + 256 * u;
+      const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
+      *reinterpret_cast<u32x4_t*>(sz + r * ZR + 8 * f) = zr[u];
+    }
+    f32x4_t v0 = w0, v1 = w1;
+    if constexpr (MODE == kMixCausal) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (b + q >= i) v0[q] = 0.0f;
+        if (b + 4 + q >= i) v1[q] = 0.0f;
       }
-      __syncthreads();  // the previous chunk's reads are done
+    }
+    const u32x4_t a32 = {pack2(v0[0], v0[1]), pack2(v0[2], v0[3]), pack2(v1[0], v1[1]),
+                         pack2(v1[2], v1[3])};
+    // the coefficient tiles are written once, with the head's first slice
+    if (slice == h && k < nk) *reinterpret_cast<u32x4_t*>(Wc + coef_tiled(M, h, i, b)) = a32;
+    lds_barrier();
+    long slice2 = slice;
+    int c2 = c + 1;
+    if (c2 == nch) {
+      c2 = 0;
+      slice2 += H;
+    }
+    if (slice2 < nslices) fetch(slice2, c2 * CH);
+    if (k < nk) {
+      const u16x8_t a = __builtin_bit_cast(u16x8_t, a32);
 #pragma unroll
-      for (int u = 0; u < ZCH; ++u) {
-        const int pc = tid + 256 * u;
-        const int r = pc / (DP / 8), f = pc - (pc / (DP / 8)) * (DP / 8);
-        *reinterpret_cast<u32x4_t*>(sz + r * ZR + 8 * f) = zr[u];
-      }
-      __syncthreads();
-      const int k = c0 / 32 + wave;      // this wave's step of the chunk
-      if (k < nk) {
-        const int b = 32 * k + 8 * grp;  // A: row i, key blocks b .. b+7
-        f32x4_t w0 = zero4(), w1 = zero4();
-        if (i < M) {
-          w0 = *reinterpret_cast<const f32x4_t*>(Wr + b);
-          w1 = *reinterpret_cast<const f32x4_t*>(Wr + b + 4);
-          if constexpr (MODE == kMixCausal) {
+      for (int t = 0; t < NT; ++t)
+        acc[t] = mfma_bf16(a, lds_tr8(sz, ZR, 32 * wave, 16 * t, lane), acc[t]);
+    }
+    if (c + 1 == nch) {
+      // acc[t] lane (s, grp) element r = z~[i0 + 4grp + r][16t + s] (partial)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              if (b + q >= i) w0[q] = 0.0f;
-              if (b + 4 + q >= i) w1[q] = 0.0f;
-            }
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[wave][4 * grp + r][16 * t + s] = acc[t][r];
+      lds_barrier();
+      for (int e = tid; e < 16 * DP / 2; e += 256) {
+        const int row = e / (DP / 2), cc = 2 * (e - row * (DP / 2));
+        if (i0 + row < M) {
+          float x0 = 0.0f, x1 = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            x0 += sacc[w][row][cc];
+            x1 += sacc[w][row][cc + 1];
           }
+          *reinterpret_cast<uint32_t*>(St + ((size_t)slice * M + i0 + row) * EP + DP * DP + cc) =
+              pack2(x0, x1);
         }
-        const u32x4_t a32 = {pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), pack2(w1[0], w1[1]),
-                             pack2(w1[2], w1[3])};
-        if (first) *reinterpret_cast<u32x4_t*>(Wc + coef_tiled(M, h, i, b)) = a32;
-        const u16x8_t a = __builtin_bit_cast(u16x8_t, a32);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t] = mfma_bf16(a, lds_tr8(sz, ZR, 32 * wave, 16 * t, lane), acc[t]);
       }
+      lds_barrier();  // sacc is rewritten by the next slice
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = zero4();
     }
-    // acc[t] lane (s, grp) element r = z~[i0 + 4grp + r][16t + s] (partial)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[wave][4 * grp + r][16 * t + s] = acc[t][r];
-    __syncthreads();
-    for (int e = tid; e < 16 * DP / 2; e += 256) {
-      const int row = e / (DP / 2), c = 2 * (e - row * (DP / 2));
-      if (i0 + row < M) {
-        float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v0 += sacc[w][row][c];
-          v1 += sacc[w][row][c + 1];
-        }
-        *reinterpret_cast<uint32_t*>(St + ((size_t)slice * M + i0 + row) * EP + DP * DP + c) =
-            pack2(v0, v1);
-      }
-    }
-    __syncthreads();  // sacc is rewritten by the next slice
+    if (slice2 >= nslices) break;
+    slice = slice2;
+    c = c2;
   }
 }
 
