@@ -426,12 +426,15 @@ def backward_bench(args):
     alg_flops = wl.B * wl.H * (12 * wl.N * d2 + 6 * wl.M * wl.M * d2)
     gbs = alg_bytes / (ms / 1e3) / 1e9
     tfs = alg_flops / (ms / 1e3) / 1e12
+    roofline = roofline_of_call(gbs, tfs, alg_bytes, alg_flops)
+    # counter-measured HBM bytes per call (blocked backward, committed summary)
+    roofline["traffic"] = measured_traffic("backward", wl.name, None)
     print(json.dumps({
         "metric": "MHLA bwd tokens/s per GPU", "value": round(wl.B * wl.N / (ms / 1e3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "dtype": "bf16",
         "config": {"workload": wl.name, "pass": "backward"},
-        "roofline": roofline_of_call(gbs, tfs, alg_bytes, alg_flops)}), flush=True)
+        "roofline": roofline}), flush=True)
     return 0
 
 
@@ -499,6 +502,8 @@ PATH_SOURCES = {
     "columns": ["k_cols.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
     "pairs": ["k_pairs.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
     "blocked": ["k_blocked.hpp", "k_causal.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
+    # the blocked backward (mhla_backward with blocks of more than 16 tokens)
+    "backward": ["k_backward.hpp", "k_blocked.hpp", "mhla_mfma.hpp", "mhla_common.hpp"],
 }
 
 

@@ -150,6 +150,31 @@ def test_backward_workload_shapes(name, B, H):
     _check(dataclasses.replace(wl, B=B, H=H), 0, name)
 
 
+@pytest.mark.parametrize("B,H,grid,block,d", [
+    (2, 2, (1, 32, 32), (1, 2, 2), 64),   # M = 256: k_dw_big, partials summed by k_dw_reduce
+    (2, 3, (1, 32, 64), (1, 4, 8), 64),   # M = 64: the split dW and its reduction
+    (2, 2, (1, 16, 16), (1, 4, 4), 72),   # 16-token blocks: the token-pair backward
+])
+def test_backward_deterministic(B, H, grid, block, d):
+    """Two calls on the same inputs give bit-identical dQ, dK, dV and dW: every
+    partial sum is combined in a fixed order (no atomics)."""
+    wl = custom_workload(B, H, d, grid, block, PHI_ELU1, DTYPE_BF16, index=613)
+    inp = make_inputs(wl)
+    gbits = make_upstream_grad(wl)
+    q, k, v, w = to_device(inp)
+    dy = _bf16_dev(gbits)
+    outs = []
+    for _ in range(2):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dw = torch.empty_like(w)
+        m.mhla_backward(q, k, v, w, dy, dq, dk, dv, dw, (grid, block), wl.phi, 0)
+        outs.append((dq, dk, dv, dw))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+
+
 def test_backward_rejects():
     wl = custom_workload(1, 1, 64, (1, 1, 128), (1, 1, 32), PHI_ELU1, DTYPE_BF16, index=2)
     inp = make_inputs(wl)
