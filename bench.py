@@ -137,7 +137,7 @@ def kernel_work(name, wl, path_name):
     Wb = wl.H * wl.M * wl.M * 4
     f_side = 2 * wl.N * wl.d * wl.d * S                 # summaries or readout
     f_mix = 2 * wl.M * wl.M * wl.d * wl.d * S
-    if name in ("k_fused", "k_pairs", "k_cols"):
+    if name in ("k_fused", "k_pairs", "k_cols", "k_generic_one"):
         return wl.algorithmic_bytes(), wl.algorithmic_flops()
     if name.startswith("k_summary"):
         return 2 * T + E, f_side

@@ -41,14 +41,17 @@ def _same(a, b):
     (("video", 1), ("m256", 2)),
     # chunkwise causal form, then a smaller causal call
     (("lm_causal", 16), ("lm_causal", 3)),
-    # fp32 generic path (fp32 tables), then a smaller fp32 call
-    (("tiny", 1), ("tiny_small", 1)),
+    # fp32 generic path in its three-kernel form (fp32 tables), then a smaller
+    # fp32 call (slices too large for the single-launch form)
+    (("f32_256", 1), ("f32_128", 1)),
 ])
 def test_noalloc_matches_the_allocating_entry_point(first, second):
     shapes = {
         "m256": custom_workload(2, 2, 64, (4, 32, 32), (1, 4, 4), PHI_ELU1, DTYPE_BF16, index=41),
-        "tiny_small": custom_workload(1, 1, 8, (1, 4, 8), (1, 2, 4), PHI_RELU, DTYPE_F32,
-                                      index=42),
+        "f32_256": custom_workload(1, 2, 64, (1, 16, 16), (1, 4, 4), PHI_RELU, DTYPE_F32,
+                                   index=42),
+        "f32_128": custom_workload(1, 1, 64, (1, 8, 16), (1, 4, 4), PHI_ELU1, DTYPE_F32,
+                                   index=43),
     }
     sizes = []
     for name, B in (first, second):
@@ -63,8 +66,9 @@ def test_noalloc_matches_the_allocating_entry_point(first, second):
 
 
 def test_noalloc_paths_without_scratch():
-    """The fused and token-pair paths keep everything on chip."""
-    for name in ("deit_t", "dit_xl2"):
+    """The fused and token-pair paths, and the generic path's single-launch
+    form (the tiny fp32 problem), keep everything on chip."""
+    for name in ("deit_t", "dit_xl2", "tiny"):
         inp = make_inputs(WORKLOADS[name], B=2)
         ref, out, need = _both(inp)
         assert need == 0

@@ -165,4 +165,88 @@ __global__ __launch_bounds__(kValuThreads) void k_readout_valu(
   }
 }
 
+// The three steps in one launch for problems whose slice fits in LDS (the
+// launch, not the arithmetic, is what a small call costs): one workgroup per
+// slice stages phi(Q), phi(K) and V with one round of loads, forms every
+// block's summary, mixes every query block's S~, then every token's
+// denominator and output.  Every sum is taken in the order the three kernels
+// above take it (tokens of a block in order, key blocks in order, features in
+// order, fma for fma).  LDS: generic_one_lds_bytes.  grid = B*H, block = 1024.
+inline size_t generic_one_lds_bytes(int N, int d, int M) {
+  const size_t C = (size_t)d + 1, L = (size_t)d * d + d;
+  return (3 * (size_t)N * C + 2 * (size_t)M * L + (size_t)N) * sizeof(float);
+}
+constexpr size_t kGenericOneLds = 64 * 1024;  // the default dynamic LDS limit
+constexpr int kGenericOneThreads = 1024;       // the whole slice's work in one workgroup
+
+template <typename T>
+__global__ __launch_bounds__(kGenericOneThreads) void k_generic_one(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ W, T* __restrict__ Y, Geo g, int N, int d, int phi, int H) {
+  extern __shared__ float sm1[];
+  const int C = d + 1;  // LDS row stride (odd: no bank conflicts along a column)
+  const int dd = d * d, L = dd + d, M = g.M, nb = g.nb;
+  float* sQ = sm1;            // phi(Q) [N][C], token order of the slice
+  float* sK = sQ + N * C;     // phi(K) [N][C]
+  float* sV = sK + N * C;     // V [N][C]
+  float* sS = sV + N * C;     // summaries [M][L] (entry c*d + k = S[k][c], then z)
+  float* sT = sS + M * L;     // mixed summaries S~ [M][L]
+  float* sden = sT + M * L;   // denominators [N]
+  const int tid = threadIdx.x;
+  const long bh = blockIdx.x;
+  const int h = (int)(bh % H);
+  const long off = bh * (long)N * d;
+  const float* Wh = W + (long)h * M * M;
+
+  for (int e = tid; e < N * d; e += kGenericOneThreads) {
+    const int t = e / d, a = e - (e / d) * d;
+    sQ[t * C + a] = phi_apply(phi, Elt<T>::load(Q + off + e));
+    sK[t * C + a] = phi_apply(phi, Elt<T>::load(K + off + e));
+    sV[t * C + a] = Elt<T>::load(V + off + e);
+  }
+  __syncthreads();
+  for (int e = tid; e < M * L; e += kGenericOneThreads) {
+    const int b = e / L, r = e - (e / L) * L;
+    float s = 0.0f;
+    if (r < dd) {
+      const int c = r / d, k = r - (r / d) * d;
+      for (int j = 0; j < nb; ++j) {
+        const int t = g.token(b, j);
+        s = fmaf(sK[t * C + k], sV[t * C + c], s);
+      }
+    } else {
+      const int k = r - dd;
+      for (int j = 0; j < nb; ++j) s += sK[g.token(b, j) * C + k];
+    }
+    sS[e] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < M * L; e += kGenericOneThreads) {
+    const int i = e / L, r = e - (e / L) * L;
+    float a = 0.0f;
+    for (int b = 0; b < M; ++b) a = fmaf(Wh[(long)i * M + b], sS[b * L + r], a);
+    sT[e] = a;
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += kGenericOneThreads) {  // e = (block i, member j)
+    const int i = e / nb, j = e - (e / nb) * nb;
+    const int t = g.token(i, j);
+    const float* zt = sT + i * L + dd;
+    float den = 0.0f;
+    for (int a = 0; a < d; ++a) den = fmaf(sQ[t * C + a], zt[a], den);
+    sden[t] = den;
+  }
+  __syncthreads();
+  for (int e = tid; e < N * d; e += kGenericOneThreads) {  // e = (block i, member j, column c)
+    const int ij = e / d, c = e - (e / d) * d;
+    const int i = ij / nb, j = ij - (ij / nb) * nb;
+    const int t = g.token(i, j);
+    const float* st = sT + i * L + c * d;
+    float acc = 0.0f;
+    for (int k = 0; k < d; ++k) acc = fmaf(sQ[t * C + k], st[k], acc);
+    const float den = sden[t];
+    Elt<T>::store(Y + off + (long)t * d + c, !g.norm ? acc : den == 0.0f ? 0.0f : acc / den);
+  }
+}
+
 }  // namespace mhla

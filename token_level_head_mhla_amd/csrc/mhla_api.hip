@@ -82,8 +82,14 @@ int choose_path(const Problem& p) {
   return -MHLA_ERR_UNSUPPORTED;
 }
 
+// The generic path's single-launch form (k_generic_one) when a slice fits in LDS.
+bool generic_one(const Problem& p) {
+  return generic_one_lds_bytes(p.N, p.d, p.g.M) <= kGenericOneLds;
+}
+
 size_t workspace_for(const Problem& p, int path) {
   if (path == MHLA_PATH_GENERIC) {
+    if (generic_one(p)) return 0;
     const size_t L = (size_t)p.d * p.d + p.d;
     return 2 * (size_t)p.slices() * p.g.M * L * sizeof(float);
   }
@@ -133,6 +139,13 @@ template <typename T>
 int launch_generic(const Problem& p, const T* Q, const T* K, const T* V, const float* W,
                    T* Y, float* ws, hipStream_t st) {
   const int M = p.g.M, d = p.d;
+  if (generic_one(p)) {
+    const size_t lds = generic_one_lds_bytes(p.N, d, M);
+    k_generic_one<T><<<dim3((unsigned)p.slices()), kGenericOneThreads, lds, st>>>(
+        Q, K, V, W, Y, p.g, p.N, d, p.phi, p.H);
+    launch_mark(st, "k_generic_one");
+    return MHLA_OK;
+  }
   const int L = d * d + d;
   float* S = ws;
   float* St = ws + (size_t)p.slices() * M * L;
