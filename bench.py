@@ -478,6 +478,22 @@ def decode_bench(args):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / wl.N
+    # prefill: the decode state from the whole sequence as a prompt, in one call
+    kp = torch.from_numpy(np.ascontiguousarray(inp.k).view(np.int16)).view(torch.bfloat16).cuda()
+    vp = torch.from_numpy(np.ascontiguousarray(inp.v).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def prefill():
+        m.mhla_decode_prefill(kp, vp, w, state, M, nb, wl.phi, wl.flags, stream=stream)
+
+    for _ in range(3):
+        prefill()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(20):
+        prefill()
+    end.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = start.elapsed_time(end) / 20
     E = wl.d * (wl.d + 1) * 4
     # per step and slice: prefix read, running summary read and written, q/k/v/y
     step_bytes = wl.B * wl.H * (3 * E + 4 * wl.d * 2)
@@ -490,7 +506,9 @@ def decode_bench(args):
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "state_bytes_per_step": step_bytes}}),
+                     "traffic": None, "state_bytes_per_step": step_bytes},
+        "prefill": {"prompt_tokens": wl.N, "us_per_call": round(prefill_ms * 1e3, 2),
+                    "tokens_per_s": round(wl.B * wl.N / (prefill_ms / 1e3), 1)}}),
           flush=True)
     return 0
 

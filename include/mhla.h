@@ -231,6 +231,25 @@ int mhla_decode_step(const void* q, const void* k, const void* v, const float* W
                      void* y, void* state, int B, int H, int d, int M, int nb, int t,
                      int phi_kind, int dtype, int flags, mhla_stream_t stream);
 
+/* Prefill for incremental inference (MHLA paper App. C, "Causal inference"):
+ * builds, from the first T tokens of every slice, the decode state that T
+ * calls of mhla_decode_step (t = 0 .. T-1) would leave, so that the stream
+ * continues with mhla_decode_step at t = T.  k, v: [B, H, T, d] device
+ * tensors of `dtype` (the prompt's keys and values; no query is needed);
+ * Wmix: [H, M, M] fp32; state: the caller's buffer of
+ * mhla_decode_state_bytes(B, H, d, M) bytes.  It writes the summaries of the
+ * ceil(T / nb) chunks the prompt touches (the last one running when T is not
+ * a multiple of nb) and the prefix mixture of chunk (T - 1) / nb, each sum
+ * taken in the order the decode step takes it, so the state is the same
+ * bits; the slots of later chunks are left as they are.  The prompt's outputs
+ * are those of mhla_forward_ex(..., MHLA_FLAG_CAUSAL, ...) on its first T
+ * tokens.  Errors: MHLA_ERR_INVALID_ARG (bad sizes, T outside [1, M*nb], NULL
+ * pointers, unknown flags), MHLA_ERR_UNSUPPORTED (as mhla_decode_step),
+ * MHLA_ERR_ALIAS (the state overlaps k, v or Wmix). */
+int mhla_decode_prefill(const void* k, const void* v, const float* Wmix, void* state, int B,
+                        int H, int d, int M, int nb, int T, int phi_kind, int dtype, int flags,
+                        mhla_stream_t stream);
+
 /* Host-only argument check (no HIP call): MHLA_OK or the code mhla_forward
  * would return for these sizes. */
 int mhla_validate(int B, int H, int N, int d, const mhla_block_shape* block_shape,

@@ -271,6 +271,29 @@ def test_decode_state_bytes_and_rejects():
                                 None) == m.MHLA_ERR_INVALID_ARG
 
 
+
+def test_decode_prefill_rejects():
+    """Every call here fails in the host checks, before any HIP call."""
+    lib = m.load_library()
+    buf = (ctypes.c_char * (1 << 16))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    k, v, w, st = (base + 4096 * i for i in range(4))
+    call = lambda *a: lib.mhla_decode_prefill(k, v, w, st, *a)
+    # (B, H, d, M, nb, T, phi, dtype, flags, stream)
+    assert call(1, 1, 16, 4, 8, 0, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG    # empty prompt
+    assert call(1, 1, 16, 4, 8, 33, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG   # T > M*nb
+    assert call(1, 1, 16, 4, 0, 4, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG    # nb = 0
+    assert call(1, 1, 16, 4, 8, 4, 2, 1, 0, None) == m.MHLA_ERR_INVALID_ARG    # unknown phi
+    assert call(1, 1, 16, 4, 8, 4, 0, 1, 4, None) == m.MHLA_ERR_INVALID_ARG    # unknown flag
+    assert call(1, 1, 12, 4, 8, 4, 0, 1, 0, None) == m.MHLA_ERR_UNSUPPORTED    # bf16, d % 8
+    assert call(1, 1, 136, 4, 8, 4, 0, 0, 0, None) == m.MHLA_ERR_UNSUPPORTED   # d > 128
+    # the state (32 KB here) would cover k
+    assert lib.mhla_decode_prefill(k, v, w, k, 1, 1, 16, 4, 8, 4, 0, 1, 0,
+                                   None) == m.MHLA_ERR_ALIAS
+    assert lib.mhla_decode_prefill(None, v, w, st, 1, 1, 16, 4, 8, 4, 0, 1, 0,
+                                   None) == m.MHLA_ERR_INVALID_ARG
+
+
 # ---------------------------------------------------------------- the contract's signatures
 
 # The boundary calls, with the argument types of the method's statement of

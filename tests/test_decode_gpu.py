@@ -77,3 +77,49 @@ def test_decode_matches_chunkwise_forward_on_gpu():
     err = slice_error(y_dec, to_f64(out))
     print("PARITY decode vs chunkwise forward err=%.3e" % err)
     assert err <= TOL[DTYPE_BF16]
+
+
+PREFILL_CASES = [
+    # (B, H, N, nb, d, phi, dtype, T): T prompt tokens, then decoding to N
+    (2, 3, 256, 64, 64, PHI_ELU1, DTYPE_BF16, 100),   # the prompt ends inside chunk 1
+    (2, 3, 256, 64, 64, PHI_ELU1, DTYPE_BF16, 128),   # ... on a chunk boundary
+    (1, 2, 96, 16, 72, PHI_RELU, DTYPE_BF16, 1),      # a one-token prompt
+    (1, 1, 64, 16, 16, PHI_RELU, DTYPE_F32, 63),
+    (1, 2, 32, 8, 128, PHI_ELU1, DTYPE_F32, 20),      # d = 128
+    (1, 2, 30, 6, 13, PHI_ELU1, DTYPE_F32, 30),       # odd d; the whole sequence as prompt
+]
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("B,H,N,nb,d,phi,dtype,T", PREFILL_CASES)
+def test_decode_prefill(B, H, N, nb, d, phi, dtype, T, norm):
+    """mhla_decode_prefill leaves the state of T decode steps, bit for bit, and
+    decoding continues from it to the oracle's outputs."""
+    flags = FLAG_CAUSAL | (0 if norm else FLAG_NO_NORM)
+    wl = custom_workload(B, H, d, (1, 1, N), (1, 1, nb), phi, dtype,
+                         index=hash((N, nb, d, T)) % 911, flags=flags)
+    inp = make_inputs(wl)
+    q, k, v, w = to_device(inp)
+    M = N // nb
+    qt, kt, vt = (x.permute(2, 0, 1, 3).contiguous() for x in (q, k, v))   # [N, B, H, d]
+    words = m.mhla_decode_state_bytes(B, H, d, M) // 4
+    stepped = torch.full((words,), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(qt)
+    for t in range(T):
+        m.mhla_decode_step(qt[t], kt[t], vt[t], w, y[t], stepped, M, nb, t, wl.phi, flags)
+    filled = torch.full((words,), float("nan"), dtype=torch.float32, device="cuda")
+    m.mhla_decode_prefill(k[:, :, :T].contiguous(), v[:, :, :T].contiguous(), w, filled, M, nb,
+                          wl.phi, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(stepped.view(torch.int32), filled.view(torch.int32))
+    for t in range(T, N):
+        m.mhla_decode_step(qt[t], kt[t], vt[t], w, y[t], filled, M, nb, t, wl.phi, flags)
+    torch.cuda.synchronize()
+    if T == N:
+        return
+    got = to_f64(y.permute(1, 2, 0, 3).contiguous())[:, :, T:]
+    ref = oracle.np_decode(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, nb, phi, norm=norm)[:, :, T:]
+    err = slice_error(got, ref)
+    print("PARITY decode prefill N=%d nb=%d d=%d T=%d dtype=%d norm=%d err=%.3e"
+          % (N, nb, d, T, dtype, norm, err))
+    assert err <= TOL[dtype]

@@ -14,7 +14,8 @@ from ._binding import (  # noqa: F401
     MHLA_PATH_PAIRS,
     MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_MAX_LAUNCHES, MhlaError, BlockShape, EXPORTED_SYMBOLS,
     PreparedForward, library_path,
-    load_library, mhla_backward, mhla_decode_state_bytes, mhla_decode_step, mhla_error_string,
+    load_library, mhla_backward, mhla_decode_prefill, mhla_decode_state_bytes, mhla_decode_step,
+    mhla_error_string,
     mhla_forward, mhla_forward_ex, mhla_forward_noalloc, mhla_forward_path, mhla_forward_profiled,
     MHLA_NOALLOC_SCRATCH_BYTES,
     mhla_last_error, mhla_lb_init, mhla_num_blocks, mhla_plan, mhla_plan_ex, mhla_release,

@@ -21,7 +21,8 @@ MHLA_MAX_LAUNCHES = 8
 
 EXPORTED_SYMBOLS = (
     "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward",
-    "mhla_decode_state_bytes", "mhla_decode_step", "mhla_validate", "mhla_plan",
+    "mhla_decode_state_bytes", "mhla_decode_step", "mhla_decode_prefill", "mhla_validate",
+    "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
     "mhla_workspace_bytes_ex", "mhla_forward_profiled", "mhla_forward_noalloc",
     "mhla_error_string", "mhla_last_error", "mhla_release",
@@ -91,6 +92,8 @@ def load_library():
     lib.mhla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip,
                                      vp]
     lib.mhla_decode_step.restype = ip
+    lib.mhla_decode_prefill.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip, vp]
+    lib.mhla_decode_prefill.restype = ip
     lib.mhla_plan_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
     lib.mhla_plan_ex.restype = ip
     lib.mhla_lb_init.argtypes = [bsp, ctypes.POINTER(ctypes.c_float), ctypes.c_size_t]
@@ -313,6 +316,34 @@ def mhla_decode_step(q, k, v, Wmix, y, state, M, nb, t, phi_kind, flags=0, strea
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())
     return y
+
+
+def mhla_decode_prefill(k, v, Wmix, state, M, nb, phi_kind, flags=0, stream=None):
+    """Decode state from a prompt: k, v are [B, H, T, d] GPU tensors (its first
+    T tokens); state is a GPU buffer of mhla_decode_state_bytes(B, H, d, M)
+    bytes.  mhla_decode_step continues at t = T."""
+    import torch
+    for name, t_ in (("k", k), ("v", v), ("Wmix", Wmix), ("state", state)):
+        if not (isinstance(t_, torch.Tensor) and t_.is_cuda and t_.is_contiguous()):
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k, v must share one [B, H, T, d] shape")
+    if v.dtype != k.dtype:
+        raise ValueError("k, v must share one dtype")
+    if Wmix.dtype != torch.float32:
+        raise ValueError("Wmix must be float32")
+    B, H, T, d = k.shape
+    if Wmix.numel() != H * int(M) * int(M):
+        raise ValueError("Wmix has %d elements; H*M*M = %d are needed"
+                         % (Wmix.numel(), H * int(M) * int(M)))
+    if state.numel() * state.element_size() < mhla_decode_state_bytes(B, H, d, M):
+        raise ValueError("state is smaller than mhla_decode_state_bytes")
+    rc = load_library().mhla_decode_prefill(
+        k.data_ptr(), v.data_ptr(), Wmix.data_ptr(), state.data_ptr(), B, H, d, int(M), int(nb),
+        T, int(phi_kind), _dtype_code(k), int(flags), _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return state
 
 
 def mhla_forward(Q, K, V, Wmix, out, block_shape, phi_kind, stream=None):

@@ -446,6 +446,37 @@ int mhla_decode_step(const void* q, const void* k, const void* v, const float* W
   return MHLA_OK;
 }
 
+int mhla_decode_prefill(const void* k, const void* v, const float* Wmix, void* state, int B,
+                        int H, int d, int M, int nb, int T, int phi_kind, int dtype, int flags,
+                        mhla_stream_t stream) {
+  if (T <= 0) return fail(MHLA_ERR_INVALID_ARG, "T=%d: the prompt must hold a token", T);
+  int rc = check_decode(B, H, d, M, nb, T - 1, phi_kind, dtype, flags);
+  if (rc != MHLA_OK) return rc;
+  if (!k || !v || !Wmix || !state) return fail(MHLA_ERR_INVALID_ARG, "a pointer is NULL");
+  const void* ptrs[4] = {k, v, Wmix, state};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+      return fail(MHLA_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  const size_t eb = dtype == MHLA_DTYPE_F32 ? 4 : 2;
+  const size_t tb = (size_t)B * H * T * d * eb;
+  const size_t sb = mhla_decode_state_bytes(B, H, d, M);
+  if (overlaps(state, sb, k, tb) || overlaps(state, sb, v, tb) ||
+      overlaps(state, sb, Wmix, (size_t)H * M * M * sizeof(float)))
+    return fail(MHLA_ERR_ALIAS, "the state overlaps k, v or Wmix");
+  hipStream_t st = stream;
+  (void)hipGetLastError();
+  const long slices = (long)B * H;
+  if (dtype == MHLA_DTYPE_F32)
+    launch_decode_prefill_t<float>(slices, H, d, M, nb, T, phi_kind, (const float*)k,
+                                   (const float*)v, Wmix, (float*)state, st);
+  else
+    launch_decode_prefill_t<bf16_t>(slices, H, d, M, nb, T, phi_kind, (const bf16_t*)k,
+                                    (const bf16_t*)v, Wmix, (float*)state, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MHLA_OK;
+}
+
 int mhla_plan_ex(int B, int H, int N, int d, const mhla_block_shape* block_shape, int phi_kind,
                  int dtype, int flags) {
   Problem p;
