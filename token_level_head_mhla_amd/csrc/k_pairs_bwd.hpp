@@ -390,85 +390,78 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
   }
   lds_barrier();
 
-  // ---- this wave's key blocks: phi(K) and V B operands (key s) ---------------
+  // ---- this wave's key blocks, one after another: each block's phi(K) and V
+  // operands and dV, dK accumulators are live only while its queries are
+  // swept (two blocks at once took more than 256 registers and spilled)
   const int myk = (M - wave + kPairsWaves - 1) / kPairsWaves;
-  int ktok[QB];
-  u16x8_t kf[QB][KSF], vf[QB][CS];
-#pragma unroll
+  const int vj = 4 * grp + (s >> 2);
+#pragma unroll 1
   for (int u = 0; u < QB; ++u) {
+    if (u >= myk) break;
     const int b = wave + u * kPairsWaves;
-    const bool real = u < myk && s < nb;
-    ktok[u] = real ? sB[b] + g.tokoff(s) : -1;
+    const bool kreal = s < nb;
+    const int ktok = kreal ? sB[b] + g.tokoff(s) : -1;
+    u16x8_t kf[KSF], vf[CS];
 #pragma unroll
-    for (int ks = 0; ks < KSF; ++ks) kf[u][ks] = feat_operand<PHI>(K + off, ktok[u], d, ks, KS, grp);
+    for (int ks = 0; ks < KSF; ++ks) kf[ks] = feat_operand<PHI>(K + off, ktok, d, ks, KS, grp);
     // V in the acc8 order of the value columns; columns past d are 0
 #pragma unroll
     for (int m = 0; m < CS; ++m) {
       // unconditional loads at clamped addresses, masked after
       const int c0 = 32 * m + 4 * grp, c1 = c0 + 16;
-      const bf16_t* vrow = V + off + (size_t)(real ? ktok[u] : 0) * d;
+      const bf16_t* vrow = V + off + (size_t)(kreal ? ktok : 0) * d;
       const uint2 lo = *reinterpret_cast<const uint2*>(vrow + min(c0, d - 4));
       const uint2 hi = *reinterpret_cast<const uint2*>(vrow + min(c1, d - 4));
       const uint2 z = make_uint2(0u, 0u);
-      vf[u][m] = from_u2x2(real && c0 < d ? lo : z, real && c1 < d ? hi : z);
+      vf[m] = from_u2x2(kreal && c0 < d ? lo : z, kreal && c1 < d ? hi : z);
     }
-  }
-
-  const int vj = 4 * grp + (s >> 2);
-
-  f32x4_t dv[QB][FT], dk[QB][FT];
+    f32x4_t dv[FT], dk[FT];
 #pragma unroll
-  for (int u = 0; u < QB; ++u)
+    for (int f = 0; f < FT; ++f) dv[f] = dk[f] = zero4();
+    for (int i0 = 0; i0 < M; i0 += 2) {
+      int qr[2], qv[2];
+      float dd[2][4];
 #pragma unroll
-    for (int f = 0; f < FT; ++f) dv[u][f] = dk[u][f] = zero4();
-  for (int i0 = 0; i0 < M; i0 += 2) {
-    int qr[2], qv[2];
-    float dd[2][4];
+      for (int hb = 0; hb < 2; ++hb) {
+        const int i = i0 + hb;
+        const bool real = i < M;
+        qr[hb] = (real && s < nb) ? i * nb + s : N;
+        qv[hb] = (real && vj < nb) ? i * nb + vj : N;
+        // this lane's output rows of P and dA: query members 4grp + r
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int i = i0 + hb;
-      const bool real = i < M;
-      qr[hb] = (real && s < nb) ? i * nb + s : N;
-      qv[hb] = (real && vj < nb) ? i * nb + vj : N;
-      // this lane's output rows of P and dA: query members 4grp + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dd[hb][r] = (real && 4 * grp + r < nb) ? sdd[i * nb + 4 * grp + r] : 0.0f;
-    }
-    // row operands (query member s): phi(Q) over features, dnum over values
-    u16x8_t qa[2][KSF], na[2][CS], nl[2][CS];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int ks = 0; ks < KSF; ++ks) qa[hb][ks] = feat_row(sQ, prow(qr[hb], RSQ), 1, ks, KS, grp);
-#pragma unroll
-      for (int m = 0; m < CS; ++m) {
-        na[hb][m] = acc8_row<CT>(sD, prow(qr[hb], RSD), 1, m, grp);
-        nl[hb][m] = acc8_row<CT>(sDl, prow(qr[hb], RSD), 1, m, grp);
+        for (int r = 0; r < 4; ++r)
+          dd[hb][r] = (real && 4 * grp + r < nb) ? sdd[i * nb + 4 * grp + r] : 0.0f;
       }
-    }
-    // transposed operands: rows c (dnum^T) and f (phi(Q)^T) = 16t + s,
-    // queries {4grp..4grp+3} of i0 then of i0 + 1
-    u16x8_t nT[FT], qT[FT];
+      // row operands (query member s): phi(Q) over features, dnum over values
+      u16x8_t qa[2][KSF], na[2][CS], nl[2][CS];
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      nT[f] = lds_tr8_rows(sD + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSD), prow(qv[1], RSD));
-      qT[f] = lds_tr8_rows(sQ + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSQ), prow(qv[1], RSQ));
-    }
+      for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      if (u >= myk) break;
-      const int b = wave + u * kPairsWaves;
+        for (int ks = 0; ks < KSF; ++ks) qa[hb][ks] = feat_row(sQ, prow(qr[hb], RSQ), 1, ks, KS, grp);
+#pragma unroll
+        for (int m = 0; m < CS; ++m) {
+          na[hb][m] = acc8_row<CT>(sD, prow(qr[hb], RSD), 1, m, grp);
+          nl[hb][m] = acc8_row<CT>(sDl, prow(qr[hb], RSD), 1, m, grp);
+        }
+      }
+      // transposed operands: rows c (dnum^T) and f (phi(Q)^T) = 16t + s,
+      // queries {4grp..4grp+3} of i0 then of i0 + 1
+      u16x8_t nT[FT], qT[FT];
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        nT[f] = lds_tr8_rows(sD + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSD), prow(qv[1], RSD));
+        qT[f] = lds_tr8_rows(sQ + 16 * f + 4 * (s & 3), 1, prow(qv[0], RSQ), prow(qv[1], RSQ));
+      }
       f32x4_t a[2], dp[2];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         f32x4_t p = zero4(), da = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KSF; ++ks) p = mfma_bf16(qa[hb][ks], kf[u][ks], p);
+        for (int ks = 0; ks < KSF; ++ks) p = mfma_bf16(qa[hb][ks], kf[ks], p);
 #pragma unroll
         for (int m = 0; m < CS; ++m) {
-          da = mfma_bf16(na[hb][m], vf[u][m], da);
-          da = mfma_bf16(nl[hb][m], vf[u][m], da);
+          da = mfma_bf16(na[hb][m], vf[m], da);
+          da = mfma_bf16(nl[hb][m], vf[m], da);
         }
         // lane (s, grp) element r: query 4grp + r of block i0 + hb, key s
 #pragma unroll
@@ -480,31 +473,25 @@ __global__ __launch_bounds__(kPairsThreads) void k_pbwd_k(
       const u16x8_t ab = pack_acc8(a[0], a[1]), dpb = pack_acc8(dp[0], dp[1]);
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
-        dv[u][f] = mfma_bf16(nT[f], ab, dv[u][f]);
-        dk[u][f] = mfma_bf16(qT[f], dpb, dk[u][f]);
+        dv[f] = mfma_bf16(nT[f], ab, dv[f]);
+        dk[f] = mfma_bf16(qT[f], dpb, dk[f]);
       }
     }
-  }
 
-  // ---- dV, dK = dphi(K) * phi'(K) ----------------------------------------------
-  // dv[u][f] / dk[u][f] lane (s, grp) element r = dV^T / dphi(K)^T[16f + 4grp + r][key s]
-#pragma unroll
-  for (int u = 0; u < QB; ++u) {
-    if (u >= myk) break;
+    // ---- dV, dK = dphi(K) * phi'(K) ----------------------------------------------
+    // dv[f] / dk[f] lane (s, grp) element r = dV^T / dphi(K)^T[16f + 4grp + r][key s]
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
       const int f0 = 16 * f + 4 * grp;
-      if (ktok[u] >= 0 && f0 < d) {
-        const uint2 x = *reinterpret_cast<const uint2*>(K + off + (size_t)ktok[u] * d + f0);
+      if (ktok >= 0 && f0 < d) {
+        const uint2 x = *reinterpret_cast<const uint2*>(K + off + (size_t)ktok * d + f0);
         const float xv[4] = {lo_f32(x.x), hi_f32(x.x), lo_f32(x.y), hi_f32(x.y)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dk[u][f][r] *= dphi_apply<PHI>(xv[r]);
+        for (int r = 0; r < 4; ++r) dk[f][r] *= dphi_apply<PHI>(xv[r]);
       }
     }
-    store_row_tiles<FT>(ktok[u] >= 0 ? dV + off + (size_t)ktok[u] * d : nullptr, d, dv[u], 1.0f,
-                        grp);
-    store_row_tiles<FT>(ktok[u] >= 0 ? dK + off + (size_t)ktok[u] * d : nullptr, d, dk[u], 1.0f,
-                        grp);
+    store_row_tiles<FT>(ktok >= 0 ? dV + off + (size_t)ktok * d : nullptr, d, dv, 1.0f, grp);
+    store_row_tiles<FT>(ktok >= 0 ? dK + off + (size_t)ktok * d : nullptr, d, dk, 1.0f, grp);
   }
 }
 
