@@ -310,6 +310,13 @@ const char* (*f_err)(int) = mhla_error_string;
 void (*f_release)(void) = mhla_release;
 int (*f_ex)(const void*, const void*, const void*, const float*, void*, int, int, int, int,
             const mhla_block_shape*, int, int, int, int, hipStream_t) = mhla_forward_ex;
+int (*f_bwd)(const void*, const void*, const void*, const float*, const void*, void*, void*,
+             void*, float*, int, int, int, int, const mhla_block_shape*, int, int, int,
+             hipStream_t) = mhla_backward;
+int (*f_step)(const void*, const void*, const void*, const float*, void*, void*, int, int, int,
+              int, int, int, int, int, int, hipStream_t) = mhla_decode_step;
+int (*f_prefill)(const void*, const void*, const float*, void*, int, int, int, int, int, int,
+                 int, int, int, hipStream_t) = mhla_decode_prefill;
 """
 
 CONTRACT_CXX = r"""
