@@ -441,7 +441,9 @@ def backward_bench(args):
 def decode_bench(args):
     """One step = one mhla_decode_step call: one new token for each of the B*H
     slices.  The timed region streams the whole sequence (N steps) after a
-    warm-up pass; tokens/s counts B tokens per step."""
+    warm-up pass; tokens/s counts B tokens per step.  Also reported: the
+    prefill of the whole sequence as a prompt, and the sequence streamed with
+    mhla_decode_steps in calls of 16 tokens."""
     import torch
     import token_level_head_mhla_amd as m
     from mhla_inputs import WORKLOADS, make_inputs
@@ -494,6 +496,24 @@ def decode_bench(args):
     end.record(stream)
     torch.cuda.synchronize()
     prefill_ms = start.elapsed_time(end) / 20
+    # several tokens per call: the sequence in calls of 16 tokens, inputs cut beforehand
+    GROUP = 16
+    qg, kg, vg = ([x[t:t + GROUP].permute(1, 2, 0, 3).contiguous()
+                   for t in range(0, wl.N, GROUP)] for x in (qt, kt, vt))
+    yg = [torch.empty_like(x) for x in qg]
+
+    def run_groups():
+        for c in range(len(qg)):
+            m.mhla_decode_steps(qg[c], kg[c], vg[c], w, yg[c], state, M, nb, c * GROUP, wl.phi,
+                                wl.flags, stream=stream)
+
+    run_groups()
+    torch.cuda.synchronize()
+    start.record(stream)
+    run_groups()
+    end.record(stream)
+    torch.cuda.synchronize()
+    group_ms = start.elapsed_time(end) / wl.N
     E = wl.d * (wl.d + 1) * 4
     # per step and slice: prefix read, running summary read and written, q/k/v/y
     step_bytes = wl.B * wl.H * (3 * E + 4 * wl.d * 2)
@@ -508,7 +528,9 @@ def decode_bench(args):
                      "frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "state_bytes_per_step": step_bytes},
         "prefill": {"prompt_tokens": wl.N, "us_per_call": round(prefill_ms * 1e3, 2),
-                    "tokens_per_s": round(wl.B * wl.N / (prefill_ms / 1e3), 1)}}),
+                    "tokens_per_s": round(wl.B * wl.N / (prefill_ms / 1e3), 1)},
+        "steps_per_call": {"tokens_per_call": GROUP, "us_per_token": round(group_ms * 1e3, 3),
+                           "tokens_per_s": round(wl.B / (group_ms / 1e3), 1)}}),
           flush=True)
     return 0
 

@@ -224,12 +224,25 @@ int mhla_backward(const void* Q, const void* K, const void* V, const float* Wmix
  * when a chunk starts.  flags: 0 or MHLA_FLAG_NO_NORM (MHLA_FLAG_CAUSAL is
  * implied and accepted).  Errors: MHLA_ERR_INVALID_ARG (bad sizes, t outside
  * [0, M*nb), NULL pointers, unknown flags), MHLA_ERR_UNSUPPORTED (d > 128, or
- * bf16 with d not a multiple of 8), MHLA_ERR_ALIAS (y overlaps q, k, v or the
- * state). */
+ * bf16 with d not a multiple of 8), MHLA_ERR_ALIAS (y overlaps q, k, v, Wmix or
+ * the state, or the state overlaps q, k, v or Wmix). */
 size_t mhla_decode_state_bytes(int B, int H, int d, int M);
 int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix,
                      void* y, void* state, int B, int H, int d, int M, int nb, int t,
                      int phi_kind, int dtype, int flags, mhla_stream_t stream);
+
+/* Several tokens per slice in one call (MHLA paper App. C, "Causal
+ * inference"): the n tokens t0 .. t0+n-1 of every slice, taken in order, each
+ * exactly as one mhla_decode_step call for it would take it, so y and the
+ * state are the same bits as those n calls leave; one launch instead of n
+ * (for a block of tokens known ahead, such as candidate tokens to check, or
+ * a prompt whose outputs are wanted as well).  q, k, v, y: [B, H, n, d]
+ * device tensors of `dtype`, token t0 + u of every slice at row u; the other
+ * arguments, the ordering rule and the errors are those of mhla_decode_step,
+ * with t0 + n - 1 in place of t (n >= 1, t0 >= 0, t0 + n <= M*nb). */
+int mhla_decode_steps(const void* q, const void* k, const void* v, const float* Wmix,
+                      void* y, void* state, int B, int H, int d, int M, int nb, int t0, int n,
+                      int phi_kind, int dtype, int flags, mhla_stream_t stream);
 
 /* Prefill for incremental inference (MHLA paper App. C, "Causal inference"):
  * builds, from the first T tokens of every slice, the decode state that T

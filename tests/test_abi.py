@@ -272,6 +272,33 @@ def test_decode_state_bytes_and_rejects():
 
 
 
+def test_decode_steps_rejects():
+    """Every call here fails in the host checks, before any HIP call."""
+    lib = m.load_library()
+    buf = (ctypes.c_char * (1 << 17))()
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    q, k, v, w, y, st = (base + 8192 * i for i in range(6))
+    call = lambda *a: lib.mhla_decode_steps(q, k, v, w, y, st, *a)
+    # (B, H, d, M, nb, t0, n, phi, dtype, flags, stream); M * nb = 32 positions
+    assert call(1, 1, 16, 4, 8, 0, 0, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG    # n = 0
+    assert call(1, 1, 16, 4, 8, 0, -3, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG   # n < 0
+    assert call(1, 1, 16, 4, 8, 30, 3, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG   # past M*nb
+    assert call(1, 1, 16, 4, 8, -1, 2, 0, 1, 0, None) == m.MHLA_ERR_INVALID_ARG   # t0 < 0
+    assert call(1, 1, 16, 4, 8, 1, 0x7fffffff, 0, 1, 0,
+                None) == m.MHLA_ERR_INVALID_ARG                                   # t0 + n overflows
+    assert call(1, 1, 16, 4, 8, 0, 2, 2, 1, 0, None) == m.MHLA_ERR_INVALID_ARG    # unknown phi
+    assert call(1, 1, 16, 4, 8, 0, 2, 0, 1, 4, None) == m.MHLA_ERR_INVALID_ARG    # unknown flag
+    assert call(1, 1, 12, 4, 8, 0, 2, 0, 1, 0, None) == m.MHLA_ERR_UNSUPPORTED    # bf16, d % 8
+    # y of 4 tokens x 16 x 2 bytes = 128 bytes written 64 bytes into q
+    assert lib.mhla_decode_steps(q, k, v, w, q + 64, st, 1, 1, 16, 4, 8, 0, 4, 0, 1, 0,
+                                 None) == m.MHLA_ERR_ALIAS
+    # the state (4 + 1 slots of 16 x 17 fp32) would start at v
+    assert lib.mhla_decode_steps(q, k, v, w, y, v, 1, 1, 16, 4, 8, 0, 4, 0, 1, 0,
+                                 None) == m.MHLA_ERR_ALIAS
+    assert lib.mhla_decode_steps(q, k, None, w, y, st, 1, 1, 16, 4, 8, 0, 4, 0, 1, 0,
+                                 None) == m.MHLA_ERR_INVALID_ARG
+
+
 def test_decode_prefill_rejects():
     """Every call here fails in the host checks, before any HIP call."""
     lib = m.load_library()
@@ -315,6 +342,8 @@ int (*f_bwd)(const void*, const void*, const void*, const float*, const void*, v
              hipStream_t) = mhla_backward;
 int (*f_step)(const void*, const void*, const void*, const float*, void*, void*, int, int, int,
               int, int, int, int, int, int, hipStream_t) = mhla_decode_step;
+int (*f_steps)(const void*, const void*, const void*, const float*, void*, void*, int, int, int,
+               int, int, int, int, int, int, int, hipStream_t) = mhla_decode_steps;
 int (*f_prefill)(const void*, const void*, const float*, void*, int, int, int, int, int, int,
                  int, int, int, hipStream_t) = mhla_decode_prefill;
 """

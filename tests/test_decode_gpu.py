@@ -1,5 +1,6 @@
 """GPU parity of incremental (streaming) inference: mhla_decode_step called
-token by token through the C ABI against the oracle's token-by-token causal
+token by token (and mhla_decode_steps over several tokens a call,
+mhla_decode_prefill from a prompt) through the C ABI against the oracle's token-by-token causal
 inference (MHLA paper App. C), which is pinned to the chunkwise causal forward.
 
 Gate: max over (batch, head) slices of max|y - y_oracle| / max|y_oracle| over
@@ -122,4 +123,56 @@ def test_decode_prefill(B, H, N, nb, d, phi, dtype, T, norm):
     err = slice_error(got, ref)
     print("PARITY decode prefill N=%d nb=%d d=%d T=%d dtype=%d norm=%d err=%.3e"
           % (N, nb, d, T, dtype, norm, err))
+    assert err <= TOL[dtype]
+
+
+STEPS_CASES = [
+    # (B, H, N, nb, d, phi, dtype, sizes): tokens per call, cycled until N
+    (2, 3, 256, 64, 64, PHI_ELU1, DTYPE_BF16, (1, 3, 64, 133, 7)),   # calls across chunk ends
+    (2, 3, 256, 64, 64, PHI_ELU1, DTYPE_BF16, (256,)),               # the whole sequence at once
+    (1, 2, 96, 16, 72, PHI_RELU, DTYPE_BF16, (16,)),                 # calls on chunk boundaries
+    (1, 1, 64, 16, 16, PHI_RELU, DTYPE_F32, (5, 1, 40)),
+    (1, 2, 32, 8, 128, PHI_ELU1, DTYPE_F32, (9, 2)),                 # d = 128
+    (1, 2, 30, 6, 13, PHI_ELU1, DTYPE_F32, (4, 11)),                 # odd d
+]
+
+
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("B,H,N,nb,d,phi,dtype,sizes", STEPS_CASES)
+def test_decode_steps(B, H, N, nb, d, phi, dtype, sizes, norm):
+    """mhla_decode_steps over calls of several tokens leaves the outputs and the
+    state of one mhla_decode_step per token, bit for bit, and the outputs
+    match the oracle."""
+    flags = FLAG_CAUSAL | (0 if norm else FLAG_NO_NORM)
+    wl = custom_workload(B, H, d, (1, 1, N), (1, 1, nb), phi, dtype,
+                         index=hash((N, nb, d, sizes)) % 907, flags=flags)
+    inp = make_inputs(wl)
+    q, k, v, w = to_device(inp)
+    M = N // nb
+    qt, kt, vt = (x.permute(2, 0, 1, 3).contiguous() for x in (q, k, v))   # [N, B, H, d]
+    words = m.mhla_decode_state_bytes(B, H, d, M) // 4
+    stepped = torch.full((words,), float("nan"), dtype=torch.float32, device="cuda")
+    y1 = torch.empty_like(qt)
+    for t in range(N):
+        m.mhla_decode_step(qt[t], kt[t], vt[t], w, y1[t], stepped, M, nb, t, wl.phi, flags)
+    grouped = torch.full((words,), float("nan"), dtype=torch.float32, device="cuda")
+    yn = torch.full_like(q, float("nan"))
+    t0, c = 0, 0
+    while t0 < N:
+        n = min(sizes[c % len(sizes)], N - t0)
+        part = torch.empty_like(q[:, :, t0:t0 + n])
+        m.mhla_decode_steps(q[:, :, t0:t0 + n].contiguous(), k[:, :, t0:t0 + n].contiguous(),
+                            v[:, :, t0:t0 + n].contiguous(), w, part, grouped, M, nb, t0,
+                            wl.phi, flags)
+        yn[:, :, t0:t0 + n] = part
+        t0, c = t0 + n, c + 1
+    torch.cuda.synchronize()
+    assert torch.equal(stepped.view(torch.int32), grouped.view(torch.int32))
+    y1 = y1.permute(1, 2, 0, 3).contiguous()
+    assert torch.equal(y1.view(torch.int16 if dtype == DTYPE_BF16 else torch.int32),
+                       yn.view(torch.int16 if dtype == DTYPE_BF16 else torch.int32))
+    ref = oracle.np_decode(inp.q_f64, inp.k_f64, inp.v_f64, inp.w_f64, nb, phi, norm=norm)
+    err = slice_error(to_f64(yn), ref)
+    print("PARITY decode steps N=%d nb=%d d=%d sizes=%s dtype=%d norm=%d err=%.3e"
+          % (N, nb, d, sizes, dtype, norm, err))
     assert err <= TOL[dtype]

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_MAX_LAUNCHES, MhlaError, BlockShape, EXPORTED_SYMBOLS,
     PreparedForward, library_path,
     load_library, mhla_backward, mhla_decode_prefill, mhla_decode_state_bytes, mhla_decode_step,
+    mhla_decode_steps,
     mhla_error_string,
     mhla_forward, mhla_forward_ex, mhla_forward_noalloc, mhla_forward_path, mhla_forward_profiled,
     MHLA_NOALLOC_SCRATCH_BYTES,

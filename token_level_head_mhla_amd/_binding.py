@@ -21,7 +21,8 @@ MHLA_MAX_LAUNCHES = 8
 
 EXPORTED_SYMBOLS = (
     "mhla_forward", "mhla_forward_path", "mhla_forward_ex", "mhla_backward",
-    "mhla_decode_state_bytes", "mhla_decode_step", "mhla_decode_prefill", "mhla_validate",
+    "mhla_decode_state_bytes", "mhla_decode_step", "mhla_decode_steps", "mhla_decode_prefill",
+    "mhla_validate",
     "mhla_plan",
     "mhla_plan_ex", "mhla_lb_init", "mhla_num_blocks", "mhla_workspace_bytes",
     "mhla_workspace_bytes_ex", "mhla_forward_profiled", "mhla_forward_noalloc",
@@ -92,6 +93,9 @@ def load_library():
     lib.mhla_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip,
                                      vp]
     lib.mhla_decode_step.restype = ip
+    lib.mhla_decode_steps.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip,
+                                      ip, vp]
+    lib.mhla_decode_steps.restype = ip
     lib.mhla_decode_prefill.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, ip, vp]
     lib.mhla_decode_prefill.restype = ip
     lib.mhla_plan_ex.argtypes = [ip, ip, ip, ip, bsp, ip, ip, ip]
@@ -312,6 +316,38 @@ def mhla_decode_step(q, k, v, Wmix, y, state, M, nb, t, phi_kind, flags=0, strea
     rc = load_library().mhla_decode_step(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), Wmix.data_ptr(), y.data_ptr(), state.data_ptr(),
         B, H, d, int(M), int(nb), int(t), int(phi_kind), _dtype_code(q), int(flags),
+        _stream_ptr(stream))
+    if rc != MHLA_OK:
+        raise MhlaError(rc, mhla_last_error())
+    return y
+
+
+def mhla_decode_steps(q, k, v, Wmix, y, state, M, nb, t0, phi_kind, flags=0, stream=None):
+    """n streaming steps in one call: q, k, v, y are [B, H, n, d] GPU tensors
+    (tokens t0 .. t0+n-1 of every slice); state is a GPU buffer of
+    mhla_decode_state_bytes(B, H, d, M) bytes.  Same results as n calls of
+    mhla_decode_step."""
+    import torch
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("Wmix", Wmix), ("y", y)):
+        if not (isinstance(t_, torch.Tensor) and t_.is_cuda and t_.is_contiguous()):
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or y.shape != q.shape:
+        raise ValueError("q, k, v, y must share one [B, H, n, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or y.dtype != q.dtype:
+        raise ValueError("q, k, v, y must share one dtype")
+    if Wmix.dtype != torch.float32:
+        raise ValueError("Wmix must be float32")
+    if not (isinstance(state, torch.Tensor) and state.is_cuda and state.is_contiguous()):
+        raise ValueError("state must be a contiguous GPU tensor")
+    B, H, n, d = q.shape
+    if Wmix.numel() != H * int(M) * int(M):
+        raise ValueError("Wmix has %d elements; H*M*M = %d are needed"
+                         % (Wmix.numel(), H * int(M) * int(M)))
+    if state.numel() * state.element_size() < mhla_decode_state_bytes(B, H, d, M):
+        raise ValueError("state is smaller than mhla_decode_state_bytes")
+    rc = load_library().mhla_decode_steps(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), Wmix.data_ptr(), y.data_ptr(), state.data_ptr(),
+        B, H, d, int(M), int(nb), int(t0), n, int(phi_kind), _dtype_code(q), int(flags),
         _stream_ptr(stream))
     if rc != MHLA_OK:
         raise MhlaError(rc, mhla_last_error())

@@ -1,5 +1,5 @@
 // k_decode.hpp -- incremental (streaming) inference of the causal form, one
-// token per (batch, head) slice per call: "MHLA: Restoring Expressivity of
+// or more tokens per (batch, head) slice per launch: "MHLA: Restoring Expressivity of
 // Linear Attention via Token-Level Multi-Head", App. C ("Causal inference").
 //
 // The sequence is cut into chunks of nb tokens; token t sits in chunk
@@ -9,7 +9,7 @@
 //                    b < i and running for b = i;
 //   slot M         : the prefix mixture [P_i | p_i] = sum_{b<i} W[i,b] [S_b | z_b],
 //                    formed once when chunk i starts.
-// One call:
+// Per token t:
 //   t starts chunk i : P_i = sum_{b<i} W[i,b] S_b (the finished summaries are
 //                      fixed from then on) and the running summary restarts;
 //   every token      : S_i += phi(k_t) [v_t | 1]^T;
@@ -20,6 +20,7 @@
 #pragma once
 
 #include "mhla_common.hpp"
+#include "mhla_mfma.hpp"
 
 namespace mhla {
 
@@ -29,72 +30,242 @@ inline size_t decode_state_elems(int d, int M) {
   return (size_t)(M + 1) * (size_t)d * (size_t)(d + 1);
 }
 
-inline size_t decode_lds_bytes(int d) {
-  const size_t E = (size_t)d * (d + 1);
-  return (E + 3 * (size_t)d + 2 * (size_t)(d + 1)) * sizeof(float);
+// LDS of the step kernel: TB tokens' phi(q), phi(k) [TB][d], [v | 1]
+// [TB][d+1] and outputs [TB][d], the readout [d+1], and one (SREG) or two
+// [d][d+1] tiles.
+inline size_t decode_step_lds_bytes(int d, int tb, bool sreg) {
+  const size_t C = (size_t)d + 1, E = (size_t)d * C;
+  return ((size_t)tb * (3 * (size_t)d + C) + C + (sreg ? 1 : 2) * E) * sizeof(float);
 }
 
-// grid = B*H, block = 256.  q, k, v, y: [B*H, d]; W: [H, M, M]; state:
-// [B*H][M+1][d][d+1] fp32.  Calls for t = 0, 1, 2, ... in order on one stream.
-template <typename T, int PHI>
-__global__ __launch_bounds__(kDecThreads) void k_decode_step(
+// grid = B*H, block = NT.  q, k, v, y: [B*H, n, d] (token t0 + u of a slice
+// at row u); W: [H, M, M]; state: [B*H][M+1][d][d+1] fp32.  A launch takes
+// the n tokens t0 .. t0+n-1 of every slice in order, each with exactly the
+// arithmetic of a launch for that token alone, so the outputs and the state
+// do not depend on how a stream is split into launches.  Launches come for
+// increasing t on one stream.
+//
+// Tokens go in groups of TB: the group's q, k, v are staged in LDS with one
+// round of loads, its tokens run from LDS, and its outputs are written to
+// y together when the group ends, so no global access waits inside a token.
+// The running summary S_i and the prefix P_i of the current chunk stay on
+// chip: they are read from the state when the launch starts inside a chunk,
+// the prefix is formed (and written) when a chunk starts, and the summary is
+// written when its chunk ends or the launch does.  With SREG thread tid
+// keeps the entries e = tid + NT x (x < EPT) in registers and writes
+// P_i + W[i,i] S_i to an LDS tile for the readout; otherwise S_i and P_i are
+// LDS tiles and the readout forms that sum itself (the same fma, so the same
+// bits).  Entry e is only ever updated by one thread, and the finished
+// summaries a chunk start mixes were written by that same thread, so the
+// barriers order LDS only.
+template <typename T, int PHI, int NT, int EPT, bool SREG, int TB>
+__global__ __launch_bounds__(NT) void k_decode_step(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ W, T* __restrict__ y, float* __restrict__ state, int H, int d, int M,
-    int nb, int t, int norm) {
+    int nb, int t0, int n, int norm) {
   extern __shared__ float smd[];
   const int C = d + 1;
   const int E = d * C;
-  float* comb = smd;        // [d][C]: P_i + W[i,i] S_i after this token's update
-  float* pq = comb + E;     // phi(q_t)
-  float* pk = pq + d;       // phi(k_t)
-  float* vv = pk + d;       // [v_t | 1]
-  float* red = vv + C;      // [n | den]
+  float* sq = smd;              // [TB][d] phi(q_t)
+  float* sk = sq + TB * d;      // [TB][d] phi(k_t)
+  float* sv = sk + TB * d;      // [TB][C] [v_t | 1]
+  float* sy = sv + TB * C;      // [TB][d] y_t
+  float* red = sy + TB * d;     // [n | den]
+  float* comb = red + C;        // SREG: [d][C] P_i + W[i,i] S_i after this token's update
+  float* ls = comb;             // otherwise: [d][C] S_i,
+  float* lp = ls + E;           //            [d][C] P_i
   const int tid = threadIdx.x;
   const long slice = blockIdx.x;
   const int h = (int)(slice % H);
-  const int i = t / nb, j = t - (t / nb) * nb;
   float* sums = state + (size_t)slice * (M + 1) * E;
   float* prefix = sums + (size_t)M * E;
-  float* Si = sums + (size_t)i * E;
-  const float* Wi = W + ((size_t)h * M + i) * M;
-  const float wii = Wi[i];
+  // feature and column of this thread's first entry, and the step to the next
+  const int f0 = tid / C, c0 = tid - (tid / C) * C;
+  const int fq = NT / C, cq = NT - (NT / C) * C;
 
-  for (int f = tid; f < d; f += kDecThreads) {
-    pq[f] = phi_apply(PHI, Elt<T>::load(q + slice * d + f));
-    pk[f] = phi_apply(PHI, Elt<T>::load(k + slice * d + f));
-    vv[f] = Elt<T>::load(v + slice * d + f);
-  }
-  if (tid == 0) vv[d] = 1.0f;
-  __syncthreads();
-
-  for (int e = tid; e < E; e += kDecThreads) {
-    const int f = e / C, c = e - (e / C) * C;
-    float P, s_old;
-    if (j == 0) {  // chunk i starts: mix the finished chunks once, restart S_i
-      P = 0.0f;
-      for (int b = 0; b < i; ++b) P = fmaf(Wi[b], sums[(size_t)b * E + e], P);
-      prefix[e] = P;
-      s_old = 0.0f;
+  float s_reg[SREG ? EPT : 1], p_reg[SREG ? EPT : 1];
+  if (t0 % nb != 0) {  // the launch starts inside a chunk: pick up its state
+    const float* Si = sums + (size_t)(t0 / nb) * E;
+    if constexpr (SREG) {
+#pragma unroll
+      for (int x = 0; x < EPT; ++x) {
+        const int e = tid + NT * x;
+        if (e < E) {
+          s_reg[x] = Si[e];
+          p_reg[x] = prefix[e];
+        }
+      }
     } else {
-      P = prefix[e];
-      s_old = Si[e];
+      for (int e = tid; e < E; e += NT) {
+        ls[e] = Si[e];
+        lp[e] = prefix[e];
+      }
     }
-    const float s_new = fmaf(pk[f], vv[c], s_old);
-    Si[e] = s_new;
-    comb[e] = fmaf(wii, s_new, P);
   }
-  __syncthreads();
+  const T* qs = q + slice * n * (long)d;
+  const T* ks = k + slice * n * (long)d;
+  const T* vs = v + slice * n * (long)d;
+  T* ys = y + slice * n * (long)d;
 
-  for (int c = tid; c < C; c += kDecThreads) {
-    float acc = 0.0f;
-    for (int f = 0; f < d; ++f) acc = fmaf(pq[f], comb[f * C + c], acc);
-    red[c] = acc;
-  }
-  __syncthreads();
-  for (int c = tid; c < d; c += kDecThreads) {
-    const float den = red[d];
-    const float val = !norm ? red[c] : den == 0.0f ? 0.0f : red[c] / den;
-    Elt<T>::store(y + slice * d + c, val);
+  for (int g0 = 0; g0 < n; g0 += TB) {
+    const int nt = min(TB, n - g0);
+    // The readers of sq, sk, sv and sy of the previous group all passed a
+    // barrier after their last read.
+    for (int x = tid; x < nt * d; x += NT) {
+      const int uu = x / d, f = x - (x / d) * d;
+      const long r = (long)g0 * d + x;
+      sq[x] = phi_apply(PHI, Elt<T>::load(qs + r));
+      sk[x] = phi_apply(PHI, Elt<T>::load(ks + r));
+      sv[uu * C + f] = Elt<T>::load(vs + r);
+    }
+    for (int uu = tid; uu < nt; uu += NT) sv[uu * C + d] = 1.0f;
+    lds_barrier();
+
+    for (int uu = 0; uu < nt; ++uu) {
+      const int t = t0 + g0 + uu;
+      const int i = t / nb, j = t - (t / nb) * nb;
+      const float* Wi = W + ((size_t)h * M + i) * M;
+      const float wii = Wi[i];
+      float* Si = sums + (size_t)i * E;
+      const bool keep = j == nb - 1 || g0 + uu == n - 1;   // the chunk or the launch ends
+      const float* pq = sq + uu * d;
+      const float* pk = sk + uu * d;
+      const float* vv = sv + uu * C;
+
+      if constexpr (SREG) {
+        if (j == 0) {  // chunk i starts: mix the finished chunks once, restart S_i
+          // P = sum over b < i in order, from 0; the loads of MB chunks are
+          // issued before their fmas so that they are in flight together.
+          constexpr int MB = 4;
+#pragma unroll
+          for (int x = 0; x < EPT; ++x) p_reg[x] = 0.0f;
+          int b = 0;
+          for (; b + MB <= i; b += MB) {
+            float sv4[MB][EPT];
+#pragma unroll
+            for (int r = 0; r < MB; ++r)
+#pragma unroll
+              for (int x = 0; x < EPT; ++x) {
+                const int e = tid + NT * x;
+                sv4[r][x] = e < E ? sums[(size_t)(b + r) * E + e] : 0.0f;
+              }
+#pragma unroll
+            for (int r = 0; r < MB; ++r) {
+              const float wb = Wi[b + r];
+#pragma unroll
+              for (int x = 0; x < EPT; ++x) p_reg[x] = fmaf(wb, sv4[r][x], p_reg[x]);
+            }
+          }
+          for (; b < i; ++b) {
+            const float wb = Wi[b];
+#pragma unroll
+            for (int x = 0; x < EPT; ++x) {
+              const int e = tid + NT * x;
+              if (e < E) p_reg[x] = fmaf(wb, sums[(size_t)b * E + e], p_reg[x]);
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < EPT; ++x) {
+            const int e = tid + NT * x;
+            if (e < E) prefix[e] = p_reg[x];
+            s_reg[x] = 0.0f;
+          }
+        }
+        int f = f0, c = c0;
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+          const int e = tid + NT * x;
+          if (e < E) {
+            const float s_new = fmaf(pk[f], vv[c], s_reg[x]);
+            s_reg[x] = s_new;
+            comb[e] = fmaf(wii, s_new, p_reg[x]);
+          }
+          f += fq;
+          c += cq;
+          if (c >= C) {
+            c -= C;
+            ++f;
+          }
+        }
+        if (keep) {
+#pragma unroll
+          for (int x = 0; x < EPT; ++x) {
+            const int e = tid + NT * x;
+            if (e < E) Si[e] = s_reg[x];
+          }
+        }
+      } else {
+        if (j == 0) {  // chunk i starts: P over b < i in order, chunk by chunk
+          for (int e = tid; e < E; e += NT) lp[e] = 0.0f;
+          for (int b = 0; b < i; ++b) {
+            const float wb = Wi[b];
+            const float* Sb = sums + (size_t)b * E;
+#pragma unroll 4
+            for (int e = tid; e < E; e += NT) lp[e] = fmaf(wb, Sb[e], lp[e]);
+          }
+          for (int e = tid; e < E; e += NT) prefix[e] = lp[e];
+        }
+        int f = f0, c = c0;
+        for (int e = tid; e < E; e += NT) {
+          const float s_old = j == 0 ? 0.0f : ls[e];
+          const float s_new = fmaf(pk[f], vv[c], s_old);
+          ls[e] = s_new;
+          if (keep) Si[e] = s_new;
+          f += fq;
+          c += cq;
+          if (c >= C) {
+            c -= C;
+            ++f;
+          }
+        }
+      }
+      lds_barrier();
+
+      for (int c = tid; c < C; c += NT) {
+        float acc = 0.0f;
+        if constexpr (SREG) {
+          // in order over f; the operands of RU terms are loaded before their fmas
+          constexpr int RU = 16;
+          int f = 0;
+          for (; f + RU <= d; f += RU) {
+            float a[RU], w[RU];
+#pragma unroll
+            for (int r = 0; r < RU; ++r) {
+              a[r] = pq[f + r];
+              w[r] = comb[(f + r) * C + c];
+            }
+#pragma unroll
+            for (int r = 0; r < RU; ++r) acc = fmaf(a[r], w[r], acc);
+          }
+          for (; f < d; ++f) acc = fmaf(pq[f], comb[f * C + c], acc);
+        } else {
+          constexpr int RU = 8;
+          int f = 0;
+          for (; f + RU <= d; f += RU) {
+            float a[RU], sw[RU], pw[RU];
+#pragma unroll
+            for (int r = 0; r < RU; ++r) {
+              a[r] = pq[f + r];
+              sw[r] = ls[(f + r) * C + c];
+              pw[r] = lp[(f + r) * C + c];
+            }
+#pragma unroll
+            for (int r = 0; r < RU; ++r) acc = fmaf(a[r], fmaf(wii, sw[r], pw[r]), acc);
+          }
+          for (; f < d; ++f) acc = fmaf(pq[f], fmaf(wii, ls[f * C + c], lp[f * C + c]), acc);
+        }
+        red[c] = acc;
+      }
+      lds_barrier();
+      // red is written again only after the next token's first barrier, which
+      // every reader here reaches after these reads
+      for (int c = tid; c < d; c += NT) {
+        const float den = red[d];
+        sy[uu * d + c] = !norm ? red[c] : den == 0.0f ? 0.0f : red[c] / den;
+      }
+    }
+    lds_barrier();
+    for (int x = tid; x < nt * d; x += NT) Elt<T>::store(ys + (long)g0 * d + x, sy[x]);
   }
 }
 
@@ -212,23 +383,41 @@ int launch_decode_prefill_t(long slices, int H, int d, int M, int nb, int Tp, in
   return 0;
 }
 
-template <typename T>
-int launch_decode_t(long slices, int H, int d, int M, int nb, int t, int phi, int norm,
-                    const T* q, const T* k, const T* v, const float* W, T* y, float* state,
-                    hipStream_t st) {
-  const size_t lds = decode_lds_bytes(d);
+// NT threads of EPT entries each hold the state of one slice, d (d + 1) fp32.
+template <typename T, int NT, int EPT, bool SREG, int TB>
+int launch_decode_ept(long slices, int H, int d, int M, int nb, int t0, int n, int phi,
+                      int norm, const T* q, const T* k, const T* v, const float* W, T* y,
+                      float* state, hipStream_t st) {
+  const size_t lds = decode_step_lds_bytes(d, TB, SREG);
   static std::atomic<bool> attr_set[2][64];
-  const void* fn = phi == PHI_RELU ? reinterpret_cast<const void*>(&k_decode_step<T, PHI_RELU>)
-                                   : reinterpret_cast<const void*>(&k_decode_step<T, PHI_ELU1>);
+  const void* fn =
+      phi == PHI_RELU ? reinterpret_cast<const void*>(&k_decode_step<T, PHI_RELU, NT, EPT, SREG, TB>)
+                      : reinterpret_cast<const void*>(&k_decode_step<T, PHI_ELU1, NT, EPT, SREG, TB>);
   if (lds > 64 * 1024 && lds_limit_once(fn, attr_set[phi == PHI_RELU ? 0 : 1], 160 * 1024) != 0)
     return -1;
   if (phi == PHI_RELU)
-    k_decode_step<T, PHI_RELU><<<dim3((unsigned)slices), kDecThreads, lds, st>>>(
-        q, k, v, W, y, state, H, d, M, nb, t, norm);
+    k_decode_step<T, PHI_RELU, NT, EPT, SREG, TB><<<dim3((unsigned)slices), NT, lds, st>>>(
+        q, k, v, W, y, state, H, d, M, nb, t0, n, norm);
   else
-    k_decode_step<T, PHI_ELU1><<<dim3((unsigned)slices), kDecThreads, lds, st>>>(
-        q, k, v, W, y, state, H, d, M, nb, t, norm);
+    k_decode_step<T, PHI_ELU1, NT, EPT, SREG, TB><<<dim3((unsigned)slices), NT, lds, st>>>(
+        q, k, v, W, y, state, H, d, M, nb, t0, n, norm);
   return 0;
+}
+
+// Up to d = 65: 256 threads of 17 entries, summary and prefix in registers
+// (4 waves: one a SIMD at one slice a CU), groups of 16 tokens.  Beyond,
+// larger per-thread shares would spill: 512 threads with both tiles in LDS
+// and groups of 8 tokens (149 KB at d = 128).
+template <typename T>
+int launch_decode_t(long slices, int H, int d, int M, int nb, int t0, int n, int phi, int norm,
+                    const T* q, const T* k, const T* v, const float* W, T* y, float* state,
+                    hipStream_t st) {
+  const long E = (long)d * (d + 1);
+  if (E <= 17 * 256)
+    return launch_decode_ept<T, 256, 17, true, 16>(slices, H, d, M, nb, t0, n, phi, norm, q, k,
+                                                   v, W, y, state, st);
+  return launch_decode_ept<T, 512, 1, false, 8>(slices, H, d, M, nb, t0, n, phi, norm, q, k, v,
+                                                W, y, state, st);
 }
 
 }  // namespace mhla

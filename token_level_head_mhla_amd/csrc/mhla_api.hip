@@ -411,11 +411,18 @@ size_t mhla_decode_state_bytes(int B, int H, int d, int M) {
   return (size_t)B * H * decode_state_elems(d, M) * sizeof(float);
 }
 
-int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix, void* y,
-                     void* state, int B, int H, int d, int M, int nb, int t, int phi_kind,
-                     int dtype, int flags, mhla_stream_t stream) {
-  int rc = check_decode(B, H, d, M, nb, t, phi_kind, dtype, flags);
+namespace {
+
+// Tokens t0 .. t0+n-1 of every slice; q, k, v, y: [B*H, n, d].
+int decode_tokens(const void* q, const void* k, const void* v, const float* Wmix, void* y,
+                  void* state, int B, int H, int d, int M, int nb, int t0, int n, int phi_kind,
+                  int dtype, int flags, hipStream_t st) {
+  if (n <= 0) return fail(MHLA_ERR_INVALID_ARG, "n=%d: at least one token per call", n);
+  int rc = check_decode(B, H, d, M, nb, t0, phi_kind, dtype, flags);
   if (rc != MHLA_OK) return rc;
+  if ((long)t0 + n > (long)M * nb)
+    return fail(MHLA_ERR_INVALID_ARG, "tokens %d..%ld run past the %ld positions of M*nb", t0,
+                (long)t0 + n - 1, (long)M * nb);
   if (!q || !k || !v || !Wmix || !y || !state)
     return fail(MHLA_ERR_INVALID_ARG, "a pointer is NULL");
   const void* ptrs[6] = {q, k, v, Wmix, y, state};
@@ -423,27 +430,48 @@ int mhla_decode_step(const void* q, const void* k, const void* v, const float* W
     if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
       return fail(MHLA_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
   const size_t eb = dtype == MHLA_DTYPE_F32 ? 4 : 2;
-  const size_t tb = (size_t)B * H * d * eb;
+  const size_t tb = (size_t)B * H * n * d * eb;
   const size_t sb = mhla_decode_state_bytes(B, H, d, M);
+  const size_t wb = (size_t)H * M * M * sizeof(float);
   if (overlaps(y, tb, q, tb) || overlaps(y, tb, k, tb) || overlaps(y, tb, v, tb) ||
-      overlaps(y, tb, state, sb))
-    return fail(MHLA_ERR_ALIAS, "y overlaps q, k, v or the state");
-  hipStream_t st = stream;
+      overlaps(y, tb, state, sb) || overlaps(y, tb, Wmix, wb))
+    return fail(MHLA_ERR_ALIAS, "y overlaps q, k, v, Wmix or the state");
+  if (overlaps(state, sb, q, tb) || overlaps(state, sb, k, tb) || overlaps(state, sb, v, tb) ||
+      overlaps(state, sb, Wmix, wb))
+    return fail(MHLA_ERR_ALIAS, "the state overlaps q, k, v or Wmix");
   (void)hipGetLastError();
   const int norm = (flags & MHLA_FLAG_NO_NORM) ? 0 : 1;
   const long slices = (long)B * H;
   if (dtype == MHLA_DTYPE_F32)
-    rc = launch_decode_t<float>(slices, H, d, M, nb, t, phi_kind, norm, (const float*)q,
+    rc = launch_decode_t<float>(slices, H, d, M, nb, t0, n, phi_kind, norm, (const float*)q,
                                 (const float*)k, (const float*)v, Wmix, (float*)y, (float*)state,
                                 st);
   else
-    rc = launch_decode_t<bf16_t>(slices, H, d, M, nb, t, phi_kind, norm, (const bf16_t*)q,
+    rc = launch_decode_t<bf16_t>(slices, H, d, M, nb, t0, n, phi_kind, norm, (const bf16_t*)q,
                                  (const bf16_t*)k, (const bf16_t*)v, Wmix, (bf16_t*)y,
                                  (float*)state, st);
   if (rc != 0) return fail(MHLA_ERR_HIP, "decode set-up failed (hipFuncSetAttribute)");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MHLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MHLA_OK;
+}
+
+}  // namespace
+
+int mhla_decode_step(const void* q, const void* k, const void* v, const float* Wmix, void* y,
+                     void* state, int B, int H, int d, int M, int nb, int t, int phi_kind,
+                     int dtype, int flags, mhla_stream_t stream) {
+  g_last_error.clear();
+  return decode_tokens(q, k, v, Wmix, y, state, B, H, d, M, nb, t, 1, phi_kind, dtype, flags,
+                       stream);
+}
+
+int mhla_decode_steps(const void* q, const void* k, const void* v, const float* Wmix, void* y,
+                      void* state, int B, int H, int d, int M, int nb, int t0, int n,
+                      int phi_kind, int dtype, int flags, mhla_stream_t stream) {
+  g_last_error.clear();
+  return decode_tokens(q, k, v, Wmix, y, state, B, H, d, M, nb, t0, n, phi_kind, dtype, flags,
+                       stream);
 }
 
 int mhla_decode_prefill(const void* k, const void* v, const float* Wmix, void* state, int B,
