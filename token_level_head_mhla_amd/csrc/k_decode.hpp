@@ -31,11 +31,11 @@ inline size_t decode_state_elems(int d, int M) {
 }
 
 // LDS of the step kernel: TB tokens' phi(q), phi(k) [TB][d], [v | 1]
-// [TB][d+1] and outputs [TB][d], the readout [d+1], and one (SREG) or two
-// [d][d+1] tiles.
+// [TB][d+1] and outputs [TB][d], the readout (up to 4 partial rows of d+1),
+// and one (SREG) or two [d][d+1] tiles.
 inline size_t decode_step_lds_bytes(int d, int tb, bool sreg) {
   const size_t C = (size_t)d + 1, E = (size_t)d * C;
-  return ((size_t)tb * (3 * (size_t)d + C) + C + (sreg ? 1 : 2) * E) * sizeof(float);
+  return ((size_t)tb * (3 * (size_t)d + C) + 4 * C + (sreg ? 1 : 2) * E) * sizeof(float);
 }
 
 // grid = B*H, block = NT.  q, k, v, y: [B*H, n, d] (token t0 + u of a slice
@@ -53,9 +53,9 @@ inline size_t decode_step_lds_bytes(int d, int tb, bool sreg) {
 // the prefix is formed (and written) when a chunk starts, and the summary is
 // written when its chunk ends or the launch does.  With SREG thread tid
 // keeps the entries e = tid + NT x (x < EPT) in registers and writes
-// P_i + W[i,i] S_i to an LDS tile for the readout; otherwise S_i and P_i are
-// LDS tiles and the readout forms that sum itself (the same fma, so the same
-// bits).  Entry e is only ever updated by one thread, and the finished
+// P_i + W[i,i] S_i to an LDS tile, whose readout the four waves share by
+// features; otherwise S_i and P_i are LDS tiles and the readout forms that
+// sum itself.  Entry e is only ever updated by one thread, and the finished
 // summaries a chunk start mixes were written by that same thread, so the
 // barriers order LDS only.
 template <typename T, int PHI, int NT, int EPT, bool SREG, int TB>
@@ -70,8 +70,8 @@ __global__ __launch_bounds__(NT) void k_decode_step(
   float* sk = sq + TB * d;      // [TB][d] phi(k_t)
   float* sv = sk + TB * d;      // [TB][C] [v_t | 1]
   float* sy = sv + TB * C;      // [TB][d] y_t
-  float* red = sy + TB * d;     // [n | den]
-  float* comb = red + C;        // SREG: [d][C] P_i + W[i,i] S_i after this token's update
+  float* red = sy + TB * d;     // [n | den]; SREG: [NT / 64][C] partial sums
+  float* comb = red + 4 * C;        // SREG: [d][C] P_i + W[i,i] S_i after this token's update
   float* ls = comb;             // otherwise: [d][C] S_i,
   float* lp = ls + E;           //            [d][C] P_i
   const int tid = threadIdx.x;
@@ -221,24 +221,45 @@ __global__ __launch_bounds__(NT) void k_decode_step(
       }
       lds_barrier();
 
-      for (int c = tid; c < C; c += NT) {
-        float acc = 0.0f;
-        if constexpr (SREG) {
-          // in order over f; the operands of RU terms are loaded before their fmas
-          constexpr int RU = 16;
-          int f = 0;
-          for (; f + RU <= d; f += RU) {
-            float a[RU], w[RU];
+      if constexpr (SREG) {
+        // Wave w sums the features of its quarter of [0, d) in order, for every
+        // column; the four partials are added in wave order when y is formed.
+        // The operands of RU terms are loaded before their fmas.
+        constexpr int NW = NT / 64, RU = 16;
+        static_assert(NW <= 4, "partial rows of the readout");
+        const int w = tid >> 6, lane = tid & 63;
+        const int fw = (d + NW - 1) / NW, fb = w * fw, fe = min(d, fb + fw);
+        for (int c = lane; c < C; c += 64) {
+          float acc = 0.0f;
+          int f = fb;
+          for (; f + RU <= fe; f += RU) {
+            float a[RU], cw[RU];
 #pragma unroll
             for (int r = 0; r < RU; ++r) {
               a[r] = pq[f + r];
-              w[r] = comb[(f + r) * C + c];
+              cw[r] = comb[(f + r) * C + c];
             }
 #pragma unroll
-            for (int r = 0; r < RU; ++r) acc = fmaf(a[r], w[r], acc);
+            for (int r = 0; r < RU; ++r) acc = fmaf(a[r], cw[r], acc);
           }
-          for (; f < d; ++f) acc = fmaf(pq[f], comb[f * C + c], acc);
-        } else {
+          for (; f < fe; ++f) acc = fmaf(pq[f], comb[f * C + c], acc);
+          red[w * C + c] = acc;
+        }
+        lds_barrier();
+        // red is written again only after the next token's first barrier,
+        // which every reader here reaches after these reads
+        for (int c = tid; c < d; c += NT) {
+          float num = red[c], den = red[d];
+#pragma unroll
+          for (int r = 1; r < NW; ++r) {
+            num += red[r * C + c];
+            den += red[r * C + d];
+          }
+          sy[uu * d + c] = !norm ? num : den == 0.0f ? 0.0f : num / den;
+        }
+      } else {
+        for (int c = tid; c < C; c += NT) {
+          float acc = 0.0f;
           constexpr int RU = 8;
           int f = 0;
           for (; f + RU <= d; f += RU) {
@@ -253,15 +274,13 @@ __global__ __launch_bounds__(NT) void k_decode_step(
             for (int r = 0; r < RU; ++r) acc = fmaf(a[r], fmaf(wii, sw[r], pw[r]), acc);
           }
           for (; f < d; ++f) acc = fmaf(pq[f], fmaf(wii, ls[f * C + c], lp[f * C + c]), acc);
+          red[c] = acc;
         }
-        red[c] = acc;
-      }
-      lds_barrier();
-      // red is written again only after the next token's first barrier, which
-      // every reader here reaches after these reads
-      for (int c = tid; c < d; c += NT) {
-        const float den = red[d];
-        sy[uu * d + c] = !norm ? red[c] : den == 0.0f ? 0.0f : red[c] / den;
+        lds_barrier();
+        for (int c = tid; c < d; c += NT) {
+          const float den = red[d];
+          sy[uu * d + c] = !norm ? red[c] : den == 0.0f ? 0.0f : red[c] / den;
+        }
       }
     }
     lds_barrier();
