@@ -379,8 +379,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_prefill_prefix(
   if (e >= E) return;
   const float* sums = state + (size_t)slice * (M + 1) * E;
   const float* Wi = W + ((size_t)(slice % H) * M + i) * M;
+  // in order over b from 0, as the step mixes; the loads of PB chunks are
+  // issued before their fmas so that they are in flight together
+  constexpr int PB = 8;
   float P = 0.0f;
-  for (int b = 0; b < i; ++b) P = fmaf(Wi[b], sums[(size_t)b * E + e], P);
+  int b = 0;
+  for (; b + PB <= i; b += PB) {
+    float sv[PB];
+#pragma unroll
+    for (int r = 0; r < PB; ++r) sv[r] = sums[(size_t)(b + r) * E + e];
+#pragma unroll
+    for (int r = 0; r < PB; ++r) P = fmaf(Wi[b + r], sv[r], P);
+  }
+  for (; b < i; ++b) P = fmaf(Wi[b], sums[(size_t)b * E + e], P);
   state[((size_t)slice * (M + 1) + M) * E + e] = P;
 }
 
